@@ -1,0 +1,290 @@
+"""Reference oracle for the MoE feed-forward layer (TEST INFRASTRUCTURE ONLY).
+
+This is a plain, slow CPU implementation of the layer, written from the
+pages' description of the method.  It exists to check the HIP path; only the
+test suite, the package's smoke check and the benchmark's CPU-baseline leg
+may import or call it.  It shares no code with the HIP path: its only inputs
+are host arrays (NumPy or anything ``np.asarray`` accepts).
+
+Precision: every floating-point step runs in float64 on the exact input
+values (fp32 and bf16 inputs convert to float64 exactly), except the
+balancing-bias update, which keeps the bias as a float32 state so that its
+value is bit-comparable.
+
+Sources (page title, section):
+
+* "Inkling, Dissected", chapter 02 "Anatomy of one MoE layer": 256 routed
+  experts of which each token uses 6, 2 shared experts every token uses, and
+  one joint normalisation over the 8 contributors.
+* "Inkling, Dissected", 02b "Sigmoid, not softmax": the router equation
+  (independent sigmoids, top-6 by s + b, gates from raw s over
+  kept-and-shared) and its NumPy sketch of one token's forward.
+* "Inkling, Dissected", 02c "A routing decision, by hand": a 4-expert top-2
+  worked example (used as a golden test).
+* "Inkling, Dissected", 02e "The aux-loss-free bias": the balancing rule
+  b_i <- b_i + gamma * sign(Lbar - L_i), with L_i the tokens that selected
+  expert i this batch and Lbar the total selections divided by the number
+  of routed experts.
+* "Under The Hood: Inkling from Thinking Machines", "MoE: the expert
+  configuration" (each expert is a SwiGLU FFN; shared experts have the same
+  width) and "The routing strategy: sigmoid + shared expert sink" (top-6 over
+  routed experts only; shared scores join the normalisation).
+
+Readings where the pages leave a step open:
+
+* the top-k list is in rank order: descending s + b, exact ties to the lower
+  expert index;
+* sign(0) = 0, and Lbar is compared exactly as sign(k*T - E*L_i);
+* the bias updates after the forward that used it;
+* SwiGLU expert: y = W_down (silu(W_gate x) * (W_up x)), silu(u) = u*sigmoid(u),
+  no bias terms, weights stored [out, in];
+* loads count routed selections only.
+
+Every function here is pinned by ``tests/test_oracle.py``; none is left
+unpinned.
+"""
+import numpy as np
+
+
+def _f64(a):
+    return np.asarray(a, dtype=np.float64)
+
+
+def sigmoid(z):
+    """s = 1 / (1 + exp(-z)), float64 ("Inkling, Dissected", 02b)."""
+    z = _f64(z)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def router_logits(x, w_router):
+    """z[t, i] = x_t . w_i for every routed and shared expert (02b).
+
+    ``w_router`` is [n_routed + n_shared, d], one routing vector per row.
+    """
+    return _f64(x) @ _f64(w_router).T
+
+
+def select_topk(key, k):
+    """Top-k expert ids of each row of ``key`` in rank order.
+
+    Rank order is descending key; among exactly equal keys the lower expert
+    index ranks first (a stable sort of the negated keys).  Also returns the
+    margin key_(k) - key_(k+1) between the last kept and the first dropped
+    expert (+inf when every expert is kept).
+    """
+    key = _f64(key)
+    order = np.argsort(-key, axis=1, kind="stable")
+    top = order[:, :k]
+    ks = np.take_along_axis(key, order, axis=1)
+    if key.shape[1] > k:
+        margin = ks[:, k - 1] - ks[:, k]
+    else:
+        margin = np.full(key.shape[0], np.inf)
+    return top.astype(np.int64), margin
+
+
+def joint_gates(s, top, shared_ids):
+    """g over the kept routed experts followed by the shared experts.
+
+    g_i = s_i / sum_{j in kept U shared} s_j, summed in slot order (02b; the
+    shared-expert sink of the Hugging Face write-up).  ``s`` holds raw
+    affinities: the balancing bias never enters the gates.
+    """
+    s = _f64(s)
+    T = s.shape[0]
+    shared = np.broadcast_to(np.asarray(shared_ids, dtype=np.int64),
+                             (T, len(shared_ids)))
+    idx = np.concatenate([top, shared], axis=1)
+    sel = np.take_along_axis(s, idx, axis=1)
+    denom = np.zeros(T)
+    for j in range(sel.shape[1]):
+        denom = denom + sel[:, j]
+    return sel / denom[:, None], idx
+
+
+def route(x, w_router, bias, n_routed=256, k=6):
+    """Router of one batch: sigmoid affinities, biased top-k, joint gates.
+
+    Returns a dict with ``z`` [T, n_routed+n_shared], ``s`` (affinities),
+    ``key`` = s[:, :n_routed] + b, ``topk_idx`` [T, k] in rank order,
+    ``margin`` [T], ``gates`` [T, k + n_shared] (routed slots first, then the
+    shared experts in id order) and ``idx`` [T, k + n_shared].
+    """
+    z = router_logits(x, w_router)
+    s = sigmoid(z)
+    n_total = s.shape[1]
+    key = s[:, :n_routed] + _f64(bias)[None, :]
+    top, margin = select_topk(key, k)
+    gates, idx = joint_gates(s, top, list(range(n_routed, n_total)))
+    return {"z": z, "s": s, "key": key, "topk_idx": top, "margin": margin,
+            "gates": gates, "idx": idx}
+
+
+def dispatch(topk_idx, n_routed=256):
+    """Expert-contiguous grouping of the (token, slot) pairs.
+
+    A pair is numbered p = t*k + j (token t, slot j).  Returns
+    ``counts`` [n_routed] (the loads L_i), ``offsets`` [n_routed+1]
+    (exclusive prefix sum of counts), ``sorted_pair`` [T*k] (pair numbers
+    grouped by expert; within one expert in ascending p, hence ascending
+    token) and ``pair_pos`` [T*k], the inverse permutation.
+    """
+    flat = np.asarray(topk_idx, dtype=np.int64).ravel()
+    counts = np.bincount(flat, minlength=n_routed)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    sorted_pair = np.argsort(flat, kind="stable")
+    pair_pos = np.empty_like(sorted_pair)
+    pair_pos[sorted_pair] = np.arange(flat.size)
+    return {"counts": counts.astype(np.int64), "offsets": offsets.astype(np.int64),
+            "sorted_pair": sorted_pair.astype(np.int64),
+            "pair_pos": pair_pos.astype(np.int64)}
+
+
+def silu(u):
+    """silu(u) = u * sigmoid(u)."""
+    return _f64(u) * sigmoid(u)
+
+
+def swiglu(X, w_gate, w_up, w_down):
+    """One SwiGLU expert on the rows of X: (silu(X Wg^T) * (X Wu^T)) Wd^T.
+
+    ("Under The Hood: Inkling", "MoE: the expert configuration": each expert
+    is a SwiGLU FFN.)  Weights are [out, in].
+    """
+    X = _f64(X)
+    h = silu(X @ _f64(w_gate).T) * (X @ _f64(w_up).T)
+    return h @ _f64(w_down).T
+
+
+def expert_ffn(x, weights, offsets, sorted_pair, k=6):
+    """Every routed expert on its rows, and every shared expert on all rows.
+
+    ``weights`` maps ``w_gate``, ``w_up`` [E, F, d], ``w_down`` [E, d, F] and
+    ``ws_gate``, ``ws_up``, ``ws_down`` (same with leading S) to arrays.
+    Returns ``y_routed`` [T*k, d] in sorted-pair order and ``y_shared``
+    [S, T, d].
+    """
+    x = _f64(x)
+    T, d = x.shape
+    offsets = np.asarray(offsets)
+    sorted_pair = np.asarray(sorted_pair)
+    E = len(offsets) - 1
+    y_routed = np.zeros((T * k, d))
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        rows = sorted_pair[lo:hi] // k
+        y_routed[lo:hi] = swiglu(x[rows], weights["w_gate"][e],
+                                 weights["w_up"][e], weights["w_down"][e])
+    S = len(weights["ws_gate"])
+    y_shared = np.stack([swiglu(x, weights["ws_gate"][s], weights["ws_up"][s],
+                                weights["ws_down"][s]) for s in range(S)]) \
+        if S else np.zeros((0, T, d))
+    return y_routed, y_shared
+
+
+def combine(y_routed, y_shared, gates, pair_pos, k=6):
+    """y_t = sum_j g[t,j] Y[pair_pos[t*k+j]] + sum_s g[t,k+s] Y_s[s,t].
+
+    Routed slots in rank order, then the shared experts in id order (02b:
+    the gate-weighted sum over the 8 contributors).
+    """
+    gates = _f64(gates)
+    T = gates.shape[0]
+    pp = np.asarray(pair_pos).reshape(T, k)
+    y = np.zeros((T, np.shape(y_routed)[1]))
+    for j in range(k):
+        y = y + gates[:, j:j + 1] * _f64(y_routed)[pp[:, j]]
+    for s in range(len(y_shared)):
+        y = y + gates[:, k + s:k + s + 1] * _f64(y_shared[s])
+    return y
+
+
+def bias_update(counts, gamma, bias, T, k=6):
+    """b_i <- b_i + gamma * sign(Lbar - L_i), float32 state.
+
+    ("Inkling, Dissected", 02e.)  Lbar = k*T / E, so the sign is taken
+    exactly as sign(k*T - E*L_i); sign(0) = 0.  The step is one float32
+    addition of float32(gamma) times the sign.
+    """
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    sgn = np.sign(k * T - E * counts).astype(np.float32)
+    b = np.asarray(bias, dtype=np.float32)
+    return (b + np.float32(gamma) * sgn).astype(np.float32)
+
+
+def moe_forward(x, w_router, weights, bias, gamma, k=6):
+    """The whole layer for one batch, followed by the bias update.
+
+    Returns the router dict, the dispatch dict, ``y_routed``, ``y_shared``,
+    ``y`` [T, d] and the next bias ``bias_next`` (float32).
+    """
+    x = _f64(x)
+    T = x.shape[0]
+    E = np.shape(bias)[0]
+    r = route(x, w_router, bias, n_routed=E, k=k)
+    dp = dispatch(r["topk_idx"], n_routed=E)
+    y_routed, y_shared = expert_ffn(x, weights, dp["offsets"], dp["sorted_pair"], k)
+    y = combine(y_routed, y_shared, r["gates"], dp["pair_pos"], k)
+    b_next = bias_update(dp["counts"], gamma, bias, T, k)
+    return {"router": r, "dispatch": dp, "y_routed": y_routed,
+            "y_shared": y_shared, "y": y, "bias_next": b_next}
+
+
+def moe_layer_per_token(x_t, experts, w_router, bias, k=6):
+    """One token's forward, step by step as the page's NumPy sketch states.
+
+    ("Inkling, Dissected", 02b.)  ``experts`` is a list of callables, routed
+    experts first and the shared experts last.  Used on small inputs to
+    cross-check the grouped ``expert_ffn`` + ``combine``.
+    """
+    x_t = _f64(x_t)
+    n_routed = len(bias)
+    s = sigmoid(_f64(w_router) @ x_t)
+    key = s[:n_routed] + _f64(bias)
+    top, _ = select_topk(key[None, :], k)
+    idx = list(top[0]) + list(range(n_routed, len(s)))
+    g = s[idx] / s[idx].sum()
+    out = np.zeros_like(x_t)
+    for g_k, e in zip(g, idx):
+        out = out + g_k * experts[e](x_t)
+    return out
+
+
+def output_rows(tokens, x, topk_idx, gates, expert_weights, k=6, n_routed=256,
+                n_shared=2):
+    """y_t for a few tokens, given their routing (for large workloads).
+
+    ``expert_weights(e)`` returns (w_gate, w_up, w_down) of expert e (shared
+    experts are ids n_routed..n_routed+n_shared-1).  Experts are visited in id
+    order and each expert's weights are fetched once, so the cost is one
+    weight conversion per distinct expert.  Contributions are added per
+    token in slot order, as ``combine`` does.
+    """
+    tokens = list(tokens)
+    x = _f64(x)
+    topk_idx = np.asarray(topk_idx)
+    gates = _f64(gates)
+    need = {}
+    for t in tokens:
+        for j, e in enumerate(list(topk_idx[t]) + list(range(n_routed, n_routed + n_shared))):
+            need.setdefault(int(e), []).append((t, j))
+    contrib = {}
+    for e in sorted(need):
+        wg, wu, wd = expert_weights(e)
+        rows = [t for t, _ in need[e]]
+        ye = swiglu(x[rows], wg, wu, wd)
+        for (t, j), yrow in zip(need[e], ye):
+            contrib[(t, j)] = yrow
+    out = np.zeros((len(tokens), x.shape[1]))
+    for n, t in enumerate(tokens):
+        for j in range(k + n_shared):
+            out[n] = out[n] + gates[t, j] * contrib[(t, j)]
+    return out

@@ -1,0 +1,58 @@
+"""Named MoE-layer workloads (shapes, dtypes and value distributions).
+
+Every workload is the DeepSeek-V3-lineage MoE feed-forward layer described in
+"Inkling, Dissected" (chapter 02, "Anatomy of one MoE layer"): 256 routed
+experts, 2 shared experts, top-6 routing.  The shapes below are synthetic
+stand-ins chosen to exercise the regimes that matter on one GPU:
+
+* ``A``  tiny fp32 layer (every tensor fp32), parity only;
+* ``B``  a prefill chunk in bf16;
+* ``C``  decode-sized: 64 tokens, bound by streaming expert weights;
+* ``D``  large batch: 16384 tokens at hidden 7168, bound by matrix cores;
+* ``E``  shape of ``D`` with a skewed router, run for 100 bias-update steps.
+
+No arithmetic of the method lives here.
+"""
+from dataclasses import dataclass, field
+
+
+@dataclass(frozen=True)
+class MoEConfig:
+    name: str
+    T: int                 # tokens in the batch
+    d: int                 # hidden size
+    F: int                 # expert ffn width (SwiGLU intermediate size)
+    E: int = 256           # routed experts
+    S: int = 2             # shared experts
+    k: int = 6             # routed experts kept per token
+    act: str = "bf16"      # dtype of x, y and the expert weights ("f32" or "bf16")
+    bias_range: float = 0.05   # balancing bias b ~ U[-bias_range, bias_range]
+    wd_std_from_F: bool = False  # W_down ~ N(0, 1/F) instead of N(0, 1/d)
+    gamma: float = 1e-3    # bias step size
+    skew_kappa: float = 0.0    # router skew strength (workload E only)
+    skew_zipf_s: float = 1.2   # exponent of the per-expert router offset
+    steps: int = 1         # bias-update steps the workload runs
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def pairs(self) -> int:
+        return self.T * self.k
+
+    def describe(self) -> str:
+        return (f"T={self.T} d={self.d} F={self.F} E={self.E}+{self.S} top-{self.k} "
+                f"{self.act}")
+
+
+CONFIGS = {
+    "A": MoEConfig("A", T=128, d=512, F=128, act="f32", bias_range=0.1,
+                   wd_std_from_F=True),
+    "B": MoEConfig("B", T=4096, d=2048, F=768, act="bf16", bias_range=0.05),
+    "C": MoEConfig("C", T=64, d=7168, F=2048, act="bf16", bias_range=0.0),
+    "D": MoEConfig("D", T=16384, d=7168, F=2048, act="bf16", bias_range=0.05),
+    "E": MoEConfig("E", T=16384, d=7168, F=2048, act="bf16", bias_range=0.0,
+                   skew_kappa=8.0, steps=100),
+}
+
+
+def get(name: str) -> MoEConfig:
+    return CONFIGS[name]

@@ -1,0 +1,342 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: values
+the pages print, closed forms, brute-force enumeration, invariants, or a
+special case that reduces to a library routine.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+from scipy.special import expit, log_expit, logsumexp
+
+from oracle import moe_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# ---------------------------------------------------------------- sigmoid
+
+def test_sigmoid_matches_library_and_closed_forms():
+    z = np.linspace(-40.0, 40.0, 2001)
+    assert np.array_equal(O.sigmoid(np.zeros(3)), np.full(3, 0.5))
+    np.testing.assert_allclose(O.sigmoid(z), expit(z), rtol=1e-15, atol=0)
+    # sigma(-z) = 1 - sigma(z)
+    np.testing.assert_allclose(O.sigmoid(-z), 1.0 - O.sigmoid(z), rtol=0, atol=2e-16)
+    assert O.sigmoid(np.array([math.log(3.0)]))[0] == pytest.approx(0.75, abs=1e-16)
+
+
+# ------------------------------------------------- worked example (02c)
+
+def test_worked_example_page_02c():
+    g = _golden("p1_02c_worked_example.json")
+    k = g["k"]
+    s = O.sigmoid(np.array([g["logits"]]))
+    np.testing.assert_allclose(s[0], g["affinity_printed"], atol=5e-4)
+
+    top, _ = O.select_topk(s, k)
+    assert list(top[0]) == g["unbiased"]["top"]
+    gates, _ = O.joint_gates(s, top, [])
+    np.testing.assert_allclose(gates[0], g["unbiased"]["gates_printed"], atol=1.5e-3)
+
+    b = np.array(g["bias"])
+    key = s + b[None, :]
+    np.testing.assert_allclose(key[0], g["biased"]["scores_printed"], atol=1.5e-3)
+    top_b, _ = O.select_topk(key, k)
+    assert list(top_b[0]) == g["biased"]["top"]
+    # gates of the new pair come from the raw affinities, not the biased keys
+    gates_b, _ = O.joint_gates(s, top_b, [])
+    np.testing.assert_allclose(gates_b[0], g["biased"]["gates_printed"], atol=1.5e-3)
+
+    sn = g["strong_need"]
+    key = np.array([sn["affinity"]]) + np.array([sn["bias"]])
+    top_s, _ = O.select_topk(key, k)
+    assert sn["must_keep"] in top_s[0]
+
+
+# ------------------------------------------------ top-k by brute force
+
+def _brute_force_topk(key, k):
+    """The unique k-subset A with: for all a in A, o not in A,
+    key_a > key_o or (key_a == key_o and a < o); listed in rank order."""
+    n = len(key)
+    found = []
+    for A in itertools.combinations(range(n), k):
+        rest = [o for o in range(n) if o not in A]
+        if all(key[a] > key[o] or (key[a] == key[o] and a < o) for a in A for o in rest):
+            found.append(A)
+    assert len(found) == 1
+    A = list(found[0])
+    # rank order: bubble the chosen ids by (key desc, id asc) with plain loops
+    for i in range(len(A)):
+        for j in range(len(A) - 1 - i):
+            a, c = A[j], A[j + 1]
+            if key[c] > key[a] or (key[c] == key[a] and c < a):
+                A[j], A[j + 1] = c, a
+    return A
+
+
+@pytest.mark.parametrize("k", [6, 3])
+def test_topk_brute_force_8_expert_toys(k):
+    rng = np.random.default_rng(1234 + k)
+    for trial in range(300):
+        if trial % 3 == 0:
+            # coarse grid: exact ties are frequent
+            key = rng.integers(0, 4, size=8) / 4.0
+        else:
+            s = expit(rng.normal(size=8))
+            b = rng.uniform(-0.05, 0.05, size=8)
+            key = s + b
+        top, margin = O.select_topk(key[None, :], k)
+        assert list(top[0]) == _brute_force_topk(list(key), k)
+        ks = sorted(key, reverse=True)
+        assert margin[0] == ks[k - 1] - ks[k]
+
+
+def test_uniform_scores_reduce_to_index_order():
+    # W_r = 0 gives s = 0.5 for every expert; with b = 0 the top-6 are 0..5
+    # and each of the 8 gates is exactly 1/8.
+    T, d = 5, 16
+    r = O.route(np.ones((T, d)), np.zeros((258, d)), np.zeros(256))
+    assert np.array_equal(r["topk_idx"], np.tile(np.arange(6), (T, 1)))
+    assert np.array_equal(r["gates"], np.full((T, 8), 0.125))
+    assert np.array_equal(r["idx"][:, 6:], np.tile([256, 257], (T, 1)))
+
+
+# ---------------------------------------------------------------- gates
+
+def _rand_router(T=64, d=32, E=256, S=2, seed=0, bias_range=0.05):
+    rng = np.random.default_rng(seed)
+    x = rng.normal(size=(T, d))
+    w = rng.normal(size=(E + S, d)) / math.sqrt(d)
+    b = rng.uniform(-bias_range, bias_range, size=E)
+    return x, w, b
+
+
+def test_gate_invariants_and_contributor_count():
+    x, w, b = _rand_router(seed=1)
+    r = O.route(x, w, b)
+    g = r["gates"]
+    assert g.shape == (64, 8)
+    np.testing.assert_allclose(g.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    assert np.all(g > 0) and np.all(g < 1)
+    for t in range(64):
+        routed = r["idx"][t, :6]
+        assert len(set(routed)) == 6 and np.all(routed < 256) and np.all(routed >= 0)
+        assert list(r["idx"][t, 6:]) == [256, 257]
+
+
+def test_gates_match_log_domain_normalisation():
+    # Hugging Face write-up: log-sigmoid -> logsumexp over the joint set of 8
+    # equals the ratio of sigmoids (before its extra route scaling).
+    x, w, b = _rand_router(seed=2)
+    r = O.route(x, w, b)
+    zsel = np.take_along_axis(r["z"], r["idx"], axis=1)
+    ls = log_expit(zsel)
+    g_log = np.exp(ls - logsumexp(ls, axis=1, keepdims=True))
+    np.testing.assert_allclose(r["gates"], g_log, rtol=1e-12, atol=0)
+
+
+def test_bias_steers_selection_only():
+    x, w, b = _rand_router(seed=3)
+    r_b = O.route(x, w, b)
+    r_0 = O.route(x, w, np.zeros(256))
+    same = np.all(np.sort(r_b["topk_idx"], 1) == np.sort(r_0["topk_idx"], 1), axis=1)
+    assert same.sum() > 0
+    # same chosen set => identical gates (as a multiset over the same experts)
+    for t in np.nonzero(same)[0]:
+        gb = dict(zip(r_b["idx"][t], r_b["gates"][t]))
+        g0 = dict(zip(r_0["idx"][t], r_0["gates"][t]))
+        for e in gb:
+            assert gb[e] == pytest.approx(g0[e], rel=1e-15, abs=0)
+    # gates are computed from raw sigmoids of the router logits
+    s_sel = np.take_along_axis(expit(x @ w.T), r_b["idx"], 1)
+    np.testing.assert_allclose(r_b["gates"], s_sel / s_sel.sum(1, keepdims=True),
+                               rtol=1e-14)
+
+
+def test_bias_only_flips_near_ties():
+    # If i is in the unbiased top-6 and s_i - s_(7) > 2 max|b|, i stays kept.
+    for seed in range(20):
+        x, w, b = _rand_router(T=128, seed=100 + seed, bias_range=0.02)
+        r_b = O.route(x, w, b)
+        s = r_b["s"][:, :256]
+        top0, _ = O.select_topk(s, 6)
+        s7 = np.sort(s, axis=1)[:, -7]
+        bound = 2 * np.abs(b).max()
+        for t in range(128):
+            for i in top0[t]:
+                if s[t, i] - s7[t] > bound:
+                    assert i in r_b["topk_idx"][t]
+
+
+# ------------------------------------------------------------- dispatch
+
+def test_dispatch_matches_explicit_loops():
+    rng = np.random.default_rng(5)
+    E, k, T = 16, 3, 37
+    top = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    dp = O.dispatch(top, n_routed=E)
+    counts = [0] * E
+    for t in range(T):
+        for j in range(k):
+            counts[top[t, j]] += 1
+    expect_sorted = []
+    for e in range(E):
+        for t in range(T):
+            for j in range(k):
+                if top[t, j] == e:
+                    expect_sorted.append(t * k + j)
+    assert list(dp["counts"]) == counts
+    assert list(dp["offsets"]) == [sum(counts[:e]) for e in range(E + 1)]
+    assert list(dp["sorted_pair"]) == expect_sorted
+    for pos, p in enumerate(expect_sorted):
+        assert dp["pair_pos"][p] == pos
+
+
+def test_dispatch_invariants_large():
+    x, w, b = _rand_router(T=512, seed=6)
+    r = O.route(x, w, b)
+    dp = O.dispatch(r["topk_idx"])
+    assert dp["counts"].sum() == 512 * 6
+    sp = dp["sorted_pair"]
+    assert np.array_equal(np.sort(sp), np.arange(512 * 6))
+    assert np.array_equal(dp["pair_pos"][sp], np.arange(512 * 6))
+    flat = r["topk_idx"].ravel()
+    for e in range(256):
+        seg = sp[dp["offsets"][e]:dp["offsets"][e + 1]]
+        assert np.all(flat[seg] == e)
+        assert np.all(np.diff(seg) > 0)
+
+
+# ---------------------------------------------- expert FFN + combine
+
+def _torch_swiglu(x, wg, wu, wd):
+    x, wg, wu, wd = (torch.as_tensor(np.asarray(a, np.float64)) for a in (x, wg, wu, wd))
+    return (torch.nn.functional.silu(x @ wg.T) * (x @ wu.T) @ wd.T).numpy()
+
+
+def _rand_weights(E, S, d, F, seed):
+    rng = np.random.default_rng(seed)
+    return {"w_gate": rng.normal(size=(E, F, d)) / math.sqrt(d),
+            "w_up": rng.normal(size=(E, F, d)) / math.sqrt(d),
+            "w_down": rng.normal(size=(E, d, F)) / math.sqrt(F),
+            "ws_gate": rng.normal(size=(S, F, d)) / math.sqrt(d),
+            "ws_up": rng.normal(size=(S, F, d)) / math.sqrt(d),
+            "ws_down": rng.normal(size=(S, d, F)) / math.sqrt(F)}
+
+
+def test_identical_experts_reduce_to_dense_swiglu():
+    # With one weight set shared by all 258 experts, sum(g) = 1 makes the
+    # layer a plain dense SwiGLU MLP whatever the routing.
+    T, d, F = 48, 32, 16
+    x, w, b = _rand_router(T=T, d=d, seed=7)
+    one = _rand_weights(1, 1, d, F, seed=8)
+    weights = {"w_gate": np.repeat(one["w_gate"], 256, 0),
+               "w_up": np.repeat(one["w_up"], 256, 0),
+               "w_down": np.repeat(one["w_down"], 256, 0),
+               "ws_gate": np.repeat(one["w_gate"], 2, 0),
+               "ws_up": np.repeat(one["w_up"], 2, 0),
+               "ws_down": np.repeat(one["w_down"], 2, 0)}
+    out = O.moe_forward(x, w, weights, b, 1e-3)
+    dense = _torch_swiglu(x, one["w_gate"][0], one["w_up"][0], one["w_down"][0])
+    np.testing.assert_allclose(out["y"], dense, rtol=1e-12, atol=1e-13)
+
+
+def test_single_active_expert_isolates_gate_slot():
+    # Zero every down projection except expert e*: y_t is then g_t[slot of e*]
+    # times that expert's SwiGLU output for tokens routed to e*, else 0.
+    T, d, F, E = 64, 16, 8, 256
+    x, w, b = _rand_router(T=T, d=d, seed=9)
+    weights = _rand_weights(E, 2, d, F, seed=10)
+    r = O.route(x, w, b)
+    e_star = int(np.bincount(r["topk_idx"].ravel(), minlength=E).argmax())
+    weights["w_down"] = np.zeros_like(weights["w_down"])
+    weights["w_down"][e_star] = _rand_weights(1, 1, d, F, seed=11)["w_down"][0]
+    weights["ws_down"] = np.zeros_like(weights["ws_down"])
+    out = O.moe_forward(x, w, weights, b, 1e-3)
+    ye = _torch_swiglu(x, weights["w_gate"][e_star], weights["w_up"][e_star],
+                       weights["w_down"][e_star])
+    s = expit(x @ w.T)
+    for t in range(T):
+        if e_star in r["topk_idx"][t]:
+            sel = list(r["topk_idx"][t]) + [256, 257]
+            g = s[t, e_star] / s[t, sel].sum()
+            np.testing.assert_allclose(out["y"][t], g * ye[t], rtol=1e-12, atol=1e-14)
+        else:
+            assert np.all(out["y"][t] == 0)
+
+
+def test_down_projection_linearity():
+    T, d, F = 40, 16, 8
+    x, w, b = _rand_router(T=T, d=d, seed=12)
+    weights = _rand_weights(256, 2, d, F, seed=13)
+    y1 = O.moe_forward(x, w, weights, b, 1e-3)["y"]
+    w2 = dict(weights)
+    w2["w_down"] = weights["w_down"] * 2.0
+    w2["ws_down"] = weights["ws_down"] * 2.0
+    y2 = O.moe_forward(x, w, w2, b, 1e-3)["y"]
+    assert np.array_equal(y2, 2.0 * y1)
+
+
+def test_grouped_matches_per_token_transcription():
+    T, d, F = 24, 16, 8
+    x, w, b = _rand_router(T=T, d=d, seed=14)
+    weights = _rand_weights(256, 2, d, F, seed=15)
+    out = O.moe_forward(x, w, weights, b, 1e-3)
+    experts = []
+    for e in range(256):
+        experts.append(lambda v, e=e: _torch_swiglu(v[None], weights["w_gate"][e],
+                                                    weights["w_up"][e],
+                                                    weights["w_down"][e])[0])
+    for s_ in range(2):
+        experts.append(lambda v, s_=s_: _torch_swiglu(v[None], weights["ws_gate"][s_],
+                                                      weights["ws_up"][s_],
+                                                      weights["ws_down"][s_])[0])
+    for t in range(T):
+        yt = O.moe_layer_per_token(x[t], experts, w, b)
+        np.testing.assert_allclose(out["y"][t], yt, rtol=1e-12, atol=1e-14)
+    # sampled-row helper agrees as well
+    get = lambda e: ((weights["w_gate"][e], weights["w_up"][e], weights["w_down"][e])
+                     if e < 256 else (weights["ws_gate"][e - 256], weights["ws_up"][e - 256],
+                                      weights["ws_down"][e - 256]))
+    rows = O.output_rows([0, 5, 23], x, out["router"]["topk_idx"],
+                         out["router"]["gates"], get)
+    np.testing.assert_allclose(rows, out["y"][[0, 5, 23]], rtol=1e-12, atol=1e-14)
+
+
+# ---------------------------------------------------------- bias update
+
+def test_bias_accumulates_page_02e():
+    g = _golden("p1_02e_bias_accumulates.json")
+    T, k, E = 128, 6, 256            # ideal load = 3
+    counts = np.full(E, 3)
+    counts[0] = 10                   # overloaded
+    counts[1], counts[2], counts[3] = 1, 0, 1   # underloaded (total kept at k*T)
+    assert counts.sum() == k * T
+    b = np.zeros(E, np.float32)
+    for _ in range(g["batches"]):
+        b = O.bias_update(counts, g["gamma"], b, T, k)
+    assert b.dtype == np.float32
+    assert b[0] == pytest.approx(g["expected_overloaded"], abs=1e-6)
+    assert b[1] == pytest.approx(-g["expected_overloaded"], abs=1e-6)
+    assert np.all(b[counts == 3] == 0.0)      # sign(0) = 0: untouched
+
+
+def test_bias_update_single_step_exact():
+    T, k = 64, 6                      # ideal load 1.5 is never hit exactly
+    counts = np.array([0, 1, 2, 3] * 64)
+    b0 = np.linspace(-0.1, 0.1, 256).astype(np.float32)
+    b1 = O.bias_update(counts, 1e-3, b0, T, k)
+    step = np.float32(1e-3)
+    expect = np.where(counts < 1.5, b0 + step, b0 - step).astype(np.float32)
+    assert np.array_equal(b1, expect)
