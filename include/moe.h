@@ -1,0 +1,213 @@
+/*
+ * moe.h -- C ABI of libmoe.so: the forward pass of a DeepSeek-V3-lineage
+ * mixture-of-experts feed-forward layer on one AMD MI355X (gfx950).
+ *
+ * The layer (sources are page title and section):
+ *
+ *   z   = x . W_r^T                       router logits over E routed + S shared
+ *   s   = sigmoid(z)                      independent affinities, no softmax
+ *   top = top-k of s[:E] + b              bias steers selection only
+ *   g   = s[top U shared] / sum(...)      one joint normalisation over k + S
+ *   y   = sum_i g_i * SwiGLU_i(x)         k routed + S shared contributions
+ *   b  += gamma * sign(Lbar - L)          after the batch, from the loads L
+ *
+ * - "Inkling, Dissected", chapter 02 "Anatomy of one MoE layer" and 02b
+ *   "Sigmoid, not softmax" (router equation, joint normalisation, the
+ *   per-token sketch of the layer);
+ * - "Inkling, Dissected", 02e "The aux-loss-free bias" (balancing rule);
+ * - "Under The Hood: Inkling from Thinking Machines", "MoE: the expert
+ *   configuration" (SwiGLU experts, shared experts of the same width) and
+ *   "The routing strategy: sigmoid + shared expert sink" (top-k over the
+ *   routed experts only, shared scores inside the normalisation).
+ *
+ * Conventions for every call:
+ * - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
+ *   are dense row-major, 16-byte aligned (256 recommended).  The library
+ *   never allocates, frees or synchronises; it keeps no mutable global
+ *   state.  Workspace is caller-provided device memory of at least
+ *   moe_workspace_size() bytes for that call.
+ * - Calls are asynchronous on `stream`.  The returned status covers host-side
+ *   validation (nothing is launched when it is not MOE_OK) plus launch errors
+ *   (MOE_ERR_HIP).  Device faults surface at the caller's next sync.
+ * - No C++ exception crosses this boundary.
+ * - Floating-point inputs holding NaN or Inf give undefined results.
+ *   Out-of-range expert ids handed to moe_dispatch are skipped (they never
+ *   cause out-of-bounds writes) and leave the outputs undefined.
+ * - Supported shapes (v1): E = 256, S = 2, k = 6; act == weight, either
+ *   MOE_F32 or MOE_BF16; d % 256 == 0; F % 128 == 0; 0 <= T and
+ *   T * (k + S) * max(d, F) < 2^40, T * k < 2^31.  Anything else is
+ *   MOE_ERR_UNSUPPORTED (or MOE_ERR_SHAPE for negative sizes).
+ *
+ * Intermediate layouts shared between calls:
+ * - pair p = t * k + j is token t's slot-j routed choice (rank order).
+ * - topk_idx  int32 [T, k]   routed expert ids in rank order (descending
+ *                            s + b, exact ties to the lower id).
+ * - gates     fp32  [T, k+S] slots 0..k-1 the routed experts in rank order,
+ *                            slots k..k+S-1 the shared experts.
+ * - counts    int32 [E]      L_e, routed selections per expert.
+ * - offsets   int32 [E+1]    exclusive prefix sum of counts.
+ * - sorted_pair int32 [T*k]  pair numbers grouped by expert, ascending p
+ *                            inside each expert (a stable permutation).
+ * - pair_pos  int32 [T*k]    inverse permutation: pair p sits at row
+ *                            pair_pos[p] of the expert-sorted buffers.
+ * - h         act   [(k+S)*T, F]  SwiGLU activations: rows 0..T*k-1 routed
+ *                            in sorted order, row k*T + s*T + t shared s.
+ * - y_routed  act   [T*k, d] expert outputs in sorted order;
+ *   y_shared  act   [S, T, d] shared-expert outputs.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                 */
+  MOE_ERR_SHAPE = 2,       /* negative size, or a non-finite gamma       */
+  MOE_ERR_DTYPE = 3,       /* unknown dtype, or act != weight            */
+  MOE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required    */
+  MOE_ERR_UNSUPPORTED = 5, /* valid but outside the v1 shape limits      */
+  MOE_ERR_HIP = 6          /* a kernel launch failed                     */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/* Which call a workspace size is asked for. */
+typedef enum {
+  MOE_CALL_ROUTER = 0,
+  MOE_CALL_DISPATCH = 1,
+  MOE_CALL_GATE_UP = 2,
+  MOE_CALL_DOWN = 3,
+  MOE_CALL_EXPERT_FFN = 4,
+  MOE_CALL_COMBINE = 5,
+  MOE_CALL_BIAS_UPDATE = 6,
+  MOE_CALL_FORWARD = 7
+} moe_call;
+
+/* Layer shape.  T tokens, hidden d, expert ffn width F, E routed experts,
+ * S shared experts, k routed experts per token; act is the dtype of x, h,
+ * y and the expert weights, weight must equal act.  The router weights and
+ * the bias are always fp32. */
+typedef struct {
+  int32_t T, d, F, E, S, k;
+  moe_dtype act, weight;
+} moe_desc;
+
+/* Weights of one layer.  Expert matrices are [out, in] row-major:
+ *   w_router [E+S, d] fp32  (rows E.. are the shared experts' vectors)
+ *   w_gate, w_up [E, F, d]   w_down [E, d, F]        (act dtype)
+ *   ws_gate, ws_up [S, F, d] ws_down [S, d, F]       (act dtype)        */
+typedef struct {
+  const float* w_router;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* ws_gate;
+  const void* ws_up;
+  const void* ws_down;
+} moe_weights;
+
+/* Optional routing outputs of moe_forward: each pointer may be NULL, in
+ * which case that tensor lives in the workspace. */
+typedef struct {
+  int32_t* topk_idx;     /* [T, k]   */
+  float* gates;          /* [T, k+S] */
+  float* margin;         /* [T] s+b of the k-th minus the (k+1)-th choice */
+  int32_t* counts;       /* [E]      */
+  int32_t* offsets;      /* [E+1]    */
+  int32_t* sorted_pair;  /* [T*k]    */
+  int32_t* pair_pos;     /* [T*k]    */
+} moe_routing;
+
+/* ABI version of the loaded library (MOE_ABI_VERSION). */
+int moe_abi_version(void);
+
+/* Static description of a status code; never NULL. */
+const char* moe_status_string(moe_status status);
+
+/* Device workspace bytes needed by `call` for this shape (0 when none).
+ * Returns the same validation errors as the call itself. */
+moe_status moe_workspace_size(const moe_desc* desc, moe_call call, size_t* bytes);
+
+/* Router ("Inkling, Dissected" 02b; "Under The Hood", routing strategy).
+ *   x [T, d] act, w_router [E+S, d] fp32, bias [E] fp32.
+ *   z = x . w_router^T accumulated in fp32 (exact bf16 splits of w_router on
+ *   the matrix cores, chunked accumulation); s = sigmoid(z) and the
+ *   selection keys s + b, the top-k and the gates are taken in fp64 from z.
+ *   Writes topk_idx [T, k], gates [T, k+S] and, when non-NULL, margin [T]. */
+moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router,
+                      const float* bias, int32_t* topk_idx, float* gates,
+                      float* margin_or_null, void* ws, size_t ws_bytes,
+                      hipStream_t stream);
+
+/* Dispatch: group the T*k (token, slot) pairs by expert ("Inkling,
+ * Dissected" 02: each token visits its 6 chosen experts; 02e: L_e is the
+ * number of tokens that selected e).  Histogram -> exclusive scan ->
+ * stable scatter; deterministic.  Writes counts, offsets, sorted_pair and
+ * pair_pos (layouts above). */
+moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
+                        int32_t* pair_pos, void* ws, size_t ws_bytes,
+                        hipStream_t stream);
+
+/* Gate/up half of every expert ("Under The Hood", expert configuration:
+ * SwiGLU experts): h = silu(X W_gate^T) * (X W_up^T), X the rows of x
+ * routed to the expert (rows gathered through sorted_pair) or all of x for
+ * a shared expert.  Matrix cores, fp32 accumulation, h rounded to act.
+ * Writes h [(k+S)*T, F]. */
+moe_status moe_expert_gate_up(const moe_desc* desc, const void* x,
+                              const moe_weights* w, const int32_t* offsets,
+                              const int32_t* sorted_pair, void* h, void* ws,
+                              size_t ws_bytes, hipStream_t stream);
+
+/* Down half of every expert: y = h W_down^T.  Reads h [(k+S)*T, F];
+ * writes y_routed [T*k, d] and y_shared [S, T, d]. */
+moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w,
+                           const int32_t* offsets, const void* h,
+                           void* y_routed, void* y_shared, void* ws,
+                           size_t ws_bytes, hipStream_t stream);
+
+/* Both halves: moe_expert_gate_up then moe_expert_down, h in the
+ * workspace. */
+moe_status moe_expert_ffn(const moe_desc* desc, const void* x,
+                          const moe_weights* w, const int32_t* offsets,
+                          const int32_t* sorted_pair, void* y_routed,
+                          void* y_shared, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/* Combine ("Inkling, Dissected" 02b: the gate-weighted sum over the 8
+ * contributors).  y[t] = sum_j gates[t,j] * y_routed[pair_pos[t*k+j]]
+ * (j = 0..k-1 in rank order) + sum_s gates[t,k+s] * y_shared[s,t], in fp32
+ * in exactly that order, rounded once to act.  Writes y [T, d]. */
+moe_status moe_combine(const moe_desc* desc, const void* y_routed,
+                       const void* y_shared, const float* gates,
+                       const int32_t* pair_pos, void* y, hipStream_t stream);
+
+/* Balancing-bias update ("Inkling, Dissected" 02e):
+ * bias[e] += gamma * sign(k*T - E*counts[e]) in fp32 (sign(0) = 0; the
+ * comparison is exact integer arithmetic).  gamma must be finite. */
+moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts,
+                           float gamma, float* bias, hipStream_t stream);
+
+/* The whole layer: router (with the incoming bias), dispatch, expert FFN,
+ * combine, then the bias update in place (the next batch routes with the
+ * new bias; gamma == 0 leaves it unchanged).  Writes y [T, d] and, when
+ * `routing` is non-NULL, its non-NULL members. */
+moe_status moe_forward(const moe_desc* desc, const void* x,
+                       const moe_weights* w, float* bias, float gamma, void* y,
+                       const moe_routing* routing_or_null, void* ws,
+                       size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -150,15 +150,19 @@ def silu(u):
     return _f64(u) * sigmoid(u)
 
 
+def swiglu_hidden(X, w_gate, w_up):
+    """The SwiGLU hidden activations silu(X Wg^T) * (X Wu^T)."""
+    X = _f64(X)
+    return silu(X @ _f64(w_gate).T) * (X @ _f64(w_up).T)
+
+
 def swiglu(X, w_gate, w_up, w_down):
     """One SwiGLU expert on the rows of X: (silu(X Wg^T) * (X Wu^T)) Wd^T.
 
     ("Under The Hood: Inkling", "MoE: the expert configuration": each expert
     is a SwiGLU FFN.)  Weights are [out, in].
     """
-    X = _f64(X)
-    h = silu(X @ _f64(w_gate).T) * (X @ _f64(w_up).T)
-    return h @ _f64(w_down).T
+    return swiglu_hidden(X, w_gate, w_up) @ _f64(w_down).T
 
 
 def expert_ffn(x, weights, offsets, sorted_pair, k=6):

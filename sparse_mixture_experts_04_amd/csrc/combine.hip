@@ -1,0 +1,98 @@
+// Combine: y_t = sum over the 8 contributors of g * expert output.
+//
+// "Inkling, Dissected", 02 and 02b: the layer output is the gate-weighted
+// sum of the 6 chosen routed experts' outputs and the 2 shared experts'
+// outputs.  Each output element is summed in fp32 in a fixed order
+// (routed slots in rank order, then the shared experts), from rows found
+// through pair_pos, with no atomics: the result is deterministic.
+#include "common.h"
+
+namespace moe {
+
+template <typename T> struct Vec;
+template <> struct Vec<bf16_t> {
+  static constexpr int N = 8;  // 16-byte loads
+  __device__ static void load(const bf16_t* p, float (&v)[8]) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static void store(bf16_t* p, const float (&v)[8]) {
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
+             (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
+    *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float* p, float (&v)[4]) {
+    const float4 u = *reinterpret_cast<const float4*>(p);
+    v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+  }
+  __device__ static void store(float* p, const float (&v)[4]) {
+    *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+// Block b handles token b / nchunk, columns (b % nchunk) * 256 * VEC + ...
+template <typename T, int K, int S>
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yr,
+                                                      const T* __restrict__ ys,
+                                                      const float* __restrict__ gates,
+                                                      const int32_t* __restrict__ pair_pos,
+                                                      int Tn, int d, int nchunk,
+                                                      T* __restrict__ y) {
+  constexpr int V = Vec<T>::N;
+  const int t = blockIdx.x / nchunk;
+  const int c0 = ((blockIdx.x % nchunk) * 256 + threadIdx.x) * V;
+  if (c0 >= d) return;
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+  float v[V];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const float g = gates[static_cast<size_t>(t) * (K + S) + j];
+    const size_t row = static_cast<size_t>(pair_pos[static_cast<size_t>(t) * K + j]);
+    Vec<T>::load(yr + row * d + c0, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s) {
+    const float g = gates[static_cast<size_t>(t) * (K + S) + K + s];
+    Vec<T>::load(ys + (static_cast<size_t>(s) * Tn + t) * d + c0, v);
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+  }
+  Vec<T>::store(y + static_cast<size_t>(t) * d + c0, acc);
+}
+
+hipError_t launch_combine(const Shape& s, const void* y_routed, const void* y_shared,
+                          const float* gates, const int32_t* pair_pos, void* y,
+                          hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (s.bf16) {
+    const int nchunk = (s.d + 256 * 8 - 1) / (256 * 8);
+    const long long blocks = static_cast<long long>(s.T) * nchunk;
+    combine_kernel<bf16_t, 6, 2><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
+        static_cast<const bf16_t*>(y_routed), static_cast<const bf16_t*>(y_shared), gates,
+        pair_pos, s.T, s.d, nchunk, static_cast<bf16_t*>(y));
+  } else {
+    const int nchunk = (s.d + 256 * 4 - 1) / (256 * 4);
+    const long long blocks = static_cast<long long>(s.T) * nchunk;
+    combine_kernel<float, 6, 2><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
+        static_cast<const float*>(y_routed), static_cast<const float*>(y_shared), gates,
+        pair_pos, s.T, s.d, nchunk, static_cast<float*>(y));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,92 @@
+// Internal declarations shared by the HIP sources of libmoe.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bfloat16 bits
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// Round to nearest even; NaN stays NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<bf16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> struct ActTraits;
+template <> struct ActTraits<float> {
+  __device__ static float load(const float* p) { return *p; }
+  __device__ static void store(float* p, float v) { *p = v; }
+};
+template <> struct ActTraits<bf16_t> {
+  __device__ static float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static void store(bf16_t* p, float v) { *p = f32_to_bf16(v); }
+};
+
+// Shape handed to the launchers (validated on the host beforehand).
+struct Shape {
+  int T, d, F, E, S, k;
+  bool bf16;
+};
+
+// Router columns are padded to a multiple of the router's column tile.
+constexpr int kRouterColTile = 64;
+constexpr int kRouterChunk = 256;  // K granularity of the split across workgroups
+inline int router_cols_padded(const Shape& s) {
+  int n = s.E + s.S;
+  return (n + kRouterColTile - 1) / kRouterColTile * kRouterColTile;
+}
+int router_ksplits(const Shape& s);
+
+// Dispatch segments: pairs handled by one stable-scatter wave.
+constexpr int kDispatchSeg = 512;
+inline int dispatch_segments(const Shape& s) {
+  long long p = static_cast<long long>(s.T) * s.k;
+  return static_cast<int>((p + kDispatchSeg - 1) / kDispatchSeg);
+}
+
+// Expert GEMM row tile chosen for a shape (routed rows per expert decide).
+int ffn_row_tile(const Shape& s);
+
+// ---- launchers (return hipSuccess or the launch error) -------------------
+hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
+                         const float* bias, int32_t* topk_idx, float* gates,
+                         float* margin, bf16_t* wplanes, double* partial,
+                         hipStream_t st);
+
+hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* counts,
+                           int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                           int32_t* seg_counts, hipStream_t st);
+
+hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile,
+                            int32_t* tile_start, hipStream_t st);
+
+hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
+                          const void* wsg, const void* wsu, const int32_t* offsets,
+                          const int32_t* sorted_pair, const int32_t* tile_start,
+                          int row_tile, void* h, hipStream_t st);
+
+hipError_t launch_down(const Shape& s, const void* wd, const void* wsd,
+                       const int32_t* offsets, const int32_t* tile_start, int row_tile,
+                       const void* h, void* y_routed, void* y_shared, hipStream_t st);
+
+hipError_t launch_combine(const Shape& s, const void* y_routed, const void* y_shared,
+                          const float* gates, const int32_t* pair_pos, void* y,
+                          hipStream_t st);
+
+hipError_t launch_bias_update(const Shape& s, const int32_t* counts, float gamma,
+                              float* bias, hipStream_t st);
+
+}  // namespace moe

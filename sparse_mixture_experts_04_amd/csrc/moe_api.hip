@@ -1,0 +1,306 @@
+// C ABI of libmoe.so: host-side validation, workspace layout and the order
+// of kernel launches.  Declarations and the meaning of every argument are
+// in include/moe.h.
+#include <cmath>
+
+#include "../../include/moe.h"
+#include "common.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+moe_status check_desc(const moe_desc* d) {
+  if (!d) return MOE_ERR_NULL;
+  if (d->T < 0 || d->d <= 0 || d->F <= 0 || d->E <= 0 || d->S < 0 || d->k <= 0)
+    return MOE_ERR_SHAPE;
+  if ((d->act != MOE_F32 && d->act != MOE_BF16) || d->weight != d->act) return MOE_ERR_DTYPE;
+  if (d->E != 256 || d->S != 2 || d->k != 6) return MOE_ERR_UNSUPPORTED;
+  if (d->d % 256 != 0 || d->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  const long long T = d->T;
+  if (T * d->k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  const long long wide = d->d > d->F ? d->d : d->F;
+  if (T * (d->k + d->S) * wide >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Shape to_shape(const moe_desc* d) {
+  Shape s;
+  s.T = d->T;
+  s.d = d->d;
+  s.F = d->F;
+  s.E = d->E;
+  s.S = d->S;
+  s.k = d->k;
+  s.bf16 = d->act == MOE_BF16;
+  return s;
+}
+
+size_t esize(const Shape& s) { return s.bf16 ? 2 : 4; }
+
+// Workspace carving: a bump allocator over the caller's buffer.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  template <typename T> T* take(size_t count) {
+    T* p = reinterpret_cast<T*>(base ? base + used : nullptr);
+    used = align_up(used + count * sizeof(T));
+    return p;
+  }
+};
+
+struct RouterWs { bf16_t* planes; double* partial; };
+RouterWs carve_router(Carver& c, const Shape& s) {
+  RouterWs r;
+  const size_t npad = router_cols_padded(s);
+  r.planes = c.take<bf16_t>(3 * npad * s.d);
+  r.partial = c.take<double>(static_cast<size_t>(router_ksplits(s)) * s.T * npad);
+  return r;
+}
+int32_t* carve_dispatch(Carver& c, const Shape& s) {
+  return c.take<int32_t>(static_cast<size_t>(dispatch_segments(s)) * s.E + 1);
+}
+int32_t* carve_plan(Carver& c, const Shape& s) { return c.take<int32_t>(s.E + s.S + 1); }
+void* carve_h(Carver& c, const Shape& s) {
+  return c.take<char>(static_cast<size_t>(s.k + s.S) * s.T * s.F * esize(s));
+}
+
+struct FwdWs {
+  int32_t* topk;
+  float* gates;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* sorted_pair;
+  int32_t* pair_pos;
+  RouterWs router;
+  int32_t* seg;
+  int32_t* plan;
+  void* h;
+  void* y_routed;
+  void* y_shared;
+};
+FwdWs carve_forward(Carver& c, const Shape& s) {
+  FwdWs w;
+  const size_t kT = static_cast<size_t>(s.k) * s.T;
+  w.topk = c.take<int32_t>(kT);
+  w.gates = c.take<float>(static_cast<size_t>(s.k + s.S) * s.T);
+  w.counts = c.take<int32_t>(s.E);
+  w.offsets = c.take<int32_t>(s.E + 1);
+  w.sorted_pair = c.take<int32_t>(kT);
+  w.pair_pos = c.take<int32_t>(kT);
+  w.router = carve_router(c, s);
+  w.seg = carve_dispatch(c, s);
+  w.plan = carve_plan(c, s);
+  w.h = carve_h(c, s);
+  w.y_routed = c.take<char>(kT * s.d * esize(s));
+  w.y_shared = c.take<char>(static_cast<size_t>(s.S) * s.T * s.d * esize(s));
+  return w;
+}
+
+size_t ws_bytes_for(const Shape& s, moe_call call) {
+  Carver c{nullptr};
+  switch (call) {
+    case MOE_CALL_ROUTER: carve_router(c, s); break;
+    case MOE_CALL_DISPATCH: carve_dispatch(c, s); break;
+    case MOE_CALL_GATE_UP:
+    case MOE_CALL_DOWN: carve_plan(c, s); break;
+    case MOE_CALL_EXPERT_FFN: carve_plan(c, s); carve_h(c, s); break;
+    case MOE_CALL_FORWARD: carve_forward(c, s); break;
+    default: break;
+  }
+  return c.used;
+}
+
+moe_status check_ws(const Shape& s, moe_call call, const void* ws, size_t ws_bytes) {
+  const size_t need = ws_bytes_for(s, call);
+  if (need == 0) return MOE_OK;
+  if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+bool weights_ok(const moe_weights* w) {
+  return w && w->w_gate && w->w_up && w->w_down && w->ws_gate && w->ws_up && w->ws_down;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_NULL: return "a required pointer is NULL";
+    case MOE_ERR_SHAPE: return "invalid size or non-finite gamma";
+    case MOE_ERR_DTYPE: return "unsupported dtype (act and weight must both be f32 or bf16)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_UNSUPPORTED: return "shape outside the supported limits";
+    case MOE_ERR_HIP: return "HIP kernel launch failed";
+  }
+  return "unknown status";
+}
+
+moe_status moe_workspace_size(const moe_desc* desc, moe_call call, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  const moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (call < MOE_CALL_ROUTER || call > MOE_CALL_FORWARD) return MOE_ERR_SHAPE;
+  *bytes = ws_bytes_for(to_shape(desc), call);
+  return MOE_OK;
+}
+
+moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router,
+                      const float* bias, int32_t* topk_idx, float* gates,
+                      float* margin_or_null, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (s.T > 0 && (!x || !w_router || !bias || !topk_idx || !gates)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_ROUTER, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  const RouterWs r = carve_router(c, s);
+  return hip_status(launch_router(s, x, w_router, bias, topk_idx, gates, margin_or_null,
+                                  r.planes, r.partial, stream));
+}
+
+moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts,
+                        int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos, void* ws,
+                        size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (s.T > 0 && (!topk_idx || !sorted_pair || !pair_pos)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_DISPATCH, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  int32_t* seg = carve_dispatch(c, s);
+  return hip_status(
+      launch_dispatch(s, topk_idx, counts, offsets, sorted_pair, pair_pos, seg, stream));
+}
+
+moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_weights* w,
+                              const int32_t* offsets, const int32_t* sorted_pair, void* h,
+                              void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!weights_ok(w) || !offsets) return MOE_ERR_NULL;
+  if (s.T > 0 && (!x || !sorted_pair || !h)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  int32_t* plan = carve_plan(c, s);
+  const int mt = ffn_row_tile(s);
+  hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
+  if (e == hipSuccess)
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
+                       plan, mt, h, stream);
+  return hip_status(e);
+}
+
+moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w, const int32_t* offsets,
+                           const void* h, void* y_routed, void* y_shared, void* ws,
+                           size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!weights_ok(w) || !offsets) return MOE_ERR_NULL;
+  if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  int32_t* plan = carve_plan(c, s);
+  const int mt = ffn_row_tile(s);
+  hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
+  if (e == hipSuccess)
+    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, stream);
+  return hip_status(e);
+}
+
+moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const moe_weights* w,
+                          const int32_t* offsets, const int32_t* sorted_pair, void* y_routed,
+                          void* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!weights_ok(w) || !offsets) return MOE_ERR_NULL;
+  if (s.T > 0 && (!x || !sorted_pair || !y_routed || !y_shared)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_EXPERT_FFN, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  int32_t* plan = carve_plan(c, s);
+  void* h = carve_h(c, s);
+  const int mt = ffn_row_tile(s);
+  hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
+  if (e == hipSuccess)
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
+                       plan, mt, h, stream);
+  if (e == hipSuccess)
+    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, stream);
+  return hip_status(e);
+}
+
+moe_status moe_combine(const moe_desc* desc, const void* y_routed, const void* y_shared,
+                       const float* gates, const int32_t* pair_pos, void* y,
+                       hipStream_t stream) {
+  const moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (s.T > 0 && (!y_routed || !y_shared || !gates || !pair_pos || !y)) return MOE_ERR_NULL;
+  return hip_status(launch_combine(s, y_routed, y_shared, gates, pair_pos, y, stream));
+}
+
+moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts, float gamma,
+                           float* bias, hipStream_t stream) {
+  const moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!counts || !bias) return MOE_ERR_NULL;
+  if (!std::isfinite(gamma)) return MOE_ERR_SHAPE;
+  return hip_status(launch_bias_update(to_shape(desc), counts, gamma, bias, stream));
+}
+
+moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
+                       float gamma, void* y, const moe_routing* routing, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!weights_ok(w) || !w->w_router || !bias) return MOE_ERR_NULL;
+  if (s.T > 0 && (!x || !y)) return MOE_ERR_NULL;
+  if (!std::isfinite(gamma)) return MOE_ERR_SHAPE;
+  if ((st = check_ws(s, MOE_CALL_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  FwdWs f = carve_forward(c, s);
+  float* margin = nullptr;
+  if (routing) {
+    if (routing->topk_idx) f.topk = routing->topk_idx;
+    if (routing->gates) f.gates = routing->gates;
+    if (routing->counts) f.counts = routing->counts;
+    if (routing->offsets) f.offsets = routing->offsets;
+    if (routing->sorted_pair) f.sorted_pair = routing->sorted_pair;
+    if (routing->pair_pos) f.pair_pos = routing->pair_pos;
+    margin = routing->margin;
+  }
+  const int mt = ffn_row_tile(s);
+  hipError_t e = launch_router(s, x, w->w_router, bias, f.topk, f.gates, margin,
+                               f.router.planes, f.router.partial, stream);
+  if (e == hipSuccess)
+    e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg, stream);
+  if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
+  if (e == hipSuccess)
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, f.offsets,
+                       f.sorted_pair, f.plan, mt, f.h, stream);
+  if (e == hipSuccess)
+    e = launch_down(s, w->w_down, w->ws_down, f.offsets, f.plan, mt, f.h, f.y_routed,
+                    f.y_shared, stream);
+  if (e == hipSuccess)
+    e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
+  if (e == hipSuccess && gamma != 0.0f) e = launch_bias_update(s, f.counts, gamma, bias, stream);
+  return hip_status(e);
+}
+
+}  // extern "C"

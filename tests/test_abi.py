@@ -1,0 +1,131 @@
+"""The C ABI loads, exports what include/moe.h declares, and validates on the
+host (no GPU needed: every call here fails validation before any launch)."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+L = pytest.importorskip("sparse_mixture_experts_04_amd._lib")
+lib = L.lib
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(L.SYMBOLS) == names
+
+
+def test_version_and_status_strings():
+    assert lib.moe_abi_version() == 1
+    for code in range(7):
+        s = lib.moe_status_string(code)
+        assert s and isinstance(s, bytes)
+    assert lib.moe_status_string(99) == b"unknown status"
+
+
+def desc(**kw):
+    base = dict(T=128, d=512, F=128, E=256, S=2, k=6, act=L.F32, weight=L.F32)
+    base.update(kw)
+    return L.Desc(**base)
+
+
+def ws_size(d, call):
+    n = ctypes.c_size_t(0)
+    st = lib.moe_workspace_size(ctypes.byref(d) if d is not None else None, call,
+                                ctypes.byref(n))
+    return st, n.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1), 2), (dict(d=0), 2), (dict(k=0), 2),
+    (dict(act=L.BF16), 3), (dict(act=7, weight=7), 3),
+    (dict(E=128), 5), (dict(S=1), 5), (dict(k=8), 5),
+    (dict(d=384), 5), (dict(F=96), 5),
+    (dict(T=1 << 29), 5),
+])
+def test_desc_validation(kw, code):
+    st, _ = ws_size(desc(**kw), L.CALL_FORWARD)
+    assert st == code
+
+
+def test_null_desc_and_null_out():
+    st, _ = ws_size(None, L.CALL_FORWARD)
+    assert st == 1
+    assert lib.moe_workspace_size(ctypes.byref(desc()), L.CALL_FORWARD, None) == 1
+
+
+def test_workspace_sizes_are_consistent():
+    for act in (L.F32, L.BF16):
+        d = desc(act=act, weight=act, T=4096, d=2048, F=768)
+        sizes = {c: ws_size(d, c)[1] for c in range(8)}
+        assert ws_size(d, 8)[0] == 2
+        assert sizes[L.CALL_COMBINE] == 0 and sizes[L.CALL_BIAS_UPDATE] == 0
+        assert sizes[L.CALL_EXPERT_FFN] > sizes[L.CALL_GATE_UP] > 0
+        assert sizes[L.CALL_FORWARD] >= max(sizes[c] for c in range(7))
+        # h alone: (k+S) * T * F elements of the act dtype
+        esz = 4 if act == L.F32 else 2
+        assert sizes[L.CALL_EXPERT_FFN] >= 8 * 4096 * 768 * esz
+    # T = 0 is valid
+    assert ws_size(desc(T=0), L.CALL_FORWARD)[0] == 0
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_calls_reject_bad_arguments_before_launch():
+    d = desc()
+    P = FAKE
+    # missing pointers
+    assert lib.moe_router(ctypes.byref(d), None, P, P, P, P, None, P, 1 << 30, None) == 1
+    assert lib.moe_dispatch(ctypes.byref(d), P, None, P, P, P, P, 1 << 30, None) == 1
+    w = L.Weights(w_router=0x1000, w_gate=0x1000, w_up=0x1000, w_down=None,
+                  ws_gate=0x1000, ws_up=0x1000, ws_down=0x1000)
+    assert lib.moe_expert_ffn(ctypes.byref(d), P, ctypes.byref(w), P, P, P, P, P, 1 << 30,
+                              None) == 1
+    assert lib.moe_combine(ctypes.byref(d), P, P, None, P, P, None) == 1
+    assert lib.moe_bias_update(ctypes.byref(d), None, 1e-3, P, None) == 1
+    # workspace too small
+    _, need = ws_size(d, L.CALL_ROUTER)
+    assert lib.moe_router(ctypes.byref(d), P, P, P, P, P, None, P, need - 1, None) == 4
+    assert lib.moe_router(ctypes.byref(d), P, P, P, P, P, None, None, need, None) == 4
+    _, need = ws_size(d, L.CALL_DISPATCH)
+    assert lib.moe_dispatch(ctypes.byref(d), P, P, P, P, P, P, need - 1, None) == 4
+    # non-finite gamma
+    assert lib.moe_bias_update(ctypes.byref(d), P, math.inf, P, None) == 2
+    assert lib.moe_bias_update(ctypes.byref(d), P, math.nan, P, None) == 2
+    wf = L.Weights(*([0x1000] * 7))
+    _, need = ws_size(d, L.CALL_FORWARD)
+    assert lib.moe_forward(ctypes.byref(d), P, ctypes.byref(wf), P, math.nan, P, None, P,
+                           need, None) == 2
+    # unsupported dtype combination
+    bad = desc(act=L.BF16, weight=L.F32)
+    assert lib.moe_forward(ctypes.byref(bad), P, ctypes.byref(wf), P, 1e-3, P, None, P,
+                           need, None) == 3
+    # forward without the router weights
+    wf2 = L.Weights(None, *([0x1000] * 6))
+    assert lib.moe_forward(ctypes.byref(d), P, ctypes.byref(wf2), P, 1e-3, P, None, P,
+                           need, None) == 1
+
+
+def test_binding_rejects_host_tensors():
+    torch = pytest.importorskip("torch")
+    d = L.make_desc(4, 512, 128, torch.float32)
+    x = torch.zeros(4, 512)
+    with pytest.raises(ValueError):
+        L._ptr(x, torch.float32, (4, 512), "x")
+    with pytest.raises(TypeError):
+        L.make_desc(4, 512, 128, torch.float16)
+    assert d.T == 4
