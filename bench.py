@@ -1,0 +1,245 @@
+"""Benchmark of the MoE-layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one ``moe_forward`` call (router, dispatch, expert SwiGLU GEMMs,
+combine, bias update) over one batch already resident in HBM:
+
+* headline workload: T=16384 tokens, d=7168, F=2048, 256 routed + 2 shared
+  experts, top-6, bf16 weights and activations, fp32 router;
+* decode workload (reported alongside): the same layer at T=64.
+
+Prints one JSON line.  ``value`` is tokens/s of the headline workload;
+``roofline`` is for its dominant kernel, the grouped gate/up GEMM (matrix
+cores), timed with HIP events on the stream it runs on; ``decode`` carries
+the T=64 numbers against HBM bandwidth; ``cpu_baseline`` times the CPU
+oracle on a bounded sample of the headline workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (T=16384) / % HBM BW (T=64 decode)"
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="D", help="headline workload (D)")
+    ap.add_argument("--decode-workload", default="C")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    return ap.parse_args()
+
+
+def expert_flops(cfg):
+    # per (token, expert) pair: gate and up GEMMs 2*(2*d*F), down 2*d*F
+    pairs = (cfg.k + cfg.S) * cfg.T
+    return 4.0 * cfg.d * cfg.F * pairs, 2.0 * cfg.d * cfg.F * pairs
+
+
+def setup(cfg, torch, L, synth):
+    inp = synth.make_inputs(cfg, device="cuda")
+    desc = L.make_desc(cfg.T, cfg.d, cfg.F, synth.act_dtype(cfg))
+    w = L.weights_from(inp)
+    y = torch.empty((cfg.T, cfg.d), dtype=synth.act_dtype(cfg), device="cuda")
+    counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
+    ws = L.alloc_workspace(desc, L.CALL_FORWARD, "cuda")
+    torch.cuda.synchronize()
+    return inp, desc, w, y, counts, ws
+
+
+def time_forward(cfg, steps, warmup, torch, L, synth):
+    inp, desc, w, y, counts, ws = setup(cfg, torch, L, synth)
+    bias = inp["bias"].clone()
+    routing = {"counts": counts}
+
+    def step():
+        L.forward(desc, inp["x"], w, bias, cfg.gamma, y, routing, ws=ws)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_events = ev0.elapsed_time(ev1) / steps
+    return inp, desc, w, ws, counts, wall * 1e3 / steps, ms_events
+
+
+def time_stages(cfg, inp, desc, w, steps, torch, L, synth):
+    """The same path through the per-stage entry points, with HIP events
+    around each stage on torch's current stream (the stream every call
+    launches on).  Returns average ms per stage."""
+    dev = "cuda"
+    T, k, S, E = cfg.T, cfg.k, cfg.S, cfg.E
+    act = synth.act_dtype(cfg)
+    i32, f32 = torch.int32, torch.float32
+    topk = torch.empty((T, k), dtype=i32, device=dev)
+    gates = torch.empty((T, k + S), dtype=f32, device=dev)
+    counts = torch.empty(E, dtype=i32, device=dev)
+    offsets = torch.empty(E + 1, dtype=i32, device=dev)
+    sp = torch.empty(T * k, dtype=i32, device=dev)
+    pp = torch.empty(T * k, dtype=i32, device=dev)
+    h = torch.empty(((k + S) * T, cfg.F), dtype=act, device=dev)
+    yr = torch.empty((T * k, cfg.d), dtype=act, device=dev)
+    ys = torch.empty((S, T, cfg.d), dtype=act, device=dev)
+    y = torch.empty((T, cfg.d), dtype=act, device=dev)
+    bias = inp["bias"].clone()
+    wsr = L.alloc_workspace(desc, L.CALL_ROUTER, dev)
+    wsd = L.alloc_workspace(desc, L.CALL_DISPATCH, dev)
+    wsg = L.alloc_workspace(desc, L.CALL_GATE_UP, dev)
+    wsn = L.alloc_workspace(desc, L.CALL_DOWN, dev)
+    names = ["router", "dispatch", "gate_up", "down", "combine", "bias_update"]
+    calls = [
+        lambda: L.router(desc, inp["x"], inp["w_router"], bias, topk, gates, ws=wsr),
+        lambda: L.dispatch(desc, topk, counts, offsets, sp, pp, ws=wsd),
+        lambda: L.expert_gate_up(desc, inp["x"], w, offsets, sp, h, ws=wsg),
+        lambda: L.expert_down(desc, w, offsets, h, yr, ys, ws=wsn),
+        lambda: L.combine(desc, yr, ys, gates, pp, y),
+        lambda: L.bias_update(desc, counts, cfg.gamma, bias),
+    ]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+           for _ in range(steps)]
+    for s in range(steps):
+        evs[s][0].record()
+        for i, c in enumerate(calls):
+            c()
+            evs[s][i + 1].record()
+    torch.cuda.synchronize()
+    out = {}
+    for i, n in enumerate(names):
+        out[n] = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
+    return out
+
+
+def decode_bytes(cfg, counts):
+    n_active = int((counts > 0).sum())
+    esz = 2 if cfg.act == "bf16" else 4
+    per_expert = 3 * cfg.F * cfg.d * esz
+    router = (cfg.E + cfg.S) * cfg.d * 4
+    xy = 2 * cfg.T * cfg.d * esz
+    return n_active * per_expert + cfg.S * per_expert + router + xy, n_active
+
+
+def cpu_baseline(cfg, inp, ntok, torch):
+    """The oracle, as it stands, on the first ``ntok`` tokens of the batch.
+    Inputs are copied to the host before the clock starts."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from oracle import moe_oracle as O
+
+    x = inp["x"][:ntok].float().cpu().numpy()
+    wr = inp["w_router"].cpu().numpy()
+    bias = inp["bias"].cpu().numpy()
+    # the experts this sample needs, fetched before timing
+    r = O.route(x, wr, bias, n_routed=cfg.E, k=cfg.k)
+    need = sorted(set(r["topk_idx"].ravel().tolist()))
+
+    class Lazy:
+        def __init__(self, t, ids):
+            self.n = t.shape[0]
+            self.d = {e: t[e].float().cpu().numpy() for e in ids}
+
+        def __getitem__(self, e):
+            return self.d[e]
+
+        def __len__(self):
+            return self.n
+
+    weights = {"w_gate": Lazy(inp["w_gate"], need), "w_up": Lazy(inp["w_up"], need),
+               "w_down": Lazy(inp["w_down"], need)}
+    for n in ("ws_gate", "ws_up", "ws_down"):
+        weights[n] = [inp[n][s].float().cpu().numpy() for s in range(cfg.S)]
+    t0 = time.perf_counter()
+    out = O.moe_forward(x, wr, weights, bias, cfg.gamma, k=cfg.k)
+    dt = time.perf_counter() - t0
+    assert out["y"].shape == (ntok, cfg.d)
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "seconds": round(dt, 2),
+            "sample": (f"first {ntok} tokens of the T={cfg.T} batch: full oracle forward "
+                       f"(fp64 router, dispatch, {len(need)} routed + {cfg.S} shared SwiGLU "
+                       f"experts, combine, bias update)")}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
+              f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from sparse_mixture_experts_04_amd import _lib as L
+    from sparse_mixture_experts_04_amd import configs, synth
+
+    cfg = configs.get(args.workload)
+    inp, desc, w, ws, counts, ms_wall, ms_ev = time_forward(cfg, args.steps, args.warmup,
+                                                            torch, L, synth)
+    stages = time_stages(cfg, inp, desc, w, max(3, min(args.steps, 10)), torch, L, synth)
+    f_gu, f_dn = expert_flops(cfg)
+    ms = ms_wall
+    tokens_s = cfg.T / (ms / 1e3)
+    gu_tflops = f_gu / (stages["gate_up"] / 1e3) / 1e12
+    result = {
+        "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1/d) weights, N(0,1) tokens)",
+        "config": {"workload": f"large-batch MoE layer, {cfg.describe()}, fp32 router",
+                   "T": cfg.T, "d": cfg.d, "F": cfg.F, "experts": f"{cfg.E}+{cfg.S}",
+                   "top_k": cfg.k},
+        "layer_tflops": round((f_gu + f_dn) / (ms / 1e3) / 1e12, 1),
+        "layer_mfma_frac": round((f_gu + f_dn) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ms_per_step_events": round(ms_ev, 4),
+        "stage_ms": {k: round(v, 4) for k, v in stages.items()},
+        "roofline": {"kernel": "ffn_bf16_kernel (grouped gate/up GEMM + SwiGLU)",
+                     "bound": "mfma", "achieved": round(gu_tflops, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+    }
+    max_load = counts.max().item()
+    result["max_over_mean_load"] = round(max_load / (cfg.T * cfg.k / cfg.E), 3)
+    del ws
+    if not args.no_decode:
+        dc = configs.get(args.decode_workload)
+        dinp = time_forward(dc, max(args.steps, 20), args.warmup, torch, L, synth)
+        d_inp, d_desc, d_w, d_ws, d_counts, d_ms, d_ms_ev = dinp
+        d_stages = time_stages(dc, d_inp, d_desc, d_w, 10, torch, L, synth)
+        nbytes, n_active = decode_bytes(dc, d_counts.cpu())
+        gbs = nbytes / (d_ms / 1e3) / 1e9
+        result["decode"] = {
+            "workload": f"decode MoE layer, {dc.describe()}, fp32 router",
+            "tokens_s": round(dc.T / (d_ms / 1e3), 1), "ms_per_step": round(d_ms, 4),
+            "stage_ms": {k: round(v, 4) for k, v in d_stages.items()},
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
+                         "bytes": nbytes, "active_experts": n_active,
+                         "scope": "whole moe_forward step"}}
+        del d_inp, d_ws
+        torch.cuda.empty_cache()
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

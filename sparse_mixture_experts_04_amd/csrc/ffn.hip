@@ -112,11 +112,17 @@ struct FfnArgs {
 
 // -------------------------------------------------------- bf16 MFMA GEMM
 
-// Tile: MT rows x 256 weight rows, K step 64, 256 threads.
+// Tile: MT rows x 256 weight rows, K step 64, 256 threads (4 waves).
 // GATED: the 256 weight rows are 128 output columns of W_gate interleaved
 // with the same 128 columns of W_up in blocks of 32, so each wave holds the
 // gate and up accumulators of the same outputs and applies SwiGLU in
 // registers.  Otherwise the 256 weight rows are 256 output columns.
+//
+// Data path: global -> LDS with the gfx950 direct loads (global_load_lds,
+// 16 bytes per lane, one contiguous KiB per wave instruction) into an
+// NS-stage ring; no staging registers.  LDS rows are 128 bytes (64 bf16)
+// and the 16-byte chunk c of row r sits in slot c ^ (r & 7), so the MFMA
+// fragment reads (32 rows, one chunk) hit 8 distinct bank groups.
 // Matrix cores: v_mfma_f32_32x32x16_bf16, fp32 accumulation.
 template <int MT, bool GATED>
 struct Bf16Cfg {
@@ -128,20 +134,171 @@ struct Bf16Cfg {
   static constexpr int WN = NB / WAVES_N;
   static constexpr int BM = WM / 32;
   static constexpr int BN = WN / 32;
-  static constexpr int LDSROW = BK + 8;  // bf16 elements; 144 B rows spread the banks
   static constexpr int NOUT = GATED ? NB / 2 : NB;
-  static constexpr int A_CH = MT * BK / 8 / 256;   // 16-byte chunks per thread
-  static constexpr int B_CH = NB * BK / 8 / 256;
-  static constexpr int NSTAGE = 2;
-  static constexpr int STAGE_ELEMS = (MT + NB) * LDSROW;
-  static constexpr size_t LDS_BYTES = static_cast<size_t>(NSTAGE) * STAGE_ELEMS * 2;
+  static constexpr int NS = MT >= 128 ? 3 : 4;          // LDS ring stages
+  static constexpr int A_LOADS = MT * 128 / 1024 / 4;   // KiB loads per wave per stage
+  static constexpr int B_LOADS = NB * 128 / 1024 / 4;
+  static constexpr int LPW = A_LOADS + B_LOADS;
+  static_assert((NS - 2) * LPW < 64, "vmcnt range");
 };
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One direct global -> LDS load: 16 bytes per lane from `src`, the wave's 64
+// lanes filling the KiB at `dst` (wave-uniform) in lane order.  Written as
+// inline asm so that the compiler does not track these LDS writes (it would
+// otherwise fall back to waiting for every outstanding load before each LDS
+// read); the ring synchronises them explicitly with vmcnt waits and
+// barriers.  The asm has no output registers.
+__device__ __forceinline__ void dma16(const bf16_t* src, bf16_t* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(dst))));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "m0");
+}
+
+template <int MT, bool GATED>
+struct TileCtx {
+  using C = Bf16Cfg<MT, GATED>;
+  const bf16_t* a_src[C::A_LOADS];  // per-lane source of each A load (chunk applied)
+  const bf16_t* b_src0;             // first B load of this lane (chunk applied)
+  const bf16_t* b_src1;             // GATED: first W_up load
+  size_t b_step;                    // elements between consecutive B loads (8 rows)
+
+  // Loads of one stage (K columns k0..k0+63) into the LDS tiles sA, sB.
+  __device__ __forceinline__ void issue(int k0, bf16_t* sA, bf16_t* sB, int wave) const {
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q)
+      dma16(a_src[q] + k0, sA + (wave * C::A_LOADS + q) * 512);
+#pragma unroll
+    for (int q = 0; q < C::B_LOADS; ++q) {
+      const bf16_t* src;
+      if (GATED) src = (q < C::B_LOADS / 2 ? b_src0 + q * b_step
+                                           : b_src1 + (q - C::B_LOADS / 2) * b_step);
+      else src = b_src0 + q * b_step;
+      dma16(src + k0, sB + (wave * C::B_LOADS + q) * 512);
+    }
+  }
+};
+
+template <int MT, bool GATED>
+__device__ __forceinline__ void load_frags(const bf16_t* sA, const bf16_t* sB, int kk, int wm,
+                                           int wn, int lane,
+                                           bf16x8_t (&af)[Bf16Cfg<MT, GATED>::BM],
+                                           bf16x8_t (&bfr)[Bf16Cfg<MT, GATED>::BN]) {
+  using C = Bf16Cfg<MT, GATED>;
+  const int r32 = lane & 31;
+  const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+  for (int i = 0; i < C::BM; ++i) {
+    const int row = wm * C::WM + i * 32 + r32;
+    af[i] = *reinterpret_cast<const bf16x8_t*>(sA + row * 64 + ((c ^ (row & 7)) << 3));
+  }
+#pragma unroll
+  for (int j = 0; j < C::BN; ++j) {
+    const int row = wn * C::WN + j * 32 + r32;
+    bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB + row * 64 + ((c ^ (row & 7)) << 3));
+  }
+}
+
+template <int MT, bool GATED>
+__device__ __forceinline__ void mfma_frags(const bf16x8_t (&af)[Bf16Cfg<MT, GATED>::BM],
+                                           const bf16x8_t (&bfr)[Bf16Cfg<MT, GATED>::BN],
+                                           f32x16_t (&acc)[Bf16Cfg<MT, GATED>::BM]
+                                                          [Bf16Cfg<MT, GATED>::BN]) {
+  using C = Bf16Cfg<MT, GATED>;
+#pragma unroll
+  for (int i = 0; i < C::BM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::BN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+// The 4 MFMA K-substeps of one stage; the fragments of substep kk+1 are
+// read from LDS before the MFMAs of substep kk are issued.
+template <int MT, bool GATED>
+__device__ __forceinline__ void compute_stage(const bf16_t* sA, const bf16_t* sB, int wm,
+                                              int wn, int lane,
+                                              f32x16_t (&acc)[Bf16Cfg<MT, GATED>::BM]
+                                                             [Bf16Cfg<MT, GATED>::BN]) {
+  using C = Bf16Cfg<MT, GATED>;
+  bf16x8_t a0[C::BM], b0[C::BN], a1[C::BM], b1[C::BN];
+  load_frags<MT, GATED>(sA, sB, 0, wm, wn, lane, a0, b0);
+  load_frags<MT, GATED>(sA, sB, 1, wm, wn, lane, a1, b1);
+  mfma_frags<MT, GATED>(a0, b0, acc);
+  load_frags<MT, GATED>(sA, sB, 2, wm, wn, lane, a0, b0);
+  mfma_frags<MT, GATED>(a1, b1, acc);
+  load_frags<MT, GATED>(sA, sB, 3, wm, wn, lane, a1, b1);
+  mfma_frags<MT, GATED>(a0, b0, acc);
+  mfma_frags<MT, GATED>(a1, b1, acc);
+  // Schedule: substep 0's reads, then each substep's MFMAs interleaved one
+  // by one with the next substep's reads, so LDS latency hides behind MFMAs.
+  constexpr int NR = C::BM + C::BN;       // fragment reads per substep
+  constexpr int NM = C::BM * C::BN;       // MFMAs per substep
+  __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);
+#pragma unroll
+  for (int kk = 0; kk < 3; ++kk) {
+#pragma unroll
+    for (int q = 0; q < NM; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NM, 0);
+}
+
+// One k-step of the ring: wait for this stage, barrier, refill the slot read
+// one step ago, compute.  U is the ring slot (compile-time).  The refill is
+// unconditional so that the compiler can tell the LDS buffers apart when it
+// places its own waits: past the last K step it reloads the last step (an
+// L2 hit whose slot is never read).  Exactly NS-2 stages are then always in
+// flight behind the one being consumed.
+template <int MT, bool GATED, int U>
+__device__ __forceinline__ void ring_step(const TileCtx<MT, GATED>& t, int kt, int nk,
+                                          bf16_t* const (&sA)[4], bf16_t* const (&sB)[4], int wave,
+                                          int wm, int wn, int lane,
+                                          f32x16_t (&acc)[Bf16Cfg<MT, GATED>::BM]
+                                                         [Bf16Cfg<MT, GATED>::BN]) {
+  using C = Bf16Cfg<MT, GATED>;
+  constexpr int NXT = (U + C::NS - 1) % C::NS;
+  wait_vm<(C::NS - 2) * C::LPW>();
+  lds_barrier();
+  const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
+  t.issue(kn * C::BK, sA[NXT], sB[NXT], wave);
+  compute_stage<MT, GATED>(sA[U], sB[U], wm, wn, lane, acc);
+}
 
 template <int MT, bool GATED>
 __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   using C = Bf16Cfg<MT, GATED>;
-  extern __shared__ __attribute__((aligned(16))) bf16_t lds[];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA0[MT * 64];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA1[MT * 64];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA2[MT * 64];
+  __shared__ __attribute__((aligned(1024))) bf16_t sA3[C::NS > 3 ? MT * 64 : 1];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB0[C::NB * 64];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB1[C::NB * 64];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB2[C::NB * 64];
+  __shared__ __attribute__((aligned(1024))) bf16_t sB3[C::NS > 3 ? C::NB * 64 : 1];
   __shared__ int ts[512];
+  bf16_t* const sA[4] = {sA0, sA1, sA2, sA3};
+  bf16_t* const sB[4] = {sB0, sB1, sB2, sB3};
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,6 +320,11 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
+  // this lane's 16-byte chunk inside a 128-byte LDS row: slot lane%8 of row
+  // lane/8 holds global chunk (lane%8) ^ (lane/8)
+  const int lrow = lane >> 3;
+  const int lchunk = ((lane & 7) ^ lrow) * 8;
+  const int nk = p.K / C::BK;
 
   for (long long it = beg + slot; it < end; it += per_xcd) {
     const Item item = decode_item(it, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
@@ -170,43 +332,34 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
                                    : kT + static_cast<size_t>(g - p.E) * p.T;
-
-    // ---- A rows of this thread's load chunks
-    const bf16_t* a_src[C::A_CH];
+    TileCtx<MT, GATED> t;
 #pragma unroll
-    for (int i = 0; i < C::A_CH; ++i) {
-      const int c = tid + 256 * i;
-      int r = c >> 3;
+    for (int q = 0; q < C::A_LOADS; ++q) {
+      int r = (wave * C::A_LOADS + q) * 8 + lrow;
       r = r < item.rows ? r : item.rows - 1;
       const int rr = item.m0 + r;
       size_t src_row;
-      if (GATED) {
-        src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
-                         : static_cast<size_t>(rr);
-      } else {
-        src_row = row_base + rr;
-      }
-      a_src[i] = A + src_row * p.K + (c & 7) * 8;
+      if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
+                                  : static_cast<size_t>(rr);
+      else src_row = row_base + rr;
+      t.a_src[q] = A + src_row * p.K + lchunk;
     }
-    // ---- weight rows of this thread's load chunks
-    const bf16_t* b_src[C::B_CH];
     const size_t wstride = static_cast<size_t>(p.N) * p.K;
-#pragma unroll
-    for (int i = 0; i < C::B_CH; ++i) {
-      const int c = tid + 256 * i;
-      const int r = c >> 3;
-      const bf16_t* base;
-      int wrow;
-      if (GATED) {
-        const int blk = r >> 5;
-        wrow = item.n * C::NOUT + (blk >> 1) * 32 + (r & 31);
-        const void* w = (blk & 1) ? (routed ? p.w1 : p.ws1) : (routed ? p.w0 : p.ws0);
-        base = static_cast<const bf16_t*>(w) + (routed ? g : g - p.E) * wstride;
-      } else {
-        wrow = item.n * C::NOUT + r;
-        base = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + (routed ? g : g - p.E) * wstride;
-      }
-      b_src[i] = base + static_cast<size_t>(wrow) * p.K + (c & 7) * 8;
+    const int ge = routed ? g : g - p.E;
+    t.b_step = static_cast<size_t>(8) * p.K;
+    if (GATED) {
+      // wave w loads rows 64w..64w+63: W_gate columns n*128 + 32w + (0..31),
+      // then the same W_up columns
+      const int col = item.n * C::NOUT + wave * 32 + lrow;
+      const bf16_t* wg = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
+      const bf16_t* wu = static_cast<const bf16_t*>(routed ? p.w1 : p.ws1) + ge * wstride;
+      t.b_src0 = wg + static_cast<size_t>(col) * p.K + lchunk;
+      t.b_src1 = wu + static_cast<size_t>(col) * p.K + lchunk;
+    } else {
+      const int col = item.n * C::NOUT + wave * C::B_LOADS * 8 + lrow;
+      const bf16_t* wd = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
+      t.b_src0 = wd + static_cast<size_t>(col) * p.K + lchunk;
+      t.b_src1 = t.b_src0;
     }
 
     f32x16_t acc[C::BM][C::BN];
@@ -217,57 +370,18 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    uint4 areg[C::A_CH], breg[C::B_CH];
-    auto gload = [&](int k0) {
+    // every wave is done with the previous item's LDS before refilling it
+    wait_vm<0>();
+    lds_barrier();
 #pragma unroll
-      for (int i = 0; i < C::A_CH; ++i) areg[i] = *reinterpret_cast<const uint4*>(a_src[i] + k0);
-#pragma unroll
-      for (int i = 0; i < C::B_CH; ++i) breg[i] = *reinterpret_cast<const uint4*>(b_src[i] + k0);
-    };
-    auto lstore = [&](int buf) {
-      bf16_t* sA = lds + buf * C::STAGE_ELEMS;
-      bf16_t* sB = sA + MT * C::LDSROW;
-#pragma unroll
-      for (int i = 0; i < C::A_CH; ++i) {
-        const int c = tid + 256 * i;
-        *reinterpret_cast<uint4*>(sA + (c >> 3) * C::LDSROW + (c & 7) * 8) = areg[i];
-      }
-#pragma unroll
-      for (int i = 0; i < C::B_CH; ++i) {
-        const int c = tid + 256 * i;
-        *reinterpret_cast<uint4*>(sB + (c >> 3) * C::LDSROW + (c & 7) * 8) = breg[i];
-      }
-    };
+    for (int s = 0; s < C::NS - 1; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sA[s], sB[s], wave);
 
-    const int nk = p.K / C::BK;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int buf = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * C::BK);
-      const bf16_t* sA = lds + buf * C::STAGE_ELEMS;
-      const bf16_t* sB = sA + MT * C::LDSROW;
-#pragma unroll
-      for (int kk = 0; kk < C::BK / 16; ++kk) {
-        const int kof = kk * 16 + (lane >> 5) * 8;
-        bf16x8_t af[C::BM], bfr[C::BN];
-#pragma unroll
-        for (int i = 0; i < C::BM; ++i)
-          af[i] = *reinterpret_cast<const bf16x8_t*>(
-              sA + (wm * C::WM + i * 32 + (lane & 31)) * C::LDSROW + kof);
-#pragma unroll
-        for (int j = 0; j < C::BN; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8_t*>(
-              sB + (wn * C::WN + j * 32 + (lane & 31)) * C::LDSROW + kof);
-#pragma unroll
-        for (int i = 0; i < C::BM; ++i)
-#pragma unroll
-          for (int j = 0; j < C::BN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
-      if (kt + 1 < nk) lstore(buf ^ 1);
-      __syncthreads();
+    for (int kt = 0; kt < nk; kt += C::NS) {
+      ring_step<MT, GATED, 0>(t, kt, nk, sA, sB, wave, wm, wn, lane, acc);
+      if (kt + 1 < nk) ring_step<MT, GATED, 1>(t, kt + 1, nk, sA, sB, wave, wm, wn, lane, acc);
+      if (kt + 2 < nk) ring_step<MT, GATED, 2>(t, kt + 2, nk, sA, sB, wave, wm, wn, lane, acc);
+      if constexpr (C::NS > 3)
+        if (kt + 3 < nk) ring_step<MT, GATED, 3>(t, kt + 3, nk, sA, sB, wave, wm, wn, lane, acc);
     }
 
     // ---- epilogue.  32x32 accumulator layout: lane l holds column l%32 and
@@ -404,14 +518,9 @@ static int device_cus() {
 
 template <int MT, bool GATED>
 static hipError_t run_bf16(const FfnArgs& a, hipStream_t st) {
-  using C = Bf16Cfg<MT, GATED>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&ffn_bf16_kernel<MT, GATED>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     static_cast<int>(C::LDS_BYTES));
-  if (e != hipSuccess) return e;
   int grid = device_cus();
   grid = (grid + 7) / 8 * 8;
-  ffn_bf16_kernel<MT, GATED><<<grid, 256, C::LDS_BYTES, st>>>(a);
+  ffn_bf16_kernel<MT, GATED><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }
 
