@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one device-to-device copy of this size (for scaling "
+                         "hardware byte counters)")
     return ap.parse_args()
 
 
@@ -192,6 +195,13 @@ def main():
     from sparse_mixture_experts_04_amd import configs, synth
 
     cfg = configs.get(args.workload)
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     inp, desc, w, ws, counts, ms_wall, ms_ev = time_forward(cfg, args.steps, args.warmup,
                                                             torch, L, synth)
     stages = time_stages(cfg, inp, desc, w, max(3, min(args.steps, 10)), torch, L, synth)

@@ -49,11 +49,11 @@ class Routing(ctypes.Structure):
                  "pair_pos")]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run "
+def _load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run "
                           "`python -m sparse_mixture_experts_04_amd.build`")
-    lib = ctypes.CDLL(LIB_PATH)
+    lib = ctypes.CDLL(path)
     P, I, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     D = ctypes.POINTER(Desc)
     W = ctypes.POINTER(Weights)

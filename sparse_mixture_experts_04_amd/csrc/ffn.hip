@@ -17,13 +17,15 @@
 // tile outer, row tile inner, so the workgroups running together on an XCD
 // share a weight tile (read from HBM once) and the group's activation rows
 // stay in that XCD's L2.
-#include "common.h"
+#include "ffn_common.h"
 
 namespace moe {
 
 // ------------------------------------------------------------- tile plan
 
-// tile_start[g] = first row tile of group g; tile_start[E+S] = total.
+// tile_start[g] = first row tile of group g; tile_start[E+S] = total.  The
+// 2 * kXcds work counters that follow (one set for the gate/up GEMM, one for
+// the down GEMM that reuses this plan) are zeroed.
 __global__ __launch_bounds__(512) void tile_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int S, int T, int MT,
                                                         int32_t* __restrict__ tile_start) {
@@ -44,10 +46,12 @@ __global__ __launch_bounds__(512) void tile_plan_kernel(const int32_t* __restric
   }
   if (g < G) tile_start[g] = sc[g] - nt;
   if (g == G - 1) tile_start[G] = sc[g];
+  if (g < 2 * kXcds) tile_start[G + 1 + g] = 0;
 }
 
 hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile,
                             int32_t* tile_start, hipStream_t st) {
+  if (row_tile == BigCfgRows) return launch_tile_plan_big(s, offsets, tile_start, st);
   tile_plan_kernel<<<1, 512, 0, st>>>(offsets, s.E, s.S, s.T, row_tile, tile_start);
   return hipGetLastError();
 }
@@ -55,60 +59,8 @@ hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile
 int ffn_row_tile(const Shape& s) {
   if (!s.bf16) return 32;
   const long long per_expert = static_cast<long long>(s.T) * s.k / s.E;
-  return per_expert < 48 ? 32 : 128;
+  return per_expert < 48 ? 32 : BigCfgRows;
 }
-
-// ------------------------------------------------------------ item walk
-
-struct Item {
-  int g;      // group
-  int m0;     // first row of the tile inside the group
-  int rows;   // valid rows in the tile
-  int n;      // column tile
-  int grows;  // rows of the group
-};
-
-// Binary search over tile_start (in LDS) and the group's item order
-// (column tile outer, row tile inner).
-__device__ __forceinline__ Item decode_item(long long it, const int* ts, int G, int n_tiles,
-                                            int MT, const int32_t* __restrict__ offsets, int T,
-                                            int E) {
-  int lo = 0, hi = G;  // find last g with ts[g] * n_tiles <= it
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (static_cast<long long>(ts[mid]) * n_tiles <= it) lo = mid;
-    else hi = mid;
-  }
-  // skip empty groups that share the same start
-  while (lo + 1 < G && ts[lo + 1] == ts[lo]) ++lo;
-  Item r;
-  r.g = lo;
-  const int mt = ts[lo + 1] - ts[lo];
-  const long long local = it - static_cast<long long>(ts[lo]) * n_tiles;
-  r.n = static_cast<int>(local / mt);
-  const int m = static_cast<int>(local % mt);
-  r.grows = lo < E ? offsets[lo + 1] - offsets[lo] : T;
-  r.m0 = m * MT;
-  const int left = r.grows - r.m0;
-  r.rows = left < MT ? left : MT;
-  return r;
-}
-
-struct FfnArgs {
-  const void* a;          // gate/up: x [T, K]; down: h [(k+S)T, K]
-  const void* w0;         // routed weights: gate (gate/up) or down  [E, N, K]
-  const void* w1;         // routed up weights (gate/up only)
-  const void* ws0;        // shared weights                          [S, N, K]
-  const void* ws1;
-  const int32_t* offsets;
-  const int32_t* sorted_pair;
-  const int32_t* tile_start;
-  void* out_routed;       // row offsets[g] + r
-  void* out_shared;       // row (g-E)*T + r
-  int T, K, N, E, S, k;   // N = weight rows per expert (F for gate/up, d for down)
-  int ldo;                // row length of the output
-  int n_tiles;            // column tiles
-};
 
 // -------------------------------------------------------- bf16 MFMA GEMM
 
@@ -121,8 +73,11 @@ struct FfnArgs {
 // Data path: global -> LDS with the gfx950 direct loads (global_load_lds,
 // 16 bytes per lane, one contiguous KiB per wave instruction) into an
 // NS-stage ring; no staging registers.  LDS rows are 128 bytes (64 bf16)
-// and the 16-byte chunk c of row r sits in slot c ^ (r & 7), so the MFMA
-// fragment reads (32 rows, one chunk) hit 8 distinct bank groups.
+// and the 16-byte chunk c of row r sits in slot c ^ swz(r), with
+// swz(r) = (r & 7) ^ ((r >> 3) & 1): the MFMA fragment reads (one chunk of
+// 32 consecutive rows) then hit distinct 16-byte bank groups both within
+// every 8 lanes (128-byte window) and within every 16 lanes (256-byte
+// window).
 // Matrix cores: v_mfma_f32_32x32x16_bf16, fp32 accumulation.
 template <int MT, bool GATED>
 struct Bf16Cfg {
@@ -142,45 +97,14 @@ struct Bf16Cfg {
   static_assert((NS - 2) * LPW < 64, "vmcnt range");
 };
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
-
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("" ::: "memory");
-}
-
-// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-// One direct global -> LDS load: 16 bytes per lane from `src`, the wave's 64
-// lanes filling the KiB at `dst` (wave-uniform) in lane order.  Written as
-// inline asm so that the compiler does not track these LDS writes (it would
-// otherwise fall back to waiting for every outstanding load before each LDS
-// read); the ring synchronises them explicitly with vmcnt waits and
-// barriers.  The asm has no output registers.
-__device__ __forceinline__ void dma16(const bf16_t* src, bf16_t* dst) {
-  const uint32_t lds = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(dst))));
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
-               :
-               : "v"(src), "s"(lds)
-               : "m0");
-}
-
 template <int MT, bool GATED>
 struct TileCtx {
   using C = Bf16Cfg<MT, GATED>;
   const bf16_t* a_src[C::A_LOADS];  // per-lane source of each A load (chunk applied)
-  const bf16_t* b_src0;             // first B load of this lane (chunk applied)
+  const bf16_t* b_src0;             // first B load of this lane (row only)
   const bf16_t* b_src1;             // GATED: first W_up load
   size_t b_step;                    // elements between consecutive B loads (8 rows)
+  int bch[2];                       // this lane's chunk offset for even / odd loads
 
   // Loads of one stage (K columns k0..k0+63) into the LDS tiles sA, sB.
   __device__ __forceinline__ void issue(int k0, bf16_t* sA, bf16_t* sB, int wave) const {
@@ -193,7 +117,7 @@ struct TileCtx {
       if (GATED) src = (q < C::B_LOADS / 2 ? b_src0 + q * b_step
                                            : b_src1 + (q - C::B_LOADS / 2) * b_step);
       else src = b_src0 + q * b_step;
-      dma16(src + k0, sB + (wave * C::B_LOADS + q) * 512);
+      dma16(src + bch[q & 1] + k0, sB + (wave * C::B_LOADS + q) * 512);
     }
   }
 };
@@ -209,12 +133,12 @@ __device__ __forceinline__ void load_frags(const bf16_t* sA, const bf16_t* sB, i
 #pragma unroll
   for (int i = 0; i < C::BM; ++i) {
     const int row = wm * C::WM + i * 32 + r32;
-    af[i] = *reinterpret_cast<const bf16x8_t*>(sA + row * 64 + ((c ^ (row & 7)) << 3));
+    af[i] = *reinterpret_cast<const bf16x8_t*>(sA + row * 64 + ((c ^ swz(row)) << 3));
   }
 #pragma unroll
   for (int j = 0; j < C::BN; ++j) {
     const int row = wn * C::WN + j * 32 + r32;
-    bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB + row * 64 + ((c ^ (row & 7)) << 3));
+    bfr[j] = *reinterpret_cast<const bf16x8_t*>(sB + row * 64 + ((c ^ swz(row)) << 3));
   }
 }
 
@@ -320,10 +244,12 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
-  // this lane's 16-byte chunk inside a 128-byte LDS row: slot lane%8 of row
-  // lane/8 holds global chunk (lane%8) ^ (lane/8)
+  // Load j of a stage fills LDS rows 8j..8j+7; its lane l lands in slot l%8
+  // of row 8j + l/8 and so must fetch global chunk (l%8) ^ swz(8j + l/8),
+  // i.e. (l%8) ^ (l/8) ^ (j & 1).
   const int lrow = lane >> 3;
-  const int lchunk = ((lane & 7) ^ lrow) * 8;
+  const int lchunk[2] = {((lane & 7) ^ lrow) * 8, ((lane & 7) ^ lrow ^ 1) * 8};
+  static_assert(C::B_LOADS % 2 == 0, "B load parity follows q");
   const int nk = p.K / C::BK;
 
   for (long long it = beg + slot; it < end; it += per_xcd) {
@@ -342,23 +268,25 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
       if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
                                   : static_cast<size_t>(rr);
       else src_row = row_base + rr;
-      t.a_src[q] = A + src_row * p.K + lchunk;
+      t.a_src[q] = A + src_row * p.K + lchunk[(wave * C::A_LOADS + q) & 1];
     }
     const size_t wstride = static_cast<size_t>(p.N) * p.K;
     const int ge = routed ? g : g - p.E;
     t.b_step = static_cast<size_t>(8) * p.K;
+    t.bch[0] = lchunk[0];
+    t.bch[1] = lchunk[1];
     if (GATED) {
       // wave w loads rows 64w..64w+63: W_gate columns n*128 + 32w + (0..31),
       // then the same W_up columns
       const int col = item.n * C::NOUT + wave * 32 + lrow;
       const bf16_t* wg = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
       const bf16_t* wu = static_cast<const bf16_t*>(routed ? p.w1 : p.ws1) + ge * wstride;
-      t.b_src0 = wg + static_cast<size_t>(col) * p.K + lchunk;
-      t.b_src1 = wu + static_cast<size_t>(col) * p.K + lchunk;
+      t.b_src0 = wg + static_cast<size_t>(col) * p.K;
+      t.b_src1 = wu + static_cast<size_t>(col) * p.K;
     } else {
       const int col = item.n * C::NOUT + wave * C::B_LOADS * 8 + lrow;
       const bf16_t* wd = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
-      t.b_src0 = wd + static_cast<size_t>(col) * p.K + lchunk;
+      t.b_src0 = wd + static_cast<size_t>(col) * p.K;
       t.b_src1 = t.b_src0;
     }
 
@@ -555,8 +483,9 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
   a.k = s.k;
   a.ldo = s.F;
   if (s.bf16) {
-    a.n_tiles = s.F / Bf16Cfg<128, true>::NOUT;
-    return row_tile == 32 ? run_bf16<32, true>(a, st) : run_bf16<128, true>(a, st);
+    a.n_tiles = s.F / 128;
+    if (row_tile == 32) return run_bf16<32, true>(a, st);
+    return launch_big(a, true, tile_start, 0, st);
   }
   a.n_tiles = s.F / 32;
   return run_f32<true>(a, st);
@@ -582,8 +511,9 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const in
   a.k = s.k;
   a.ldo = s.d;
   if (s.bf16) {
-    a.n_tiles = s.d / Bf16Cfg<128, false>::NOUT;
-    return row_tile == 32 ? run_bf16<32, false>(a, st) : run_bf16<128, false>(a, st);
+    a.n_tiles = s.d / 256;
+    if (row_tile == 32) return run_bf16<32, false>(a, st);
+    return launch_big(a, false, tile_start, 1, st);
   }
   a.n_tiles = s.d / 64;
   return run_f32<false>(a, st);

@@ -1,0 +1,364 @@
+// Expert GEMMs for large batches: row tiles of up to 256 rows.
+//
+// Same computation as the 32-row kernel in ffn.hip ("Under The Hood:
+// Inkling", expert configuration: SwiGLU experts; "Inkling, Dissected", 02:
+// routed and shared experts), with a tile shaped for the matrix cores when
+// the routed experts hold hundreds of rows each:
+//
+// * Tile: up to 256 rows x 256 weight rows, K step 32, 512 threads.  Wave
+//   (wm, wn) = (wave / 4, wave % 4) owns weight rows 64wn..64wn+63 (two
+//   32-wide MFMA column blocks) and row blocks 4wm..4wm+3.  The two waves
+//   of a SIMD (same wn) together cover every row block, so a row tile that
+//   is only partly filled skips whole 32-row MFMA blocks on every SIMD
+//   alike: the cost of an expert follows its row count in steps of 32.
+// * GATED: the 64 weight rows of column group wn are the W_gate columns
+//   32wn..32wn+31 of the 128-column output tile followed by the same W_up
+//   columns; SwiGLU is applied to the accumulators in registers.
+// * Data path: direct global -> LDS loads into a 4-stage ring (32 KiB per
+//   stage), 64-byte LDS rows with chunk c of row r in slot c ^ f(r),
+//   f(r) = ((r >> 1) ^ (r >> 3)) & 3, which keeps the fragment reads free of
+//   bank conflicts for 8- and 16-lane groups.
+// * Scheduling: persistent workgroups; the item list is cut into one
+//   contiguous chunk per XCD and the workgroups of an XCD take the next item
+//   of their chunk from a counter, so consecutive items (sharing weight and
+//   activation tiles) run together on one XCD and uneven items balance.
+#include "ffn_common.h"
+
+namespace moe {
+
+struct BigCfg {
+  static constexpr int THREADS = 512;
+  static constexpr int WAVES = THREADS / 64;
+  static constexpr int BK = 32;
+  static constexpr int MT = 256;
+  static constexpr int NB = 256;
+  static constexpr int NS = 4;
+  static constexpr int BM = MT / 32 / 2;              // row blocks per wave
+  static constexpr int BN = 2;                        // column blocks per wave
+  static constexpr int A_LOADS = MT * 64 / 1024 / WAVES;  // KiB loads per wave per stage
+  static constexpr int B_LOADS = NB * 64 / 1024 / WAVES;
+  static constexpr int LPW = A_LOADS + B_LOADS;
+  static constexpr int STAGE_ELEMS = MT * BK;         // bf16 elements of one tile
+  static_assert((NS - 2) * LPW < 64, "vmcnt range");
+};
+
+__device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
+
+template <bool GATED>
+struct BigCtx {
+  using C = BigCfg;
+  const bf16_t* a_src[C::A_LOADS];  // per-lane A source of each load (chunk applied)
+  const bf16_t* b_src[C::B_LOADS];  // per-lane B source of each load (chunk applied)
+
+  __device__ __forceinline__ void issue(int k0, bf16_t* sA, bf16_t* sB, int wave) const {
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q) dma16(a_src[q] + k0, sA + (wave * C::A_LOADS + q) * 512);
+#pragma unroll
+    for (int q = 0; q < C::B_LOADS; ++q) dma16(b_src[q] + k0, sB + (wave * C::B_LOADS + q) * 512);
+  }
+};
+
+// Fragments of one stage for one wave: 2 MFMA substeps x (4 row blocks of
+// A, 2 column blocks of B).  Row block i of group grp is tile row block
+// 2i + grp (groups interleave so a partly filled tile stays balanced).
+struct BigFrags {
+  bf16x8_t a[2][BigCfg::BM];
+  bf16x8_t b[2][BigCfg::BN];
+};
+
+// Fragment reads.  Rows of a 32-row block differ only above bit 4, so the
+// swizzle depends only on the lane's row inside the block: one per-lane
+// offset per substep (`off[kk]`, in elements) plus a compile-time block
+// offset addresses every fragment.
+template <int NBG>
+__device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* sB, int grp,
+                                               int wn, const int (&off)[2], BigFrags& f) {
+  using C = BigCfg;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) {
+#pragma unroll
+    for (int j = 0; j < C::BN; ++j)
+      f.b[kk][j] =
+          *reinterpret_cast<const bf16x8_t*>(sB + (wn * 2 + j) * 1024 + off[kk]);
+#pragma unroll
+    for (int i = 0; i < NBG; ++i)
+      f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + grp) * 1024 + off[kk]);
+  }
+}
+
+template <int NBG>
+__device__ __forceinline__ void big_mfma(const BigFrags& f,
+                                         f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
+  using C = BigCfg;
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int i = 0; i < NBG; ++i)
+#pragma unroll
+      for (int j = 0; j < C::BN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j],
+                                                            0, 0, 0);
+}
+
+// The K loop with the two wave groups in ping-pong.  Barrier points are
+// numbered 0, 1, 2, ...; group 0 runs memory(j) between points 2j and 2j+1
+// and compute(j) between 2j+1 and 2j+2, group 1 the same one point later.
+// So on every SIMD one wave issues MFMAs while its partner reads fragments
+// and issues the next loads.
+//   memory(j): read stage j's fragments into registers, issue this wave's
+//              share of the loads for stage j+3 into the slot of stage j-1
+//              (both groups finished reading it one point earlier), wait
+//              for the fragment reads;
+//   compute(j): the MFMAs of stage j from registers.
+// Before every even point 2j, every wave has waited for its loads of stage
+// j (two later stages stay in flight), so stage j is complete in LDS when
+// group 0 starts reading it.  Past the last K step the loads repeat the
+// last step (L2 hits into slots never read), which keeps the counts
+// uniform.
+template <int NBG, int U, bool GATED>
+__device__ __forceinline__ void big_pp_step(const BigCtx<GATED>& t, int kt, int nk,
+                                            bf16_t* const (&sA)[4], bf16_t* const (&sB)[4],
+                                            int wave, int grp, int wn, const int (&off)[2],
+                                            f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
+  using C = BigCfg;
+  constexpr int NXT = (U + 3) % 4;
+  BigFrags f;
+  big_read_frags<NBG>(sA[U], sB[U], grp, wn, off, f);
+  const int kn = kt + 3 < nk ? kt + 3 : nk - 1;
+  t.issue(kn * C::BK, sA[NXT], sB[NXT], wave);
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
+  if (grp == 1) wait_vm<2 * C::LPW>();
+  lds_barrier();
+  big_mfma<NBG>(f, acc);
+  if (grp == 0) wait_vm<2 * C::LPW>();
+  lds_barrier();
+}
+
+template <int NBG, bool GATED>
+__device__ __forceinline__ void big_kloop(const BigCtx<GATED>& t, int nk,
+                                          bf16_t* const (&sA)[4], bf16_t* const (&sB)[4],
+                                          int wave, int lane,
+                                          f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
+  using C = BigCfg;
+  const int grp = wave >> 2, wn = wave & 3;
+  const int r32 = lane & 31;
+  const int off[2] = {r32 * 32 + (((lane >> 5) ^ swz4(r32)) << 3),
+                      r32 * 32 + (((2 + (lane >> 5)) ^ swz4(r32)) << 3)};
+#pragma unroll
+  for (int s = 0; s < 3; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sA[s], sB[s], wave);
+  wait_vm<2 * C::LPW>();
+  lds_barrier();                  // point 0: stage 0 complete
+  if (grp == 1) lds_barrier();    // point 1 for group 1 (its phase 0 is idle)
+  for (int kt = 0; kt < nk; kt += 4) {
+    big_pp_step<NBG, 0, GATED>(t, kt, nk, sA, sB, wave, grp, wn, off, acc);
+    if (kt + 1 < nk) big_pp_step<NBG, 1, GATED>(t, kt + 1, nk, sA, sB, wave, grp, wn, off, acc);
+    if (kt + 2 < nk) big_pp_step<NBG, 2, GATED>(t, kt + 2, nk, sA, sB, wave, grp, wn, off, acc);
+    if (kt + 3 < nk) big_pp_step<NBG, 3, GATED>(t, kt + 3, nk, sA, sB, wave, grp, wn, off, acc);
+  }
+  if (grp == 0) lds_barrier();    // both groups pass the same number of points
+}
+
+// One launch covers one tile list: the tiles with more than 128 rows
+// (NBG = 4 row blocks per wave group) or the groups' tails of at most 128
+// rows (NBG = 2).  Each instance is straight-line code, which keeps the
+// 128 accumulators and the fragments of a wave in registers.
+template <bool GATED, int NBG>
+__global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_t* list,
+                                                         bool tail_list, int32_t* counters) {
+  using C = BigCfg;
+  // 4 ring slots of A and B tiles; after the K loop the same memory stages
+  // the output tile for coalesced stores
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[8 * C::STAGE_ELEMS];
+  __shared__ int ts[512];
+  __shared__ int s_next;
+  bf16_t* const sA[4] = {lds, lds + 2 * C::STAGE_ELEMS, lds + 4 * C::STAGE_ELEMS,
+                         lds + 6 * C::STAGE_ELEMS};
+  bf16_t* const sB[4] = {lds + C::STAGE_ELEMS, lds + 3 * C::STAGE_ELEMS,
+                         lds + 5 * C::STAGE_ELEMS, lds + 7 * C::STAGE_ELEMS};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int G = p.E + p.S;
+  for (int g = tid; g <= G; g += C::THREADS) ts[g] = list[g];
+  __syncthreads();
+
+  const long long total = static_cast<long long>(ts[G]) * p.n_tiles;
+  const int xcd = blockIdx.x % kXcds;
+  const long long chunk = (total + kXcds - 1) / kXcds;
+  const long long beg = xcd * chunk;
+  const long long len = (beg + chunk < total ? beg + chunk : total) - beg;
+
+  const bf16_t* A = static_cast<const bf16_t*>(p.a);
+  const size_t kT = static_cast<size_t>(p.k) * p.T;
+  const int nk = p.K / C::BK;
+  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  // load j of a stage fills LDS rows 16j..16j+15; lane l lands in slot l%4
+  // of row 16j + l/4 and fetches chunk (l%4) ^ f(16j + l/4), which is
+  // (l%4) ^ (((l >> 3) ^ (l >> 5)) & 3) ^ 2*(j & 1)
+  const int lrow = lane >> 2;
+  const int cbase = (lane & 3) ^ (((lane >> 3) ^ (lane >> 5)) & 3);
+  const int lchunk[2] = {cbase * 8, (cbase ^ 2) * 8};
+
+  for (;;) {
+    if (tid == 0) s_next = atomicAdd(&counters[xcd], 1);
+    __syncthreads();  // also: every wave is done with the previous item's LDS
+    const int local = s_next;
+    if (local >= len) break;
+    const Item item =
+        decode_item(beg + local, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E, tail_list);
+    const int g = item.g;
+    const bool routed = g < p.E;
+    const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
+                                   : kT + static_cast<size_t>(g - p.E) * p.T;
+    BigCtx<GATED> t;
+#pragma unroll
+    for (int q = 0; q < C::A_LOADS; ++q) {
+      const int j = wave * C::A_LOADS + q;
+      int r = j * 16 + lrow;
+      r = r < item.rows ? r : item.rows - 1;
+      const int rr = item.m0 + r;
+      size_t src_row;
+      if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
+                                  : static_cast<size_t>(rr);
+      else src_row = row_base + rr;
+      t.a_src[q] = A + src_row * p.K + lchunk[j & 1];
+    }
+    const int ge = routed ? g : g - p.E;
+#pragma unroll
+    for (int q = 0; q < C::B_LOADS; ++q) {
+      const int j = wave * C::B_LOADS + q;
+      const int R = j * 16 + lrow;  // LDS B row
+      const int grp = R >> 6, rl = R & 63;
+      const bf16_t* base;
+      int col;
+      if (GATED) {
+        const bool up = rl >= 32;
+        base = static_cast<const bf16_t*>(up ? (routed ? p.w1 : p.ws1) : (routed ? p.w0 : p.ws0));
+        col = item.n * (C::NB / 2) + grp * 32 + (rl & 31);
+      } else {
+        base = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0);
+        col = item.n * C::NB + R;
+      }
+      t.b_src[q] = base + ge * wstride + static_cast<size_t>(col) * p.K + lchunk[j & 1];
+    }
+
+    f32x16_t acc[C::BM][C::BN];
+#pragma unroll
+    for (int i = 0; i < C::BM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::BN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    big_kloop<NBG, GATED>(t, nk, sA, sB, wave, lane, acc);
+
+    // ---- epilogue: accumulators (lane l holds column l%32 and rows
+    // 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block) -> bf16 tile in LDS ->
+    // 16-byte coalesced global stores of the valid rows.
+    constexpr int NOUT = GATED ? C::NB / 2 : C::NB;
+    bf16_t* tile = lds;  // [MT][NOUT]; every wave left the ring at the last point
+#pragma unroll
+    for (int i = 0; i < NBG; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (GATED) {
+          const float gt = acc[i][0][r];
+          const float up = acc[i][1][r];
+          tile[row * NOUT + wn * 32 + (lane & 31)] =
+              f32_to_bf16(gt * __frcp_rn(1.0f + __expf(-gt)) * up);
+        } else {
+#pragma unroll
+          for (int j = 0; j < C::BN; ++j)
+            tile[row * NOUT + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
+        }
+      }
+    }
+    __syncthreads();
+    bf16_t* out = static_cast<bf16_t*>(routed ? p.out_routed : p.out_shared);
+    const size_t orow0 = routed ? static_cast<size_t>(p.offsets[g]) + item.m0
+                                : static_cast<size_t>(g - p.E) * p.T + item.m0;
+    constexpr int CPR = NOUT / 8;  // 16-byte chunks per row
+    const int col0 = item.n * NOUT;
+    for (int c = tid; c < item.rows * CPR; c += C::THREADS) {
+      const int row = c / CPR, ch = c % CPR;
+      *reinterpret_cast<uint4*>(out + (orow0 + row) * p.ldo + col0 + ch * 8) =
+          *reinterpret_cast<const uint4*>(tile + row * NOUT + ch * 8);
+    }
+  }
+}
+
+static int device_cus_big() {
+  int dev = 0, cus = 256;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 256;
+  return cus > 0 ? cus : 256;
+}
+
+// Tile lists for the large-batch GEMMs.  Group g (routed expert g, then the
+// shared experts) with L rows has L / 256 full tiles and a tail of L % 256
+// rows; a tail of more than 128 rows joins the full list (a 256-row tile),
+// a shorter one forms the tail list (a 128-row tile).  Writes both prefix
+// arrays and zeroes the work counters.
+__global__ __launch_bounds__(512) void tile_plan_big_kernel(const int32_t* __restrict__ offsets,
+                                                            int E, int S, int T,
+                                                            int32_t* __restrict__ plan) {
+  __shared__ int sf[512], st[512];
+  const int g = threadIdx.x;
+  const int G = E + S;
+  int rows = 0;
+  if (g < E) rows = offsets[g + 1] - offsets[g];
+  else if (g < G) rows = T;
+  const int rem = rows % BigCfg::MT;
+  const int nf = rows / BigCfg::MT + (rem > 128 ? 1 : 0);
+  const int nt = (rem > 0 && rem <= 128) ? 1 : 0;
+  sf[g] = nf;
+  st[g] = nt;
+  __syncthreads();
+  for (int off = 1; off < 512; off <<= 1) {
+    const int vf = g >= off ? sf[g - off] : 0;
+    const int vt = g >= off ? st[g - off] : 0;
+    __syncthreads();
+    sf[g] += vf;
+    st[g] += vt;
+    __syncthreads();
+  }
+  if (g < G) {
+    plan[g] = sf[g] - nf;
+    plan[G + 1 + g] = st[g] - nt;
+  }
+  if (g == G - 1) {
+    plan[G] = sf[g];
+    plan[2 * G + 1] = st[g];
+  }
+  if (g < 4 * kXcds) plan[2 * (G + 1) + g] = 0;
+}
+
+hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,
+                                hipStream_t st) {
+  tile_plan_big_kernel<<<1, 512, 0, st>>>(offsets, s.E, s.S, s.T, plan);
+  return hipGetLastError();
+}
+
+// `which`: 0 = gate/up, 1 = down (each has its own work counters).
+hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
+                      hipStream_t st) {
+  const int G = a.E + a.S;
+  int32_t* ctr = const_cast<int32_t*>(plan) + 2 * (G + 1) + which * 2 * kXcds;
+  const int32_t* full = plan;
+  const int32_t* tail = plan + G + 1;
+  const int grid = (device_cus_big() + kXcds - 1) / kXcds * kXcds;
+  if (gated) {
+    ffn_big_kernel<true, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
+    ffn_big_kernel<true, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
+  } else {
+    ffn_big_kernel<false, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
+    ffn_big_kernel<false, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

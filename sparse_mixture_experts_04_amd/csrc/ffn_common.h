@@ -1,0 +1,133 @@
+// Internal declarations shared by the expert GEMM kernels.
+#pragma once
+
+#include "common.h"
+
+namespace moe {
+
+// ------------------------------------------------------------ item walk
+
+// Number of XCDs, and of the per-XCD work counters stored after
+// tile_start[E+S].
+constexpr int kXcds = 8;
+
+struct Item {
+  int g;      // group
+  int m0;     // first row of the tile inside the group
+  int rows;   // valid rows in the tile
+  int n;      // column tile
+  int grows;  // rows of the group
+};
+
+// Binary search over tile_start (in LDS), then the item's place in its
+// group.  A group's row tiles are taken in bands of up to kBand tiles; a
+// band's items run column tile outer, row tile inner.  Routed experts at
+// large batch have a few row tiles (one band: each weight tile is read from
+// HBM once while all of the expert's rows use it); the shared experts'
+// many row tiles go band by band, so the workgroups running together on an
+// XCD share both activation and weight tiles.
+constexpr int kBand = 8;
+
+// tail_list: the list holds only each group's last, partial tile (rows
+// past the last multiple of MT); otherwise row tile m starts at m * MT.
+__device__ __forceinline__ Item decode_item(long long it, const int* ts, int G, int n_tiles,
+                                            int MT, const int32_t* __restrict__ offsets, int T,
+                                            int E, bool tail_list = false) {
+  int lo = 0, hi = G;  // find last g with ts[g] * n_tiles <= it
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (static_cast<long long>(ts[mid]) * n_tiles <= it) lo = mid;
+    else hi = mid;
+  }
+  Item r;
+  r.g = lo;
+  const int mt = ts[lo + 1] - ts[lo];
+  const int local = static_cast<int>(it - static_cast<long long>(ts[lo]) * n_tiles);
+  const int band = mt < kBand ? mt : kBand;
+  const int full = mt / band;
+  const int in_full = full * band * n_tiles;
+  int m;
+  if (local < in_full) {
+    const int b = local / (band * n_tiles);
+    const int rem = local - b * band * n_tiles;
+    r.n = rem / band;
+    m = b * band + rem % band;
+  } else {
+    const int last = mt - full * band;
+    const int rem = local - in_full;
+    r.n = rem / last;
+    m = full * band + rem % last;
+  }
+  r.grows = lo < E ? offsets[lo + 1] - offsets[lo] : T;
+  r.m0 = tail_list ? r.grows / MT * MT : m * MT;
+  const int left = r.grows - r.m0;
+  r.rows = left < MT ? left : MT;
+  return r;
+}
+
+struct FfnArgs {
+  const void* a;          // gate/up: x [T, K]; down: h [(k+S)T, K]
+  const void* w0;         // routed weights: gate (gate/up) or down  [E, N, K]
+  const void* w1;         // routed up weights (gate/up only)
+  const void* ws0;        // shared weights                          [S, N, K]
+  const void* ws1;
+  const int32_t* offsets;
+  const int32_t* sorted_pair;
+  const int32_t* tile_start;
+  void* out_routed;       // row offsets[g] + r
+  void* out_shared;       // row (g-E)*T + r
+  int T, K, N, E, S, k;   // N = weight rows per expert (F for gate/up, d for down)
+  int ldo;                // row length of the output
+  int n_tiles;            // column tiles
+};
+
+
+// ---------------------------------------------------------- LDS helpers
+
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt vmcnt(n), leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// One direct global -> LDS load: 16 bytes per lane from `src`, the wave's 64
+// lanes filling the KiB at `dst` (wave-uniform) in lane order.  Written as
+// inline asm so that the compiler does not track these LDS writes (it would
+// otherwise fall back to waiting for every outstanding load before each LDS
+// read); the ring synchronises them explicitly with vmcnt waits and
+// barriers.  The asm has no output registers.
+__device__ __forceinline__ void dma16(const bf16_t* src, bf16_t* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(dst))));
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(lds)
+               : "m0");
+}
+
+
+// Row tile of the large-batch GEMMs and their tile plan.
+constexpr int BigCfgRows = 256;
+hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,
+                                hipStream_t st);
+// Large-batch GEMMs: `plan` is the layout written by tile_plan_big_kernel.
+hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
+                      hipStream_t st);
+// Per-group tile lists of the large-batch GEMM: [full (G+1) | tail (G+1) |
+// counters 2 GEMMs x 2 lists x kXcds].
+inline int big_plan_ints(int G) { return 2 * (G + 1) + 4 * kXcds; }
+
+}  // namespace moe

@@ -4,13 +4,14 @@
 #include <cmath>
 
 #include "../../include/moe.h"
-#include "common.h"
+#include "ffn_common.h"
 
 using namespace moe;
 
 namespace {
 
 constexpr size_t kAlign = 256;
+constexpr int kPlanCounters = 2 * kXcds;  // GEMM work counters after the tile plan
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -64,7 +65,11 @@ RouterWs carve_router(Carver& c, const Shape& s) {
 int32_t* carve_dispatch(Carver& c, const Shape& s) {
   return c.take<int32_t>(static_cast<size_t>(dispatch_segments(s)) * s.E + 1);
 }
-int32_t* carve_plan(Carver& c, const Shape& s) { return c.take<int32_t>(s.E + s.S + 1); }
+int32_t* carve_plan(Carver& c, const Shape& s) {
+  const int small = s.E + s.S + 1 + kPlanCounters;
+  const int big = big_plan_ints(s.E + s.S);
+  return c.take<int32_t>(small > big ? small : big);
+}
 void* carve_h(Carver& c, const Shape& s) {
   return c.take<char>(static_cast<size_t>(s.k + s.S) * s.T * s.F * esize(s));
 }

@@ -166,3 +166,45 @@ def test_skewed_bias_trajectory_lockstep():
         log(f"  step {step}: {st}, max/mean load {c.max() / c.mean():.2f}")
     del inp
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1200, 3000])
+def test_expert_ffn_tile_boundaries(T):
+    # Hand-picked per-expert row counts around every tile size the GEMMs use
+    # (32-row tiles, 256-row tiles with 128-row tails): 0, 1, 31..33, 63..65,
+    # 127..129, 255..257, 383, 384, 511..513, the rest spread over the other
+    # experts.  sorted_pair is a seeded permutation of the pair ids, so rows
+    # gather arbitrary tokens.
+    cfg = MoEConfig(f"tiles{T}", T=T, d=512, F=256, act="bf16")
+    inp = to_dev(synth.make_inputs(cfg, device="cpu"))
+    E, k = cfg.E, cfg.k
+    special = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384,
+               511, 512, 513]
+    counts = np.zeros(E, dtype=np.int64)
+    counts[:len(special)] = special
+    left = k * T - counts.sum()
+    assert left >= 0
+    rest = np.arange(len(special), E)
+    counts[rest] = left // len(rest)
+    counts[rest[: left % len(rest)]] += 1
+    assert counts.sum() == k * T
+    rng = np.random.default_rng(T)
+    sorted_pair = rng.permutation(k * T)
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    desc = desc_for(cfg)
+    d_off = torch.tensor(offsets, dtype=torch.int32, device=DEV)
+    d_sp = torch.tensor(sorted_pair, dtype=torch.int32, device=DEV)
+    b = Buffers(desc, DEV)
+    from sparse_mixture_experts_04_amd import _lib as L
+    L.expert_ffn(desc, inp["x"], L.weights_from(inp), d_off, d_sp, b.y_routed, b.y_shared)
+    torch.cuda.synchronize()
+    yr_ref, ys_ref = O.expert_ffn(np64(inp["x"]), host_weights(inp), offsets, sorted_pair, k)
+    yr = np64(b.y_routed)
+    for e in range(len(special)):
+        lo, hi = offsets[e], offsets[e + 1]
+        if hi > lo:
+            err = rel_l2(yr[lo:hi], yr_ref[lo:hi])
+            assert err <= 2e-2, (e, counts[e], err)
+    e_all, e_sh = rel_l2(yr, yr_ref), rel_l2(np64(b.y_shared), ys_ref)
+    log(f"  T={T}: y_routed {e_all:.2e} y_shared {e_sh:.2e}")
+    assert e_all <= 2e-2 and e_sh <= 2e-2
