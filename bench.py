@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--decode-workload", default="C")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=16)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (for scaling "
                          "hardware byte counters)")
@@ -86,9 +86,11 @@ def time_forward(cfg, steps, warmup, torch, L, synth):
 
 
 def time_stages(cfg, inp, desc, w, steps, torch, L, synth):
-    """The same path through the per-stage entry points, with HIP events
-    around each stage on torch's current stream (the stream every call
-    launches on).  Returns average ms per stage."""
+    """The same path through the per-stage entry points, with HIP events on
+    torch's current stream (the stream every call launches on).  The expert
+    GEMM stages use the marked entry points, which also record events
+    between their kernel launches.  Returns average ms per stage and per
+    GEMM kernel, and the routing counts of the last step."""
     dev = "cuda"
     T, k, S, E = cfg.T, cfg.k, cfg.S, cfg.E
     act = synth.act_dtype(cfg)
@@ -108,30 +110,67 @@ def time_stages(cfg, inp, desc, w, steps, torch, L, synth):
     wsd = L.alloc_workspace(desc, L.CALL_DISPATCH, dev)
     wsg = L.alloc_workspace(desc, L.CALL_GATE_UP, dev)
     wsn = L.alloc_workspace(desc, L.CALL_DOWN, dev)
-    names = ["router", "dispatch", "gate_up", "down", "combine", "bias_update"]
-    calls = [
-        lambda: L.router(desc, inp["x"], inp["w_router"], bias, topk, gates, ws=wsr),
-        lambda: L.dispatch(desc, topk, counts, offsets, sp, pp, ws=wsd),
-        lambda: L.expert_gate_up(desc, inp["x"], w, offsets, sp, h, ws=wsg),
-        lambda: L.expert_down(desc, w, offsets, h, yr, ys, ws=wsn),
-        lambda: L.combine(desc, yr, ys, gates, pp, y),
-        lambda: L.bias_update(desc, counts, cfg.gamma, bias),
-    ]
-    for c in calls:
-        c()
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+    rec = []
+    for _ in range(steps + 1):
+        r = {n: ev() for n in ("t0", "router", "dispatch", "gu_plan", "gu_full", "gu_tail",
+                               "dn_plan", "dn_full", "dn_tail", "combine", "bias")}
+        for e in r.values():
+            e.record()          # raw handles exist once an event was recorded
+        rec.append(r)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
-           for _ in range(steps)]
-    for s in range(steps):
-        evs[s][0].record()
-        for i, c in enumerate(calls):
-            c()
-            evs[s][i + 1].record()
+    for r in rec:
+        r["t0"].record()
+        L.router(desc, inp["x"], inp["w_router"], bias, topk, gates, ws=wsr)
+        r["router"].record()
+        L.dispatch(desc, topk, counts, offsets, sp, pp, ws=wsd)
+        r["dispatch"].record()
+        L.expert_gate_up_marked(desc, inp["x"], w, offsets, sp, h,
+                                [r["gu_plan"], r["gu_full"], r["gu_tail"]], ws=wsg)
+        L.expert_down_marked(desc, w, offsets, h, yr, ys,
+                             [r["dn_plan"], r["dn_full"], r["dn_tail"]], ws=wsn)
+        L.combine(desc, yr, ys, gates, pp, y)
+        r["combine"].record()
+        L.bias_update(desc, counts, cfg.gamma, bias)
+        r["bias"].record()
     torch.cuda.synchronize()
-    out = {}
-    for i, n in enumerate(names):
-        out[n] = sum(evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(steps)) / steps
-    return out
+    rec = rec[1:]            # the first pass warms up
+    span = lambda a, b: sum(r[a].elapsed_time(r[b]) for r in rec) / len(rec)
+    stages = {"router": span("t0", "router"), "dispatch": span("router", "dispatch"),
+              "gate_up": span("dispatch", "gu_tail"), "down": span("gu_tail", "dn_tail"),
+              "combine": span("dn_tail", "combine"), "bias_update": span("combine", "bias")}
+    kernels = {"gate_up_full": span("gu_plan", "gu_full"),
+               "gate_up_tail": span("gu_full", "gu_tail"),
+               "down_full": span("dn_plan", "dn_full"), "down_tail": span("dn_full", "dn_tail")}
+    return stages, kernels, counts.cpu()
+
+
+def full_tile_rows(cfg, counts):
+    """Rows the full-tile GEMM launch covers: every group's rows except a
+    tail of at most 128 rows past its last multiple of 256."""
+    rows = [int(c) for c in counts] + [cfg.T] * cfg.S
+    tot = 0
+    for r in rows:
+        rem = r % 256
+        tot += r - (rem if 0 < rem <= 128 else 0)
+    return tot
+
+
+def traffic_for(kernel_file, profile):
+    """HBM bytes per launch from the committed counter summary, or None when
+    the kernel source changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    src = os.path.join(ROOT, "sparse_mixture_experts_04_amd", "csrc", kernel_file)
+    with open(src, "rb") as f:
+        digest = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("source_sha256") != digest:
+        return None
+    return rec.get("bytes_per_launch")
 
 
 def decode_bytes(cfg, counts):
@@ -204,11 +243,15 @@ def main():
         del src, dst
     inp, desc, w, ws, counts, ms_wall, ms_ev = time_forward(cfg, args.steps, args.warmup,
                                                             torch, L, synth)
-    stages = time_stages(cfg, inp, desc, w, max(3, min(args.steps, 10)), torch, L, synth)
+    stages, kernels, st_counts = time_stages(cfg, inp, desc, w, max(3, min(args.steps, 10)),
+                                             torch, L, synth)
     f_gu, f_dn = expert_flops(cfg)
     ms = ms_wall
     tokens_s = cfg.T / (ms / 1e3)
-    gu_tflops = f_gu / (stages["gate_up"] / 1e3) / 1e12
+    # dominant kernel: the gate/up GEMM over the full row tiles
+    full_rows = full_tile_rows(cfg, st_counts)
+    f_gu_full = 4.0 * cfg.d * cfg.F * full_rows
+    gu_tflops = f_gu_full / (kernels["gate_up_full"] / 1e3) / 1e12
     result = {
         "metric": METRIC, "value": round(tokens_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
@@ -221,10 +264,15 @@ def main():
         "layer_mfma_frac": round((f_gu + f_dn) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_events": round(ms_ev, 4),
         "stage_ms": {k: round(v, 4) for k, v in stages.items()},
-        "roofline": {"kernel": "ffn_bf16_kernel (grouped gate/up GEMM + SwiGLU)",
+        "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
+        "roofline": {"kernel": "ffn_big_kernel<gate/up, 256-row tiles> (grouped gate/up "
+                               "GEMM + SwiGLU over the full row tiles)",
                      "bound": "mfma", "achieved": round(gu_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None},
+                     "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),
+                     "flop_per_launch": f_gu_full, "rows": full_rows,
+                     "ms_per_launch": round(kernels["gate_up_full"], 4),
+                     "traffic": traffic_for("ffn_big.hip", "ffn_big_gate_up_D_traffic.json")},
     }
     max_load = counts.max().item()
     result["max_over_mean_load"] = round(max_load / (cfg.T * cfg.k / cfg.E), 3)
@@ -233,7 +281,7 @@ def main():
         dc = configs.get(args.decode_workload)
         dinp = time_forward(dc, max(args.steps, 20), args.warmup, torch, L, synth)
         d_inp, d_desc, d_w, d_ws, d_counts, d_ms, d_ms_ev = dinp
-        d_stages = time_stages(dc, d_inp, d_desc, d_w, 10, torch, L, synth)
+        d_stages, _, _ = time_stages(dc, d_inp, d_desc, d_w, 10, torch, L, synth)
         nbytes, n_active = decode_bytes(dc, d_counts.cpu())
         gbs = nbytes / (d_ms / 1e3) / 1e9
         result["decode"] = {

@@ -139,10 +139,13 @@ moe_status moe_workspace_size(const moe_desc* desc, moe_call call, size_t* bytes
 
 /* Router ("Inkling, Dissected" 02b; "Under The Hood", routing strategy).
  *   x [T, d] act, w_router [E+S, d] fp32, bias [E] fp32.
- *   z = x . w_router^T accumulated in fp32 (exact bf16 splits of w_router on
- *   the matrix cores, chunked accumulation); s = sigmoid(z) and the
- *   selection keys s + b, the top-k and the gates are taken in fp64 from z.
- *   Writes topk_idx [T, k], gates [T, k+S] and, when non-NULL, margin [T]. */
+ *   z = x . w_router^T: w_router is split exactly into three bf16 planes,
+ *   the products run on the bf16 matrix cores (exact in fp32), each
+ *   32-element K step starts a fresh fp32 accumulator that is then added to
+ *   an fp64 running sum.  s = sigmoid(z), the selection keys s + b, the
+ *   top-k (rank order, exact ties to the lower id) and the gates are taken
+ *   in fp64.  Writes topk_idx [T, k], gates [T, k+S] and, when non-NULL,
+ *   margin [T] (key of the k-th minus the (k+1)-th choice). */
 moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router,
                       const float* bias, int32_t* topk_idx, float* gates,
                       float* margin_or_null, void* ws, size_t ws_bytes,
@@ -174,6 +177,24 @@ moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w,
                            const int32_t* offsets, const void* h,
                            void* y_routed, void* y_shared, void* ws,
                            size_t ws_bytes, hipStream_t stream);
+
+/* Profiling variants of the two calls above, for timing their kernels
+ * with events on the caller's stream.  Same arguments, results and
+ * workspace; in addition marks[0] is recorded after the tile-plan kernel,
+ * marks[1] after the GEMM over the full row tiles and marks[2] after the
+ * GEMM over the groups' short tails (for batches on the 32-row path, which
+ * has a single GEMM launch, marks[1] and marks[2] are recorded together
+ * after it).  marks[0..2] must be valid events (MOE_ERR_NULL otherwise). */
+moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x,
+                                     const moe_weights* w, const int32_t* offsets,
+                                     const int32_t* sorted_pair, void* h, void* ws,
+                                     size_t ws_bytes, hipEvent_t* marks,
+                                     hipStream_t stream);
+moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
+                                  const int32_t* offsets, const void* h,
+                                  void* y_routed, void* y_shared, void* ws,
+                                  size_t ws_bytes, hipEvent_t* marks,
+                                  hipStream_t stream);
 
 /* Both halves: moe_expert_gate_up then moe_expert_down, h in the
  * workspace. */

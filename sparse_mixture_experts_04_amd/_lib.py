@@ -23,7 +23,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE"
 
 SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router",
            "moe_dispatch", "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn",
-           "moe_combine", "moe_bias_update", "moe_forward")
+           "moe_combine", "moe_bias_update", "moe_forward", "moe_expert_gate_up_marked",
+           "moe_expert_down_marked")
 
 
 class MoEError(RuntimeError):
@@ -65,6 +66,8 @@ def _load(path=LIB_PATH):
         "moe_dispatch": (I, [D, P, P, P, P, P, P, Z, P]),
         "moe_expert_gate_up": (I, [D, P, W, P, P, P, P, Z, P]),
         "moe_expert_down": (I, [D, W, P, P, P, P, P, Z, P]),
+        "moe_expert_gate_up_marked": (I, [D, P, W, P, P, P, P, Z, P, P]),
+        "moe_expert_down_marked": (I, [D, W, P, P, P, P, P, Z, P, P]),
         "moe_expert_ffn": (I, [D, P, W, P, P, P, P, P, Z, P]),
         "moe_combine": (I, [D, P, P, P, P, P, P]),
         "moe_bias_update": (I, [D, P, ctypes.c_float, P, P]),
@@ -202,6 +205,40 @@ def expert_down(desc, weights, offsets, h, y_routed, y_shared, ws=None):
                              _ptr(ws, torch.uint8, None, "ws"), ws.numel(),
                              _stream(offsets.device))
     _check("moe_expert_down", st)
+
+
+def _marks(events):
+    if len(events) != 3:
+        raise ValueError("three events are needed")
+    arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+    return arr
+
+
+def expert_gate_up_marked(desc, x, weights, offsets, sorted_pair, h, events, ws=None):
+    """moe_expert_gate_up recording events[0..2] (torch.cuda.Event, created
+    with enable_timing=True and recorded once beforehand) after the tile
+    plan, the full-tile GEMM and the tail GEMM."""
+    ws = alloc_workspace(desc, CALL_GATE_UP, offsets.device) if ws is None else ws
+    st = lib.moe_expert_gate_up_marked(
+        ctypes.byref(desc), _ptr(x, _act(desc), (desc.T, desc.d), "x"), ctypes.byref(weights),
+        _ptr(offsets, torch.int32, None, "offsets"),
+        _ptr(sorted_pair, torch.int32, None, "sorted_pair"),
+        _ptr(h, _act(desc), ((desc.k + desc.S) * desc.T, desc.F), "h"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _marks(events), _stream(offsets.device))
+    _check("moe_expert_gate_up_marked", st)
+
+
+def expert_down_marked(desc, weights, offsets, h, y_routed, y_shared, events, ws=None):
+    """moe_expert_down with the same three marks as expert_gate_up_marked."""
+    ws = alloc_workspace(desc, CALL_DOWN, offsets.device) if ws is None else ws
+    T, d, k, S = desc.T, desc.d, desc.k, desc.S
+    st = lib.moe_expert_down_marked(
+        ctypes.byref(desc), ctypes.byref(weights), _ptr(offsets, torch.int32, None, "offsets"),
+        _ptr(h, _act(desc), ((k + S) * T, desc.F), "h"),
+        _ptr(y_routed, _act(desc), (T * k, d), "y_routed"),
+        _ptr(y_shared, _act(desc), (S, T, d), "y_shared"),
+        _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _marks(events), _stream(offsets.device))
+    _check("moe_expert_down_marked", st)
 
 
 def expert_ffn(desc, x, weights, offsets, sorted_pair, y_routed, y_shared, ws=None):

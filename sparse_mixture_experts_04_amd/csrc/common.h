@@ -73,14 +73,17 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* cou
 hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile,
                             int32_t* tile_start, hipStream_t st);
 
+// marks (optional, may be null): see launch_big; the 32-row path records
+// marks[0] and marks[1] together after its single launch.
 hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
                           const void* wsg, const void* wsu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start,
-                          int row_tile, void* h, hipStream_t st);
+                          int row_tile, void* h, hipEvent_t* marks, hipStream_t st);
 
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
-                       const void* h, void* y_routed, void* y_shared, hipStream_t st);
+                       const void* h, void* y_routed, void* y_shared, hipEvent_t* marks,
+                       hipStream_t st);
 
 hipError_t launch_combine(const Shape& s, const void* y_routed, const void* y_shared,
                           const float* gates, const int32_t* pair_pos, void* y,

@@ -452,6 +452,13 @@ static hipError_t run_bf16(const FfnArgs& a, hipStream_t st) {
   return hipGetLastError();
 }
 
+static hipError_t record_marks(hipEvent_t* marks, hipStream_t st) {
+  if (!marks) return hipSuccess;
+  if (hipEventRecord(marks[0], st) != hipSuccess) return hipErrorInvalidValue;
+  if (hipEventRecord(marks[1], st) != hipSuccess) return hipErrorInvalidValue;
+  return hipSuccess;
+}
+
 template <bool GATED>
 static hipError_t run_f32(const FfnArgs& a, hipStream_t st) {
   ffn_f32_kernel<GATED><<<device_cus() * 4, 256, 0, st>>>(a);
@@ -461,7 +468,7 @@ static hipError_t run_f32(const FfnArgs& a, hipStream_t st) {
 hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
                           const void* wsg, const void* wsu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start, int row_tile,
-                          void* h, hipStream_t st) {
+                          void* h, hipEvent_t* marks, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   FfnArgs a{};
   a.a = x;
@@ -484,16 +491,18 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
   a.ldo = s.F;
   if (s.bf16) {
     a.n_tiles = s.F / 128;
-    if (row_tile == 32) return run_bf16<32, true>(a, st);
-    return launch_big(a, true, tile_start, 0, st);
+    if (row_tile != 32) return launch_big(a, true, tile_start, 0, marks, st);
+    hipError_t e = run_bf16<32, true>(a, st);
+    return e == hipSuccess ? record_marks(marks, st) : e;
   }
   a.n_tiles = s.F / 32;
-  return run_f32<true>(a, st);
+  hipError_t e = run_f32<true>(a, st);
+  return e == hipSuccess ? record_marks(marks, st) : e;
 }
 
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const int32_t* offsets,
                        const int32_t* tile_start, int row_tile, const void* h, void* y_routed,
-                       void* y_shared, hipStream_t st) {
+                       void* y_shared, hipEvent_t* marks, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   FfnArgs a{};
   a.a = h;
@@ -512,11 +521,13 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const in
   a.ldo = s.d;
   if (s.bf16) {
     a.n_tiles = s.d / 256;
-    if (row_tile == 32) return run_bf16<32, false>(a, st);
-    return launch_big(a, false, tile_start, 1, st);
+    if (row_tile != 32) return launch_big(a, false, tile_start, 1, marks, st);
+    hipError_t e = run_bf16<32, false>(a, st);
+    return e == hipSuccess ? record_marks(marks, st) : e;
   }
   a.n_tiles = s.d / 64;
-  return run_f32<false>(a, st);
+  hipError_t e = run_f32<false>(a, st);
+  return e == hipSuccess ? record_marks(marks, st) : e;
 }
 
 }  // namespace moe

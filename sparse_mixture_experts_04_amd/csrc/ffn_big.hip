@@ -344,20 +344,21 @@ hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t*
 }
 
 // `which`: 0 = gate/up, 1 = down (each has its own work counters).
+// marks (optional): events recorded after the full-tile launch (marks[0])
+// and after the tail launch (marks[1]).
 hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
-                      hipStream_t st) {
+                      hipEvent_t* marks, hipStream_t st) {
   const int G = a.E + a.S;
   int32_t* ctr = const_cast<int32_t*>(plan) + 2 * (G + 1) + which * 2 * kXcds;
   const int32_t* full = plan;
   const int32_t* tail = plan + G + 1;
   const int grid = (device_cus_big() + kXcds - 1) / kXcds * kXcds;
-  if (gated) {
-    ffn_big_kernel<true, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
-    ffn_big_kernel<true, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
-  } else {
-    ffn_big_kernel<false, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
-    ffn_big_kernel<false, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
-  }
+  if (gated) ffn_big_kernel<true, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
+  else ffn_big_kernel<false, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
+  if (marks && hipEventRecord(marks[0], st) != hipSuccess) return hipErrorInvalidValue;
+  if (gated) ffn_big_kernel<true, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
+  else ffn_big_kernel<false, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
+  if (marks && hipEventRecord(marks[1], st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -125,7 +125,7 @@ hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t*
                                 hipStream_t st);
 // Large-batch GEMMs: `plan` is the layout written by tile_plan_big_kernel.
 hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
-                      hipStream_t st);
+                      hipEvent_t* marks, hipStream_t st);
 // Per-group tile lists of the large-batch GEMM: [full (G+1) | tail (G+1) |
 // counters 2 GEMMs x 2 lists x kXcds].
 inline int big_plan_ints(int G) { return 2 * (G + 1) + 4 * kXcds; }

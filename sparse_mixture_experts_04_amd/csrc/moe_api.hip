@@ -205,7 +205,7 @@ moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_wei
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
-                       plan, mt, h, stream);
+                       plan, mt, h, nullptr, stream);
   return hip_status(e);
 }
 
@@ -223,7 +223,52 @@ moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w, const int
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, stream);
+    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
+                    stream);
+  return hip_status(e);
+}
+
+moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x, const moe_weights* w,
+                                     const int32_t* offsets, const int32_t* sorted_pair, void* h,
+                                     void* ws, size_t ws_bytes, hipEvent_t* marks,
+                                     hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1] || !marks[2])
+    return MOE_ERR_NULL;
+  if (s.T > 0 && (!x || !sorted_pair || !h)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  int32_t* plan = carve_plan(c, s);
+  const int mt = ffn_row_tile(s);
+  hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
+  if (e == hipSuccess) e = hipEventRecord(marks[0], stream);
+  if (e == hipSuccess)
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
+                       plan, mt, h, marks + 1, stream);
+  return hip_status(e);
+}
+
+moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
+                                  const int32_t* offsets, const void* h, void* y_routed,
+                                  void* y_shared, void* ws, size_t ws_bytes, hipEvent_t* marks,
+                                  hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1] || !marks[2])
+    return MOE_ERR_NULL;
+  if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
+  if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
+  Carver c{static_cast<char*>(ws)};
+  int32_t* plan = carve_plan(c, s);
+  const int mt = ffn_row_tile(s);
+  hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
+  if (e == hipSuccess) e = hipEventRecord(marks[0], stream);
+  if (e == hipSuccess)
+    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared,
+                    marks + 1, stream);
   return hip_status(e);
 }
 
@@ -243,9 +288,10 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const moe_weights
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
-                       plan, mt, h, stream);
+                       plan, mt, h, nullptr, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, stream);
+    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
+                    stream);
   return hip_status(e);
 }
 
@@ -298,10 +344,10 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, f.offsets,
-                       f.sorted_pair, f.plan, mt, f.h, stream);
+                       f.sorted_pair, f.plan, mt, f.h, nullptr, stream);
   if (e == hipSuccess)
     e = launch_down(s, w->w_down, w->ws_down, f.offsets, f.plan, mt, f.h, f.y_routed,
-                    f.y_shared, stream);
+                    f.y_shared, nullptr, stream);
   if (e == hipSuccess)
     e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
   if (e == hipSuccess && gamma != 0.0f) e = launch_bias_update(s, f.counts, gamma, bias, stream);
