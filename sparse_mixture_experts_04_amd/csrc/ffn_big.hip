@@ -253,12 +253,17 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     big_kloop<NBG, GATED>(t, nk, sA, sB, wave, lane, acc);
+    // the last steps refill ring slots with copies of the final stage, and
+    // those copies may still be landing: drain every wave's loads before the
+    // ring memory is reused for the output tile
+    wait_vm<0>();
+    __syncthreads();
 
     // ---- epilogue: accumulators (lane l holds column l%32 and rows
     // 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block) -> bf16 tile in LDS ->
     // 16-byte coalesced global stores of the valid rows.
     constexpr int NOUT = GATED ? C::NB / 2 : C::NB;
-    bf16_t* tile = lds;  // [MT][NOUT]; every wave left the ring at the last point
+    bf16_t* tile = lds;  // [MT][NOUT]
 #pragma unroll
     for (int i = 0; i < NBG; ++i) {
 #pragma unroll
