@@ -180,11 +180,9 @@ moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w,
 
 /* Profiling variants of the two calls above, for timing their kernels
  * with events on the caller's stream.  Same arguments, results and
- * workspace; in addition marks[0] is recorded after the tile-plan kernel,
- * marks[1] after the GEMM over the full row tiles and marks[2] after the
- * GEMM over the groups' short tails (for batches on the 32-row path, which
- * has a single GEMM launch, marks[1] and marks[2] are recorded together
- * after it).  marks[0..2] must be valid events (MOE_ERR_NULL otherwise). */
+ * workspace; in addition marks[0] is recorded after the tile-plan kernel
+ * and marks[1] after the GEMM kernel.  marks[0..1] must be valid events
+ * (MOE_ERR_NULL otherwise). */
 moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x,
                                      const moe_weights* w, const int32_t* offsets,
                                      const int32_t* sorted_pair, void* h, void* ws,

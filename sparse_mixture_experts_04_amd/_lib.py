@@ -208,16 +208,16 @@ def expert_down(desc, weights, offsets, h, y_routed, y_shared, ws=None):
 
 
 def _marks(events):
-    if len(events) != 3:
-        raise ValueError("three events are needed")
-    arr = (ctypes.c_void_p * 3)(*[e.cuda_event for e in events])
+    if len(events) != 2:
+        raise ValueError("two events are needed")
+    arr = (ctypes.c_void_p * 2)(*[e.cuda_event for e in events])
     return arr
 
 
 def expert_gate_up_marked(desc, x, weights, offsets, sorted_pair, h, events, ws=None):
-    """moe_expert_gate_up recording events[0..2] (torch.cuda.Event, created
+    """moe_expert_gate_up recording events[0..1] (torch.cuda.Event, created
     with enable_timing=True and recorded once beforehand) after the tile
-    plan, the full-tile GEMM and the tail GEMM."""
+    plan and after the GEMM kernel."""
     ws = alloc_workspace(desc, CALL_GATE_UP, offsets.device) if ws is None else ws
     st = lib.moe_expert_gate_up_marked(
         ctypes.byref(desc), _ptr(x, _act(desc), (desc.T, desc.d), "x"), ctypes.byref(weights),
@@ -229,7 +229,7 @@ def expert_gate_up_marked(desc, x, weights, offsets, sorted_pair, h, events, ws=
 
 
 def expert_down_marked(desc, weights, offsets, h, y_routed, y_shared, events, ws=None):
-    """moe_expert_down with the same three marks as expert_gate_up_marked."""
+    """moe_expert_down with the same two marks as expert_gate_up_marked."""
     ws = alloc_workspace(desc, CALL_DOWN, offsets.device) if ws is None else ws
     T, d, k, S = desc.T, desc.d, desc.k, desc.S
     st = lib.moe_expert_down_marked(

@@ -7,10 +7,14 @@
 //
 // * Tile: up to 256 rows x 256 weight rows, K step 32, 512 threads.  Wave
 //   (wm, wn) = (wave / 4, wave % 4) owns weight rows 64wn..64wn+63 (two
-//   32-wide MFMA column blocks) and row blocks 4wm..4wm+3.  The two waves
-//   of a SIMD (same wn) together cover every row block, so a row tile that
-//   is only partly filled skips whole 32-row MFMA blocks on every SIMD
-//   alike: the cost of an expert follows its row count in steps of 32.
+//   32-wide MFMA column blocks) and the 32-row blocks 2i + wm, i = 0..3.
+//   A tile that is only partly filled skips the MFMAs (and fragment reads)
+//   of its empty row blocks, so its cost follows its row count in steps of
+//   32 rows.
+// * Row tiles: a group of L rows is cut into t = ceil(L / 256) tiles of
+//   nearly equal size (multiples of 32 rows but the last), all in one
+//   launch, so every weight tile of an expert is streamed while all of its
+//   rows use it.
 // * GATED: the 64 weight rows of column group wn are the W_gate columns
 //   32wn..32wn+31 of the 128-column output tile followed by the same W_up
 //   columns; SwiGLU is applied to the accumulators in registers.
@@ -69,10 +73,11 @@ struct BigFrags {
 // Fragment reads.  Rows of a 32-row block differ only above bit 4, so the
 // swizzle depends only on the lane's row inside the block: one per-lane
 // offset per substep (`off[kk]`, in elements) plus a compile-time block
-// offset addresses every fragment.
-template <int NBG>
+// offset addresses every fragment.  `nv` (wave-uniform) is the number of
+// this wave's row blocks that hold rows of the tile.
 __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* sB, int grp,
-                                               int wn, const int (&off)[2], BigFrags& f) {
+                                               int wn, int nv, const int (&off)[2],
+                                               BigFrags& f) {
   using C = BigCfg;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk) {
@@ -81,23 +86,24 @@ __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* s
       f.b[kk][j] =
           *reinterpret_cast<const bf16x8_t*>(sB + (wn * 2 + j) * 1024 + off[kk]);
 #pragma unroll
-    for (int i = 0; i < NBG; ++i)
-      f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + grp) * 1024 + off[kk]);
+    for (int i = 0; i < C::BM; ++i)
+      if (i < nv)
+        f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + grp) * 1024 + off[kk]);
   }
 }
 
-template <int NBG>
-__device__ __forceinline__ void big_mfma(const BigFrags& f,
+__device__ __forceinline__ void big_mfma(const BigFrags& f, int nv,
                                          f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
   using C = BigCfg;
 #pragma unroll
   for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int i = 0; i < NBG; ++i)
+    for (int i = 0; i < C::BM; ++i)
+      if (i < nv)
 #pragma unroll
-      for (int j = 0; j < C::BN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j],
-                                                            0, 0, 0);
+        for (int j = 0; j < C::BN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j],
+                                                              0, 0, 0);
 }
 
 // The K loop with the two wave groups in ping-pong.  Barrier points are
@@ -115,29 +121,29 @@ __device__ __forceinline__ void big_mfma(const BigFrags& f,
 // group 0 starts reading it.  Past the last K step the loads repeat the
 // last step (L2 hits into slots never read), which keeps the counts
 // uniform.
-template <int NBG, int U, bool GATED>
+template <int U, bool GATED>
 __device__ __forceinline__ void big_pp_step(const BigCtx<GATED>& t, int kt, int nk,
                                             bf16_t* const (&sA)[4], bf16_t* const (&sB)[4],
-                                            int wave, int grp, int wn, const int (&off)[2],
+                                            int wave, int grp, int wn, int nv, const int (&off)[2],
                                             f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
   using C = BigCfg;
   constexpr int NXT = (U + 3) % 4;
   BigFrags f;
-  big_read_frags<NBG>(sA[U], sB[U], grp, wn, off, f);
+  big_read_frags(sA[U], sB[U], grp, wn, nv, off, f);
   const int kn = kt + 3 < nk ? kt + 3 : nk - 1;
   t.issue(kn * C::BK, sA[NXT], sB[NXT], wave);
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
   if (grp == 1) wait_vm<2 * C::LPW>();
   lds_barrier();
-  big_mfma<NBG>(f, acc);
+  big_mfma(f, nv, acc);
   if (grp == 0) wait_vm<2 * C::LPW>();
   lds_barrier();
 }
 
-template <int NBG, bool GATED>
+template <bool GATED>
 __device__ __forceinline__ void big_kloop(const BigCtx<GATED>& t, int nk,
                                           bf16_t* const (&sA)[4], bf16_t* const (&sB)[4],
-                                          int wave, int lane,
+                                          int wave, int lane, int nv,
                                           f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
   using C = BigCfg;
   const int grp = wave >> 2, wn = wave & 3;
@@ -150,21 +156,20 @@ __device__ __forceinline__ void big_kloop(const BigCtx<GATED>& t, int nk,
   lds_barrier();                  // point 0: stage 0 complete
   if (grp == 1) lds_barrier();    // point 1 for group 1 (its phase 0 is idle)
   for (int kt = 0; kt < nk; kt += 4) {
-    big_pp_step<NBG, 0, GATED>(t, kt, nk, sA, sB, wave, grp, wn, off, acc);
-    if (kt + 1 < nk) big_pp_step<NBG, 1, GATED>(t, kt + 1, nk, sA, sB, wave, grp, wn, off, acc);
-    if (kt + 2 < nk) big_pp_step<NBG, 2, GATED>(t, kt + 2, nk, sA, sB, wave, grp, wn, off, acc);
-    if (kt + 3 < nk) big_pp_step<NBG, 3, GATED>(t, kt + 3, nk, sA, sB, wave, grp, wn, off, acc);
+    big_pp_step<0, GATED>(t, kt, nk, sA, sB, wave, grp, wn, nv, off, acc);
+    if (kt + 1 < nk) big_pp_step<1, GATED>(t, kt + 1, nk, sA, sB, wave, grp, wn, nv, off, acc);
+    if (kt + 2 < nk) big_pp_step<2, GATED>(t, kt + 2, nk, sA, sB, wave, grp, wn, nv, off, acc);
+    if (kt + 3 < nk) big_pp_step<3, GATED>(t, kt + 3, nk, sA, sB, wave, grp, wn, nv, off, acc);
   }
   if (grp == 0) lds_barrier();    // both groups pass the same number of points
 }
 
-// One launch covers one tile list: the tiles with more than 128 rows
-// (NBG = 4 row blocks per wave group) or the groups' tails of at most 128
-// rows (NBG = 2).  Each instance is straight-line code, which keeps the
-// 128 accumulators and the fragments of a wave in registers.
-template <bool GATED, int NBG>
-__global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_t* list,
-                                                         bool tail_list, int32_t* counters) {
+// One launch covers every row tile of every group.  `plan` holds the row
+// tiles per group as an exclusive prefix (G+1 entries); `counters` the
+// per-XCD work counters, zero at launch.
+template <bool GATED>
+__global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_t* plan,
+                                                         int32_t* counters) {
   using C = BigCfg;
   // 4 ring slots of A and B tiles; after the K loop the same memory stages
   // the output tile for coalesced stores
@@ -178,10 +183,10 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 2, wn = wave & 3;
   const int G = p.E + p.S;
-  for (int g = tid; g <= G; g += C::THREADS) ts[g] = list[g];
+  for (int g = tid; g <= G; g += C::THREADS) ts[g] = plan[g];
   __syncthreads();
 
   const long long total = static_cast<long long>(ts[G]) * p.n_tiles;
@@ -207,7 +212,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     const int local = s_next;
     if (local >= len) break;
     const Item item =
-        decode_item(beg + local, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E, tail_list);
+        decode_item(beg + local, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E, true);
     const int g = item.g;
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
@@ -252,7 +257,10 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
 #pragma unroll
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    big_kloop<NBG, GATED>(t, nk, sA, sB, wave, lane, acc);
+    // row blocks of this wave's group (2i + wm) that hold rows of the tile
+    const int nblk = (item.rows + 31) >> 5;
+    const int nv = min((nblk - wm + 1) >> 1, C::BM);
+    big_kloop<GATED>(t, nk, sA, sB, wave, lane, nv, acc);
     // the last steps refill ring slots with copies of the final stage, and
     // those copies may still be landing: drain every wave's loads before the
     // ring memory is reused for the output tile
@@ -265,7 +273,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     constexpr int NOUT = GATED ? C::NB / 2 : C::NB;
     bf16_t* tile = lds;  // [MT][NOUT]
 #pragma unroll
-    for (int i = 0; i < NBG; ++i) {
+    for (int i = 0; i < C::BM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -303,43 +311,30 @@ static int device_cus_big() {
   return cus > 0 ? cus : 256;
 }
 
-// Tile lists for the large-batch GEMMs.  Group g (routed expert g, then the
-// shared experts) with L rows has L / 256 full tiles and a tail of L % 256
-// rows; a tail of more than 128 rows joins the full list (a 256-row tile),
-// a shorter one forms the tail list (a 128-row tile).  Writes both prefix
-// arrays and zeroes the work counters.
+// Tile plan of the large-batch GEMMs: group g (routed expert g, then the
+// shared experts) with L rows gets ceil(L / 256) row tiles.  Writes the
+// exclusive prefix over groups and zeroes both GEMMs' work counters.
 __global__ __launch_bounds__(512) void tile_plan_big_kernel(const int32_t* __restrict__ offsets,
                                                             int E, int S, int T,
                                                             int32_t* __restrict__ plan) {
-  __shared__ int sf[512], st[512];
+  __shared__ int sf[512];
   const int g = threadIdx.x;
   const int G = E + S;
   int rows = 0;
   if (g < E) rows = offsets[g + 1] - offsets[g];
   else if (g < G) rows = T;
-  const int rem = rows % BigCfg::MT;
-  const int nf = rows / BigCfg::MT + (rem > 128 ? 1 : 0);
-  const int nt = (rem > 0 && rem <= 128) ? 1 : 0;
-  sf[g] = nf;
-  st[g] = nt;
+  const int nt = (rows + BigCfg::MT - 1) / BigCfg::MT;
+  sf[g] = nt;
   __syncthreads();
   for (int off = 1; off < 512; off <<= 1) {
-    const int vf = g >= off ? sf[g - off] : 0;
-    const int vt = g >= off ? st[g - off] : 0;
+    const int v = g >= off ? sf[g - off] : 0;
     __syncthreads();
-    sf[g] += vf;
-    st[g] += vt;
+    sf[g] += v;
     __syncthreads();
   }
-  if (g < G) {
-    plan[g] = sf[g] - nf;
-    plan[G + 1 + g] = st[g] - nt;
-  }
-  if (g == G - 1) {
-    plan[G] = sf[g];
-    plan[2 * G + 1] = st[g];
-  }
-  if (g < 4 * kXcds) plan[2 * (G + 1) + g] = 0;
+  if (g < G) plan[g] = sf[g] - nt;
+  if (g == G - 1) plan[G] = sf[g];
+  if (g < 2 * kXcds) plan[G + 1 + g] = 0;
 }
 
 hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,
@@ -348,22 +343,14 @@ hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t*
   return hipGetLastError();
 }
 
-// `which`: 0 = gate/up, 1 = down (each has its own work counters).
-// marks (optional): events recorded after the full-tile launch (marks[0])
-// and after the tail launch (marks[1]).
 hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
                       hipEvent_t* marks, hipStream_t st) {
   const int G = a.E + a.S;
-  int32_t* ctr = const_cast<int32_t*>(plan) + 2 * (G + 1) + which * 2 * kXcds;
-  const int32_t* full = plan;
-  const int32_t* tail = plan + G + 1;
+  int32_t* ctr = const_cast<int32_t*>(plan) + (G + 1) + which * kXcds;
   const int grid = (device_cus_big() + kXcds - 1) / kXcds * kXcds;
-  if (gated) ffn_big_kernel<true, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
-  else ffn_big_kernel<false, 4><<<grid, BigCfg::THREADS, 0, st>>>(a, full, false, ctr);
+  if (gated) ffn_big_kernel<true><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
+  else ffn_big_kernel<false><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
   if (marks && hipEventRecord(marks[0], st) != hipSuccess) return hipErrorInvalidValue;
-  if (gated) ffn_big_kernel<true, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
-  else ffn_big_kernel<false, 2><<<grid, BigCfg::THREADS, 0, st>>>(a, tail, true, ctr + kXcds);
-  if (marks && hipEventRecord(marks[1], st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

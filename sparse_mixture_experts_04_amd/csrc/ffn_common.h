@@ -28,11 +28,12 @@ struct Item {
 // XCD share both activation and weight tiles.
 constexpr int kBand = 8;
 
-// tail_list: the list holds only each group's last, partial tile (rows
-// past the last multiple of MT); otherwise row tile m starts at m * MT.
+// balanced: a group of L rows in t row tiles gets tiles of
+// base = 32 * ceil(L / (32 t)) rows (the last one the rest, at least one
+// row); otherwise row tile m starts at m * MT.
 __device__ __forceinline__ Item decode_item(long long it, const int* ts, int G, int n_tiles,
                                             int MT, const int32_t* __restrict__ offsets, int T,
-                                            int E, bool tail_list = false) {
+                                            int E, bool balanced = false) {
   int lo = 0, hi = G;  // find last g with ts[g] * n_tiles <= it
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -59,9 +60,10 @@ __device__ __forceinline__ Item decode_item(long long it, const int* ts, int G, 
     m = full * band + rem % last;
   }
   r.grows = lo < E ? offsets[lo + 1] - offsets[lo] : T;
-  r.m0 = tail_list ? r.grows / MT * MT : m * MT;
+  const int base = balanced ? (r.grows + 32 * mt - 1) / (32 * mt) * 32 : MT;
+  r.m0 = m * base;
   const int left = r.grows - r.m0;
-  r.rows = left < MT ? left : MT;
+  r.rows = left < base ? left : base;
   return r;
 }
 
@@ -123,11 +125,13 @@ __device__ __forceinline__ void dma16(const bf16_t* src, bf16_t* dst) {
 constexpr int BigCfgRows = 256;
 hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,
                                 hipStream_t st);
-// Large-batch GEMMs: `plan` is the layout written by tile_plan_big_kernel.
+// Large-batch GEMMs: `plan` is the layout written by tile_plan_big_kernel;
+// `which` (0 = gate/up, 1 = down) picks the work counters; marks[0]
+// (optional) is recorded after the GEMM launch.
 hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
                       hipEvent_t* marks, hipStream_t st);
-// Per-group tile lists of the large-batch GEMM: [full (G+1) | tail (G+1) |
-// counters 2 GEMMs x 2 lists x kXcds].
-inline int big_plan_ints(int G) { return 2 * (G + 1) + 4 * kXcds; }
+// Tile plan of the large-batch GEMM: [row tiles per group, exclusive
+// prefix (G+1) | work counters 2 GEMMs x kXcds].
+inline int big_plan_ints(int G) { return (G + 1) + 2 * kXcds; }
 
 }  // namespace moe

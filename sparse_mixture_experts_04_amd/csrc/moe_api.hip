@@ -235,7 +235,7 @@ moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x, const 
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1] || !marks[2])
+  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1])
     return MOE_ERR_NULL;
   if (s.T > 0 && (!x || !sorted_pair || !h)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
@@ -257,7 +257,7 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1] || !marks[2])
+  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1])
     return MOE_ERR_NULL;
   if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
