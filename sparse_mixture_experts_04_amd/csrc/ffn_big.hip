@@ -36,29 +36,28 @@ struct BigCfg {
   static constexpr int BK = 32;
   static constexpr int MT = 256;
   static constexpr int NB = 256;
-  static constexpr int NS = 4;
+  static constexpr int NSA = 3;                       // A (activation) ring slots
+  static constexpr int NSB = 6;                       // B (weight) ring slots
   static constexpr int BM = MT / 32 / 2;              // row blocks per wave
   static constexpr int BN = 2;                        // column blocks per wave
-  static constexpr int A_LOADS = MT * 64 / 1024 / WAVES;  // KiB loads per wave per stage
-  static constexpr int B_LOADS = NB * 64 / 1024 / WAVES;
-  static constexpr int LPW = A_LOADS + B_LOADS;
-  static constexpr int STAGE_ELEMS = MT * BK;         // bf16 elements of one tile
-  static_assert((NS - 2) * LPW < 64, "vmcnt range");
+  static constexpr int LPW = MT * 64 / 1024 / (WAVES / 2);  // KiB loads per loading wave
+  static constexpr int STAGE_ELEMS = MT * BK;         // bf16 elements of one operand stage
+  static_assert(MT == NB, "both operands use the same load shape");
+  static_assert((NSB - 2) * LPW < 64, "vmcnt range");
 };
 
 __device__ __forceinline__ int swz4(int row) { return ((row >> 1) ^ (row >> 3)) & 3; }
 
-template <bool GATED>
+// Wave group 0 loads the weight (B) tiles, group 1 the activation (A)
+// tiles; each wave issues LPW 1 KiB loads per stage, load j = 4 * (wave % 4)
+// + q filling LDS rows 16j..16j+15 of its operand's slot.
 struct BigCtx {
   using C = BigCfg;
-  const bf16_t* a_src[C::A_LOADS];  // per-lane A source of each load (chunk applied)
-  const bf16_t* b_src[C::B_LOADS];  // per-lane B source of each load (chunk applied)
+  const bf16_t* src[C::LPW];  // per-lane source of each load (chunk applied)
 
-  __device__ __forceinline__ void issue(int k0, bf16_t* sA, bf16_t* sB, int wave) const {
+  __device__ __forceinline__ void issue(int k0, bf16_t* slot, int wig) const {
 #pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q) dma16(a_src[q] + k0, sA + (wave * C::A_LOADS + q) * 512);
-#pragma unroll
-    for (int q = 0; q < C::B_LOADS; ++q) dma16(b_src[q] + k0, sB + (wave * C::B_LOADS + q) * 512);
+    for (int q = 0; q < C::LPW; ++q) dma16(src[q] + k0, slot + (wig * C::LPW + q) * 512);
   }
 };
 
@@ -110,56 +109,72 @@ __device__ __forceinline__ void big_mfma(const BigFrags& f, int nv,
 // numbered 0, 1, 2, ...; group 0 runs memory(j) between points 2j and 2j+1
 // and compute(j) between 2j+1 and 2j+2, group 1 the same one point later.
 // So on every SIMD one wave issues MFMAs while its partner reads fragments
-// and issues the next loads.
-//   memory(j): read stage j's fragments into registers, issue this wave's
-//              share of the loads for stage j+3 into the slot of stage j-1
-//              (both groups finished reading it one point earlier), wait
-//              for the fragment reads;
+// and issues loads.
+//   memory(j): read stage j's fragments into registers; group 0 issues its
+//              share of the B loads of stage j+5 into the B slot of stage
+//              j-1, group 1 its share of the A loads of stage j+2 into the
+//              A slot of stage j-1 (both groups finished reading those one
+//              point earlier); wait for the fragment reads;
 //   compute(j): the MFMAs of stage j from registers.
 // Before every even point 2j, every wave has waited for its loads of stage
-// j (two later stages stay in flight), so stage j is complete in LDS when
-// group 0 starts reading it.  Past the last K step the loads repeat the
-// last step (L2 hits into slots never read), which keeps the counts
-// uniform.
+// j (the loads of later stages stay in flight: four for B, one for A), so
+// stage j is complete in LDS when group 0 starts reading it.  Weights come
+// from HBM with a long latency and get the deep ring; activation rows are
+// mostly L2 hits.  A wave's loads complete in issue order, so keeping each
+// operand on its own waves lets the B loads run far ahead without the A
+// waits depending on them.  Past the last K step the loads repeat the last
+// step (L2 hits into slots never read), which keeps the counts uniform.
 template <int U, bool GATED>
-__device__ __forceinline__ void big_pp_step(const BigCtx<GATED>& t, int kt, int nk,
-                                            bf16_t* const (&sA)[4], bf16_t* const (&sB)[4],
-                                            int wave, int grp, int wn, int nv, const int (&off)[2],
+__device__ __forceinline__ void big_pp_step(const BigCtx& t, int kt, int nk,
+                                            bf16_t* const (&sA)[BigCfg::NSA],
+                                            bf16_t* const (&sB)[BigCfg::NSB], int grp, int wig,
+                                            int nv, const int (&off)[2],
                                             f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
   using C = BigCfg;
-  constexpr int NXT = (U + 3) % 4;
   BigFrags f;
-  big_read_frags(sA[U], sB[U], grp, wn, nv, off, f);
-  const int kn = kt + 3 < nk ? kt + 3 : nk - 1;
-  t.issue(kn * C::BK, sA[NXT], sB[NXT], wave);
+  big_read_frags(sA[U % C::NSA], sB[U % C::NSB], grp, wig, nv, off, f);
+  {
+    const int ahead = grp == 0 ? C::NSB - 1 : C::NSA - 1;
+    const int ks = kt + ahead < nk ? kt + ahead : nk - 1;
+    bf16_t* slot = grp == 0 ? sB[(U + C::NSB - 1) % C::NSB] : sA[(U + C::NSA - 1) % C::NSA];
+    t.issue(ks * C::BK, slot, wig);
+  }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
-  if (grp == 1) wait_vm<2 * C::LPW>();
+  if (grp == 1) wait_vm<(C::NSA - 2) * C::LPW>();
   lds_barrier();
   big_mfma(f, nv, acc);
-  if (grp == 0) wait_vm<2 * C::LPW>();
+  if (grp == 0) wait_vm<(C::NSB - 2) * C::LPW>();
   lds_barrier();
 }
 
 template <bool GATED>
-__device__ __forceinline__ void big_kloop(const BigCtx<GATED>& t, int nk,
-                                          bf16_t* const (&sA)[4], bf16_t* const (&sB)[4],
-                                          int wave, int lane, int nv,
-                                          f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
+__device__ __forceinline__ void big_kloop(const BigCtx& t, int nk,
+                                          bf16_t* const (&sA)[BigCfg::NSA],
+                                          bf16_t* const (&sB)[BigCfg::NSB], int wave, int lane,
+                                          int nv, f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
   using C = BigCfg;
-  const int grp = wave >> 2, wn = wave & 3;
+  const int grp = wave >> 2, wig = wave & 3;
   const int r32 = lane & 31;
   const int off[2] = {r32 * 32 + (((lane >> 5) ^ swz4(r32)) << 3),
                       r32 * 32 + (((2 + (lane >> 5)) ^ swz4(r32)) << 3)};
+  if (grp == 0) {
 #pragma unroll
-  for (int s = 0; s < 3; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sA[s], sB[s], wave);
-  wait_vm<2 * C::LPW>();
+    for (int s = 0; s < C::NSB - 1; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sB[s], wig);
+    wait_vm<(C::NSB - 2) * C::LPW>();
+  } else {
+#pragma unroll
+    for (int s = 0; s < C::NSA - 1; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sA[s], wig);
+    wait_vm<(C::NSA - 2) * C::LPW>();
+  }
   lds_barrier();                  // point 0: stage 0 complete
   if (grp == 1) lds_barrier();    // point 1 for group 1 (its phase 0 is idle)
-  for (int kt = 0; kt < nk; kt += 4) {
-    big_pp_step<0, GATED>(t, kt, nk, sA, sB, wave, grp, wn, nv, off, acc);
-    if (kt + 1 < nk) big_pp_step<1, GATED>(t, kt + 1, nk, sA, sB, wave, grp, wn, nv, off, acc);
-    if (kt + 2 < nk) big_pp_step<2, GATED>(t, kt + 2, nk, sA, sB, wave, grp, wn, nv, off, acc);
-    if (kt + 3 < nk) big_pp_step<3, GATED>(t, kt + 3, nk, sA, sB, wave, grp, wn, nv, off, acc);
+  for (int kt = 0; kt < nk; kt += 6) {
+    big_pp_step<0, GATED>(t, kt, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 1 < nk) big_pp_step<1, GATED>(t, kt + 1, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 2 < nk) big_pp_step<2, GATED>(t, kt + 2, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 3 < nk) big_pp_step<3, GATED>(t, kt + 3, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 4 < nk) big_pp_step<4, GATED>(t, kt + 4, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 5 < nk) big_pp_step<5, GATED>(t, kt + 5, nk, sA, sB, grp, wig, nv, off, acc);
   }
   if (grp == 0) lds_barrier();    // both groups pass the same number of points
 }
@@ -171,15 +186,16 @@ template <bool GATED>
 __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_t* plan,
                                                          int32_t* counters) {
   using C = BigCfg;
-  // 4 ring slots of A and B tiles; after the K loop the same memory stages
-  // the output tile for coalesced stores
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[8 * C::STAGE_ELEMS];
+  // ring slots of the A and B tiles; after the K loop the same memory
+  // stages the output tile for coalesced stores
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[(C::NSA + C::NSB) * C::STAGE_ELEMS];
   __shared__ int ts[512];
   __shared__ int s_next;
-  bf16_t* const sA[4] = {lds, lds + 2 * C::STAGE_ELEMS, lds + 4 * C::STAGE_ELEMS,
-                         lds + 6 * C::STAGE_ELEMS};
-  bf16_t* const sB[4] = {lds + C::STAGE_ELEMS, lds + 3 * C::STAGE_ELEMS,
-                         lds + 5 * C::STAGE_ELEMS, lds + 7 * C::STAGE_ELEMS};
+  bf16_t* const sA[C::NSA] = {lds, lds + C::STAGE_ELEMS, lds + 2 * C::STAGE_ELEMS};
+  bf16_t* sB[C::NSB];
+#pragma unroll
+  for (int i = 0; i < C::NSB; ++i) sB[i] = lds + (C::NSA + i) * C::STAGE_ELEMS;
+  static_assert(C::NSA == 3, "slot list");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -217,36 +233,40 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
                                    : kT + static_cast<size_t>(g - p.E) * p.T;
-    BigCtx<GATED> t;
+    BigCtx t;
+    if (wm == 1) {
 #pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q) {
-      const int j = wave * C::A_LOADS + q;
-      int r = j * 16 + lrow;
-      r = r < item.rows ? r : item.rows - 1;
-      const int rr = item.m0 + r;
-      size_t src_row;
-      if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
-                                  : static_cast<size_t>(rr);
-      else src_row = row_base + rr;
-      t.a_src[q] = A + src_row * p.K + lchunk[j & 1];
-    }
-    const int ge = routed ? g : g - p.E;
-#pragma unroll
-    for (int q = 0; q < C::B_LOADS; ++q) {
-      const int j = wave * C::B_LOADS + q;
-      const int R = j * 16 + lrow;  // LDS B row
-      const int grp = R >> 6, rl = R & 63;
-      const bf16_t* base;
-      int col;
-      if (GATED) {
-        const bool up = rl >= 32;
-        base = static_cast<const bf16_t*>(up ? (routed ? p.w1 : p.ws1) : (routed ? p.w0 : p.ws0));
-        col = item.n * (C::NB / 2) + grp * 32 + (rl & 31);
-      } else {
-        base = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0);
-        col = item.n * C::NB + R;
+      for (int q = 0; q < C::LPW; ++q) {
+        const int j = wn * C::LPW + q;
+        int r = j * 16 + lrow;
+        r = r < item.rows ? r : item.rows - 1;
+        const int rr = item.m0 + r;
+        size_t src_row;
+        if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
+                                    : static_cast<size_t>(rr);
+        else src_row = row_base + rr;
+        t.src[q] = A + src_row * p.K + lchunk[j & 1];
       }
-      t.b_src[q] = base + ge * wstride + static_cast<size_t>(col) * p.K + lchunk[j & 1];
+    } else {
+      const int ge = routed ? g : g - p.E;
+#pragma unroll
+      for (int q = 0; q < C::LPW; ++q) {
+        const int j = wn * C::LPW + q;
+        const int R = j * 16 + lrow;  // LDS B row
+        const int cg = R >> 6, rl = R & 63;
+        const bf16_t* base;
+        int col;
+        if (GATED) {
+          const bool up = rl >= 32;
+          base = static_cast<const bf16_t*>(up ? (routed ? p.w1 : p.ws1)
+                                               : (routed ? p.w0 : p.ws0));
+          col = item.n * (C::NB / 2) + cg * 32 + (rl & 31);
+        } else {
+          base = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0);
+          col = item.n * C::NB + R;
+        }
+        t.src[q] = base + ge * wstride + static_cast<size_t>(col) * p.K + lchunk[j & 1];
+      }
     }
 
     f32x16_t acc[C::BM][C::BN];
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
           const float gt = acc[i][0][r];
           const float up = acc[i][1][r];
           tile[row * NOUT + wn * 32 + (lane & 31)] =
-              f32_to_bf16(gt * __frcp_rn(1.0f + __expf(-gt)) * up);
+              f32_to_bf16(gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up);
         } else {
 #pragma unroll
           for (int j = 0; j < C::BN; ++j)
