@@ -9,6 +9,9 @@ namespace moe {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
 
+// Generic -> LDS address-space cast of a pointer into a __shared__ array.
+#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));

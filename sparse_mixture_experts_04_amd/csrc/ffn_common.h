@@ -86,7 +86,6 @@ struct FfnArgs {
 
 // ---------------------------------------------------------- LDS helpers
 
-#define LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
 
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 

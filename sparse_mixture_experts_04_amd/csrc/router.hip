@@ -62,6 +62,26 @@ __device__ __forceinline__ void split3(const float (&v)[8], bf16x8_t& p0, bf16x8
   p2 = __builtin_bit_cast(bf16x8_t, c);
 }
 
+// x fragments of one K step for the 4 row blocks of a lane, straight from
+// global memory (fp32 x is split into its 3 bf16 planes on the fly).
+template <int NXP>
+__device__ __forceinline__ void router_load_x(const void* __restrict__ xv, const size_t (&xoff)[4],
+                                              int k, bf16x8_t (&a)[NXP][4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if constexpr (NXP == 1) {
+      const bf16_t* xp = static_cast<const bf16_t*>(xv) + xoff[i] + k;
+      a[0][i] = *reinterpret_cast<const bf16x8_t*>(xp);
+    } else {
+      const float* xp = static_cast<const float*>(xv) + xoff[i] + k;
+      const float4 v0 = *reinterpret_cast<const float4*>(xp);
+      const float4 v1 = *reinterpret_cast<const float4*>(xp + 4);
+      const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      split3(v, a[0][i], a[1][i], a[2][i]);
+    }
+  }
+}
+
 // Workgroup tile: 128 tokens x 64 router columns over one K range.
 // 4 waves: wave (wm, wn) owns tokens wm*64..+64 and columns wn*32..+32 as
 // 4 x 2 blocks of 16x16 (MFMA 16x16x32 bf16).  The W planes are staged in
@@ -121,27 +141,21 @@ __global__ __launch_bounds__(256) void router_logits(
   for (int p = 0; p < 3; ++p) *reinterpret_cast<uint4*>(&sB[0][p][brow][bkc]) = breg[p];
   __syncthreads();
 
+  bf16x8_t a[NXP][4], an[NXP][4];
+  router_load_x<NXP>(xv, xoff, kbeg, an);
+
   for (int s = 0; s < nsteps; ++s) {
     const int k = kbeg + s * KS;
     const int buf = s & 1;
+#pragma unroll
+    for (int q = 0; q < NXP; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[q][i] = an[q][i];
     if (s + 1 < nsteps) {
 #pragma unroll
       for (int p = 0; p < 3; ++p)
         breg[p] = *reinterpret_cast<const uint4*>(bsrc + p * pstride + k + KS);
-    }
-    bf16x8_t a[NXP][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if constexpr (NXP == 1) {
-        const bf16_t* xp = static_cast<const bf16_t*>(xv) + xoff[i] + k;
-        a[0][i] = *reinterpret_cast<const bf16x8_t*>(xp);
-      } else {
-        const float* xp = static_cast<const float*>(xv) + xoff[i] + k;
-        const float4 v0 = *reinterpret_cast<const float4*>(xp);
-        const float4 v1 = *reinterpret_cast<const float4*>(xp + 4);
-        const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        split3(v, a[0][i], a[1][i], a[2][i]);
-      }
+      router_load_x<NXP>(xv, xoff, k + KS, an);
     }
     bf16x8_t b[3][2];
 #pragma unroll
@@ -188,6 +202,137 @@ __global__ __launch_bounds__(256) void router_logits(
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = tok0 + i * 16 + 4 * (lane >> 4) + r;
+        const int c = col0 + wn * 32 + j * 16 + (lane & 15);
+        if (t < T) out[static_cast<size_t>(t) * npad + c] = run[i][j][r];
+      }
+}
+
+// Logits for bf16 x with direct global -> LDS loads.  Same tile and
+// arithmetic as router_logits<1> (128 tokens x 64 columns, MFMA 16x16x32,
+// a fresh fp32 accumulator per 32-wide K step added into fp64 sums), with
+// the x rows and the three W planes of each K step staged through a ring
+// of RS stages so that several steps of loads are in flight.  LDS rows are
+// 64 bytes with chunk c of row r in slot c ^ f(r), f(r) = ((r >> 1) ^
+// (r >> 3)) & 3, which keeps the 16-lane fragment reads conflict-free.
+constexpr int kRouterRing = 4;
+constexpr int kRouterStageElems = (128 + 3 * 64) * 32;  // x rows, then 3 planes x 64 rows
+
+__global__ __launch_bounds__(256) void router_logits_bf16(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, int T, int d, int npad,
+    int nks, double* __restrict__ partial) {
+  constexpr int KS = 32;
+  constexpr int RS = kRouterRing;
+  constexpr int SE = kRouterStageElems;
+  constexpr int LPW = 5;  // 1 KiB loads per wave per stage: 8 for x, 12 for the planes
+  constexpr int STEPS_PER_CHUNK = kRouterChunk / KS;
+  __shared__ __attribute__((aligned(1024))) bf16_t ring[RS * SE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave & 1, wn = wave >> 1;
+  const int tok0 = blockIdx.x * 128;
+  const int col0 = blockIdx.y * 64;
+
+  const int nch = d / kRouterChunk;
+  const int ch_b = static_cast<int>(static_cast<long long>(blockIdx.z) * nch / nks);
+  const int ch_e = static_cast<int>(static_cast<long long>(blockIdx.z + 1) * nch / nks);
+  const int kbeg = ch_b * kRouterChunk;
+  const int nsteps = (ch_e - ch_b) * STEPS_PER_CHUNK;
+
+  // load j (16 LDS rows) of a stage: j < 8 x rows 16j.., else plane
+  // (j - 8) / 4, rows 16 ((j - 8) % 4)..; lane l fills slot l % 4 of row
+  // l / 4 of its load with source chunk (l % 4) ^ f(row)
+  const size_t pstride = static_cast<size_t>(npad) * d;
+  const int lrow = lane >> 2;
+  const int cbase = (lane & 3) ^ (((lane >> 3) ^ (lane >> 5)) & 3);
+  const bf16_t* src[LPW];
+  uint32_t dst_off[LPW];
+#pragma unroll
+  for (int q = 0; q < LPW; ++q) {
+    const int j = wave * LPW + q;
+    const int chunk = (cbase ^ ((j & 1) << 1)) * 8;
+    if (j < 8) {
+      int r = tok0 + j * 16 + lrow;
+      r = r < T ? r : T - 1;
+      src[q] = x + static_cast<size_t>(r) * d + kbeg + chunk;
+    } else {
+      const int jb = j - 8;
+      src[q] = planes + (jb >> 2) * pstride +
+               static_cast<size_t>(col0 + (jb & 3) * 16 + lrow) * d + kbeg + chunk;
+    }
+    dst_off[q] = static_cast<uint32_t>(j * 512 * sizeof(bf16_t));
+  }
+  const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(ring)));
+  auto issue = [&](int s, int slot) {
+    const int ko = (s < nsteps ? s : nsteps - 1) * KS;
+#pragma unroll
+    for (int q = 0; q < LPW; ++q) {
+      const uint32_t m0 = __builtin_amdgcn_readfirstlane(ring_base + slot * SE * 2 + dst_off[q]);
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+                   :
+                   : "v"(src[q] + ko), "s"(m0)
+                   : "m0");
+    }
+  };
+
+  // fragment offsets: row r16 = lane % 16 of a 16-row block whose bit 4 is
+  // the block's parity, chunk lane / 16
+  const int r16 = lane & 15;
+  const int f0 = ((r16 >> 1) ^ (r16 >> 3)) & 3;
+  const int cq = lane >> 4;
+  const int offe = r16 * 32 + ((cq ^ f0) << 3);
+  const int offo = r16 * 32 + ((cq ^ f0 ^ 2) << 3);
+
+  double run[4][2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) run[i][j][r] = 0.0;
+
+#pragma unroll
+  for (int s = 0; s < RS - 1; ++s) issue(s, s);
+  for (int s = 0; s < nsteps; ++s) {
+    __builtin_amdgcn_s_waitcnt((((RS - 2) * LPW) & 0xF) | (0x7 << 4) | (0xF << 8) |
+                               ((((RS - 2) * LPW) >> 4) << 14));  // stage s landed
+    __builtin_amdgcn_s_barrier();
+    issue(s + RS - 1, (s + RS - 1) % RS);
+    const bf16_t* st = ring + (s % RS) * SE;
+    bf16x8_t a[4], b[3][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      a[i] = *reinterpret_cast<const bf16x8_t*>(st + (wm * 64 + i * 16) * 32 + ((i & 1) ? offo : offe));
+#pragma unroll
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[p][j] = *reinterpret_cast<const bf16x8_t*>(st + (128 + p * 64 + wn * 32 + j * 16) * 32 +
+                                                     ((j & 1) ? offo : offe));
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[2][j], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[1][j], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[0][j], c, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) run[i][j][r] += static_cast<double>(c[r]);
+      }
+  }
+  __builtin_amdgcn_s_waitcnt(0 | (0x7 << 4) | (0xF << 8));
+
+  // 16x16 accumulator layout: lane l holds column l%16, rows 4*(l/16)+r.
+  double* out = partial + static_cast<size_t>(blockIdx.z) * T * npad;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = tok0 + wm * 64 + i * 16 + 4 * (lane >> 4) + r;
         const int c = col0 + wn * 32 + j * 16 + (lane & 15);
         if (t < T) out[static_cast<size_t>(t) * npad + c] = run[i][j][r];
       }
@@ -302,7 +447,7 @@ __global__ __launch_bounds__(256) void router_select(
 int router_ksplits(const Shape& s) {
   const int tiles = ((s.T + 127) / 128) * (router_cols_padded(s) / kRouterColTile);
   const int nch = s.d / kRouterChunk;
-  int want = (512 + tiles - 1) / (tiles > 0 ? tiles : 1);
+  int want = (1280 + tiles - 1) / (tiles > 0 ? tiles : 1);  // ~2.5 waves of 2 workgroups per CU
   if (want < 1) want = 1;
   return want < nch ? want : nch;
 }
@@ -319,7 +464,8 @@ hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
   const int nks = router_ksplits(s);
   dim3 grid((s.T + 127) / 128, npad / kRouterColTile, nks);
   if (s.bf16)
-    router_logits<1><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, partial);
+    router_logits_bf16<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), wplanes, s.T, s.d,
+                                              npad, nks, partial);
   else
     router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, partial);
   router_select<6, 2><<<(s.T + 3) / 4, 256, 0, st>>>(partial, nks, s.T, npad, s.E, bias,
