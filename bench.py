@@ -7,7 +7,10 @@ combine, bias update) over one batch already resident in HBM:
 
 * headline workload: T=16384 tokens, d=7168, F=2048, 256 routed + 2 shared
   experts, top-6, bf16 weights and activations, fp32 router;
-* decode workload (reported alongside): the same layer at T=64.
+* decode workload (reported alongside): the same layer at T=64;
+* skewed workload (reported alongside): the headline shape with a skewed
+  router, 100 consecutive batches (fresh tokens each) and the balancing
+  bias updating after every batch.
 
 Prints one JSON line.  ``value`` is tokens/s of the headline workload;
 ``roofline`` is for its dominant kernel, the grouped gate/up GEMM (matrix
@@ -37,8 +40,11 @@ def parse():
     ap.add_argument("--workload", default="D", help="headline workload (D)")
     ap.add_argument("--decode-workload", default="C")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--skewed-workload", default="E")
+    ap.add_argument("--skewed-steps", type=int, default=100)
+    ap.add_argument("--no-skewed", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run one device-to-device copy of this size (for scaling "
                          "hardware byte counters)")
@@ -158,6 +164,44 @@ def traffic_for(kernel_file, profile):
     if rec.get("source_sha256") != digest:
         return None
     return rec.get("bytes_per_launch")
+
+
+def time_skewed(cfg, steps, torch, L, synth):
+    """Consecutive batches of the skewed workload: fresh tokens every batch
+    (generated outside the timed region), the bias carried from batch to
+    batch.  Returns per-batch times and the routing load statistics."""
+    import statistics
+    inp, desc, w, y, counts, ws = setup(cfg, torch, L, synth)
+    bias = inp["bias"].clone()
+    routing = {"counts": counts}
+    mean_load = cfg.T * cfg.k / cfg.E
+    ms, maxmean = [], []
+    for s in range(steps + 1):          # batch 0 also warms up
+        x = synth.make_x(cfg, device="cuda", step=s)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        L.forward(desc, x, w, bias, cfg.gamma, y, routing, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        if s > 0:
+            ms.append(e0.elapsed_time(e1))
+        maxmean.append(counts.max().item() / mean_load)
+    f_gu, f_dn = expert_flops(cfg)
+    med = statistics.median(ms)
+    del inp, w, ws, y
+    torch.cuda.empty_cache()
+    return {"workload": f"skewed MoE layer, {cfg.describe()}, router offset kappa="
+                        f"{cfg.skew_kappa}, {steps} consecutive batches, bias step "
+                        f"{cfg.gamma}",
+            "ms_per_step_median": round(med, 4),
+            "ms_per_step_p10_p90": [round(sorted(ms)[len(ms) // 10], 4),
+                                    round(sorted(ms)[(9 * len(ms)) // 10], 4)],
+            "tokens_s": round(cfg.T / (med / 1e3), 1),
+            "mfma_frac": round((f_gu + f_dn) / (med / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "max_over_mean_load": {"first": round(maxmean[0], 3),
+                                   "middle": round(maxmean[len(maxmean) // 2], 3),
+                                   "last": round(maxmean[-1], 3)},
+            "bias_range": [round(bias.min().item(), 5), round(bias.max().item(), 5)]}
 
 
 def decode_bytes(cfg, counts):
@@ -280,6 +324,9 @@ def main():
                          "scope": "whole moe_forward step"}}
         del d_inp, d_ws
         torch.cuda.empty_cache()
+    if not args.no_skewed:
+        result["skewed"] = time_skewed(configs.get(args.skewed_workload), args.skewed_steps,
+                                       torch, L, synth)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch)
     print(json.dumps(result), flush=True)
