@@ -10,7 +10,10 @@ combine, bias update) over one batch already resident in HBM:
 * decode workload (reported alongside): the same layer at T=64;
 * skewed workload (reported alongside): the headline shape with a skewed
   router, 100 consecutive batches (fresh tokens each) and the balancing
-  bias updating after every batch.
+  bias updating after every batch;
+* native-shape workload (reported alongside): hidden 6144, expert width
+  3072, gates by logsumexp over log-sigmoids times a route scale, at the
+  headline batch size.
 
 Prints one JSON line.  ``value`` is tokens/s of the headline workload;
 ``roofline`` is for its dominant kernel, the grouped gate/up GEMM (matrix
@@ -43,6 +46,8 @@ def parse():
     ap.add_argument("--skewed-workload", default="E")
     ap.add_argument("--skewed-steps", type=int, default=100)
     ap.add_argument("--no-skewed", action="store_true")
+    ap.add_argument("--native-workload", default="I")
+    ap.add_argument("--no-native", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -59,7 +64,8 @@ def expert_flops(cfg):
 
 def setup(cfg, torch, L, synth):
     inp = synth.make_inputs(cfg, device="cuda")
-    desc = L.make_desc(cfg.T, cfg.d, cfg.F, synth.act_dtype(cfg))
+    desc = L.make_desc(cfg.T, cfg.d, cfg.F, synth.act_dtype(cfg), gate_norm=cfg.gate_norm,
+                       gate_scale=cfg.gate_scale)
     w = L.weights_from(inp)
     y = torch.empty((cfg.T, cfg.d), dtype=synth.act_dtype(cfg), device="cuda")
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
@@ -323,6 +329,18 @@ def main():
                          "bytes": nbytes, "active_experts": n_active,
                          "scope": "whole moe_forward step"}}
         del d_inp, d_ws
+        torch.cuda.empty_cache()
+    if not args.no_native:
+        nc = configs.get(args.native_workload)
+        n_inp, _, _, n_ws, _, n_ms, _ = time_forward(nc, max(5, min(args.steps, 10)),
+                                                     args.warmup, torch, L, synth)
+        f_gu_n, f_dn_n = expert_flops(nc)
+        result["native"] = {
+            "workload": f"MoE layer at the native shape, {nc.describe()}, gates "
+                        f"{nc.gate_norm} x {nc.gate_scale}, fp32 router",
+            "tokens_s": round(nc.T / (n_ms / 1e3), 1), "ms_per_step": round(n_ms, 4),
+            "mfma_frac": round((f_gu_n + f_dn_n) / (n_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+        del n_inp, n_ws
         torch.cuda.empty_cache()
     if not args.no_skewed:
         result["skewed"] = time_skewed(configs.get(args.skewed_workload), args.skewed_steps,

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -92,13 +92,30 @@ typedef enum {
   MOE_CALL_FORWARD = 7
 } moe_call;
 
+/* How the gates of the k kept routed experts and the S shared experts are
+ * normalised (the top-k selection is the same for both):
+ *   MOE_GATE_RATIO      g_j = s_j / sum_i s_i over the k + S contributors,
+ *                       s = sigmoid(z) ("Inkling, Dissected", 02b);
+ *   MOE_GATE_LOGSUMEXP  g_j = exp(logsigmoid(z_j) - logsumexp_i logsigmoid(z_i))
+ *                       over the same set ("Under The Hood: Inkling", the
+ *                       routing strategy: log-sigmoid, then logsumexp over
+ *                       the joint set of 8).
+ * Both equal each other in exact arithmetic; they differ in rounding only.
+ * Either is then multiplied by gate_scale (1 for the first page's layer;
+ * route_scale * global_scale, e.g. 8.0 times the learned scalar, for the
+ * second page's configuration). */
+typedef enum { MOE_GATE_RATIO = 0, MOE_GATE_LOGSUMEXP = 1 } moe_gate_norm;
+
 /* Layer shape.  T tokens, hidden d, expert ffn width F, E routed experts,
  * S shared experts, k routed experts per token; act is the dtype of x, h,
  * y and the expert weights, weight must equal act.  The router weights and
- * the bias are always fp32. */
+ * the bias are always fp32.  gate_norm and gate_scale (finite, > 0) set the
+ * gate normalisation above. */
 typedef struct {
   int32_t T, d, F, E, S, k;
   moe_dtype act, weight;
+  int32_t gate_norm;  /* moe_gate_norm */
+  float gate_scale;
 } moe_desc;
 
 /* Weights of one layer.  Expert matrices are [out, in] row-major:

@@ -28,7 +28,9 @@ Sources (page title, section):
 * "Under The Hood: Inkling from Thinking Machines", "MoE: the expert
   configuration" (each expert is a SwiGLU FFN; shared experts have the same
   width) and "The routing strategy: sigmoid + shared expert sink" (top-6 over
-  routed experts only; shared scores join the normalisation).
+  routed experts only; shared scores join the normalisation, written there
+  as log-sigmoid followed by logsumexp over the joint set of 8, and the
+  weights are then scaled by route_scale times a learned global scale).
 
 Readings where the pages leave a step open:
 
@@ -88,28 +90,63 @@ def select_topk(key, k):
     return top.astype(np.int64), margin
 
 
-def joint_gates(s, top, shared_ids):
+def _joint_idx(top, shared_ids, T):
+    shared = np.broadcast_to(np.asarray(shared_ids, dtype=np.int64),
+                             (T, len(shared_ids)))
+    return np.concatenate([top, shared], axis=1)
+
+
+def joint_gates(s, top, shared_ids, scale=1.0):
     """g over the kept routed experts followed by the shared experts.
 
     g_i = s_i / sum_{j in kept U shared} s_j, summed in slot order (02b; the
-    shared-expert sink of the Hugging Face write-up).  ``s`` holds raw
-    affinities: the balancing bias never enters the gates.
+    shared-expert sink of the Hugging Face write-up), times ``scale`` (1 for
+    the layer of "Inkling, Dissected").  ``s`` holds raw affinities: the
+    balancing bias never enters the gates.
     """
     s = _f64(s)
     T = s.shape[0]
-    shared = np.broadcast_to(np.asarray(shared_ids, dtype=np.int64),
-                             (T, len(shared_ids)))
-    idx = np.concatenate([top, shared], axis=1)
+    idx = _joint_idx(top, shared_ids, T)
     sel = np.take_along_axis(s, idx, axis=1)
     denom = np.zeros(T)
     for j in range(sel.shape[1]):
         denom = denom + sel[:, j]
-    return sel / denom[:, None], idx
+    return sel / denom[:, None] * scale, idx
 
 
-def route(x, w_router, bias, n_routed=256, k=6):
+def logsigmoid(z):
+    """log(sigmoid(z)) = min(z, 0) - log(1 + exp(-|z|)), float64."""
+    z = _f64(z)
+    return np.minimum(z, 0.0) - np.log1p(np.exp(-np.abs(z)))
+
+
+def joint_gates_logsumexp(z, top, shared_ids, scale=1.0):
+    """Gates in the form of "Under The Hood: Inkling", the routing strategy:
+    the logits of the kept routed experts and of the shared experts go
+    through log-sigmoid, are normalised by their logsumexp over that joint
+    set, and the weights are multiplied by ``scale`` (route_scale times the
+    learned global scale).
+
+    g_i = exp(ls_i - lse), ls = logsigmoid(z[kept U shared]),
+    lse = m + log(sum_j exp(ls_j - m)), m = max_j ls_j (sum in slot order).
+    """
+    z = _f64(z)
+    T = z.shape[0]
+    idx = _joint_idx(top, shared_ids, T)
+    ls = logsigmoid(np.take_along_axis(z, idx, axis=1))
+    m = ls.max(axis=1)
+    acc = np.zeros(T)
+    for j in range(ls.shape[1]):
+        acc = acc + np.exp(ls[:, j] - m)
+    lse = m + np.log(acc)
+    return np.exp(ls - lse[:, None]) * scale, idx
+
+
+def route(x, w_router, bias, n_routed=256, k=6, gate_norm="ratio", gate_scale=1.0):
     """Router of one batch: sigmoid affinities, biased top-k, joint gates.
 
+    ``gate_norm`` is "ratio" (``joint_gates``) or "logsumexp"
+    (``joint_gates_logsumexp``); both scale the gates by ``gate_scale``.
     Returns a dict with ``z`` [T, n_routed+n_shared], ``s`` (affinities),
     ``key`` = s[:, :n_routed] + b, ``topk_idx`` [T, k] in rank order,
     ``margin`` [T], ``gates`` [T, k + n_shared] (routed slots first, then the
@@ -120,7 +157,13 @@ def route(x, w_router, bias, n_routed=256, k=6):
     n_total = s.shape[1]
     key = s[:, :n_routed] + _f64(bias)[None, :]
     top, margin = select_topk(key, k)
-    gates, idx = joint_gates(s, top, list(range(n_routed, n_total)))
+    shared = list(range(n_routed, n_total))
+    if gate_norm == "ratio":
+        gates, idx = joint_gates(s, top, shared, gate_scale)
+    elif gate_norm == "logsumexp":
+        gates, idx = joint_gates_logsumexp(z, top, shared, gate_scale)
+    else:
+        raise ValueError(gate_norm)
     return {"z": z, "s": s, "key": key, "topk_idx": top, "margin": margin,
             "gates": gates, "idx": idx}
 

@@ -36,7 +36,8 @@ class MoEError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("S", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("act", ctypes.c_int), ("weight", ctypes.c_int)]
+                ("act", ctypes.c_int), ("weight", ctypes.c_int),
+                ("gate_norm", ctypes.c_int32), ("gate_scale", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
@@ -96,9 +97,13 @@ def act_code(dtype):
     raise TypeError(f"unsupported activation dtype {dtype}")
 
 
-def make_desc(T, d, F, act_dtype, E=256, S=2, k=6):
+GATE_RATIO, GATE_LOGSUMEXP = 0, 1
+
+
+def make_desc(T, d, F, act_dtype, E=256, S=2, k=6, gate_norm="ratio", gate_scale=1.0):
     a = act_code(act_dtype)
-    return Desc(T, d, F, E, S, k, a, a)
+    norm = {"ratio": GATE_RATIO, "logsumexp": GATE_LOGSUMEXP}[gate_norm]
+    return Desc(T, d, F, E, S, k, a, a, norm, gate_scale)
 
 
 def _act(desc):

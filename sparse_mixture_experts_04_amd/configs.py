@@ -9,7 +9,11 @@ stand-ins chosen to exercise the regimes that matter on one GPU:
 * ``B``  a prefill chunk in bf16;
 * ``C``  decode-sized: 64 tokens, bound by streaming expert weights;
 * ``D``  large batch: 16384 tokens at hidden 7168, bound by matrix cores;
-* ``E``  shape of ``D`` with a skewed router, run for 100 bias-update steps.
+* ``E``  shape of ``D`` with a skewed router, run for 100 bias-update steps;
+* ``I``  the configuration of "Under The Hood: Inkling" (hidden 6144, expert
+  width 3072, gates normalised by logsumexp over log-sigmoids and scaled by
+  route_scale = 8 times a global scale; the learned global scale is stood in
+  for by 0.8125), at the large batch of ``D``.
 
 No arithmetic of the method lives here.
 """
@@ -32,6 +36,8 @@ class MoEConfig:
     skew_kappa: float = 0.0    # router skew strength (workload E only)
     skew_zipf_s: float = 1.2   # exponent of the per-expert router offset
     steps: int = 1         # bias-update steps the workload runs
+    gate_norm: str = "ratio"   # "ratio" or "logsumexp"
+    gate_scale: float = 1.0    # multiplier of every gate
     extra: dict = field(default_factory=dict)
 
     @property
@@ -51,6 +57,8 @@ CONFIGS = {
     "D": MoEConfig("D", T=16384, d=7168, F=2048, act="bf16", bias_range=0.05),
     "E": MoEConfig("E", T=16384, d=7168, F=2048, act="bf16", bias_range=0.0,
                    skew_kappa=8.0, steps=100),
+    "I": MoEConfig("I", T=16384, d=6144, F=3072, act="bf16", bias_range=0.05,
+                   gate_norm="logsumexp", gate_scale=8.0 * 0.8125),
 }
 
 

@@ -40,6 +40,8 @@ template <> struct ActTraits<bf16_t> {
 struct Shape {
   int T, d, F, E, S, k;
   bool bf16;
+  bool gate_logsumexp = false;  // gate normalisation (router only)
+  float gate_scale = 1.0f;
 };
 
 // Router columns are padded to a multiple of the router's column tile.

@@ -20,6 +20,8 @@ moe_status check_desc(const moe_desc* d) {
   if (d->T < 0 || d->d <= 0 || d->F <= 0 || d->E <= 0 || d->S < 0 || d->k <= 0)
     return MOE_ERR_SHAPE;
   if ((d->act != MOE_F32 && d->act != MOE_BF16) || d->weight != d->act) return MOE_ERR_DTYPE;
+  if (d->gate_norm != MOE_GATE_RATIO && d->gate_norm != MOE_GATE_LOGSUMEXP) return MOE_ERR_SHAPE;
+  if (!(d->gate_scale > 0.0f) || !(d->gate_scale < INFINITY)) return MOE_ERR_SHAPE;
   if (d->E != 256 || d->S != 2 || d->k != 6) return MOE_ERR_UNSUPPORTED;
   if (d->d % 256 != 0 || d->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const long long T = d->T;
@@ -38,6 +40,8 @@ Shape to_shape(const moe_desc* d) {
   s.S = d->S;
   s.k = d->k;
   s.bf16 = d->act == MOE_BF16;
+  s.gate_logsumexp = d->gate_norm == MOE_GATE_LOGSUMEXP;
+  s.gate_scale = d->gate_scale;
   return s;
 }
 

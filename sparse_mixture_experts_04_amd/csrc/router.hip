@@ -352,12 +352,12 @@ template <int K, int S>
 __global__ __launch_bounds__(256) void router_select(
     const double* __restrict__ partial, int nks, int T, int npad, int E,
     const float* __restrict__ bias, int32_t* __restrict__ topk, float* __restrict__ gates,
-    float* __restrict__ margin) {
+    float* __restrict__ margin, bool logsumexp_norm, double gate_scale) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together; no block barrier below
 
-  double sv[4], key[4];
+  double sv[4], zv[4], key[4];
   bool taken[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -366,18 +366,20 @@ __global__ __launch_bounds__(256) void router_select(
     for (int ks = 0; ks < nks; ++ks) z += partial[(static_cast<size_t>(ks) * T + t) * npad + c];
     const double s = 1.0 / (1.0 + exp(-z));
     sv[q] = s;
+    zv[q] = z;
     key[q] = s + static_cast<double>(bias[c]);
     taken[q] = false;
   }
-  double s_shared = 0.0;
+  double s_shared = 0.0, z_shared = 0.0;
   if (lane < S) {
     double z = 0.0;
     for (int ks = 0; ks < nks; ++ks)
       z += partial[(static_cast<size_t>(ks) * T + t) * npad + E + lane];
     s_shared = 1.0 / (1.0 + exp(-z));
+    z_shared = z;
   }
 
-  double s_sel[K + S];
+  double s_sel[K + S], z_sel[K + S];
   int i_sel[K];
   double k_last = 0.0, k_next = 0.0;
 #pragma unroll
@@ -406,11 +408,15 @@ __global__ __launch_bounds__(256) void router_select(
     } else {
       const int q = bi >> 6;
       const int owner = bi & 63;
-      double my = sv[0];
+      double my = sv[0], mz = zv[0];
       my = q == 1 ? sv[1] : my;
       my = q == 2 ? sv[2] : my;
       my = q == 3 ? sv[3] : my;
+      mz = q == 1 ? zv[1] : mz;
+      mz = q == 2 ? zv[2] : mz;
+      mz = q == 3 ? zv[3] : mz;
       s_sel[r] = __shfl(my, owner);
+      z_sel[r] = __shfl(mz, owner);
       if (lane == owner) {
         taken[0] = taken[0] || q == 0;
         taken[1] = taken[1] || q == 1;
@@ -422,11 +428,35 @@ __global__ __launch_bounds__(256) void router_select(
     }
   }
 #pragma unroll
-  for (int j = 0; j < S; ++j) s_sel[K + j] = __shfl(s_shared, j);
+  for (int j = 0; j < S; ++j) {
+    s_sel[K + j] = __shfl(s_shared, j);
+    z_sel[K + j] = __shfl(z_shared, j);
+  }
 
+  // gates: s_j / sum s, or exp(logsigmoid(z_j) - logsumexp logsigmoid(z)),
+  // both over the k kept and S shared contributors in slot order, then
+  // times gate_scale.  Written as g_j = num_j / denom.
   double denom = 0.0;
+  if (logsumexp_norm) {
 #pragma unroll
-  for (int j = 0; j < K + S; ++j) denom += s_sel[j];
+    for (int j = 0; j < K + S; ++j) {
+      const double z = z_sel[j];  // logsigmoid(z) = min(z, 0) - log1p(exp(-|z|))
+      s_sel[j] = fmin(z, 0.0) - log1p(exp(-fabs(z)));
+    }
+    double m = s_sel[0];
+#pragma unroll
+    for (int j = 1; j < K + S; ++j) m = fmax(m, s_sel[j]);
+#pragma unroll
+    for (int j = 0; j < K + S; ++j) denom += exp(s_sel[j] - m);
+    const double lse = m + log(denom);
+#pragma unroll
+    for (int j = 0; j < K + S; ++j) s_sel[j] = exp(s_sel[j] - lse) * gate_scale;
+    denom = 1.0;
+  } else {
+#pragma unroll
+    for (int j = 0; j < K + S; ++j) denom += s_sel[j];
+    denom /= gate_scale;
+  }
   if (lane < K) {
     int id = i_sel[0];
 #pragma unroll
@@ -469,7 +499,8 @@ hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
   else
     router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, partial);
   router_select<6, 2><<<(s.T + 3) / 4, 256, 0, st>>>(partial, nks, s.T, npad, s.E, bias,
-                                                      topk_idx, gates, margin);
+                                                      topk_idx, gates, margin,
+                                                      s.gate_logsumexp, s.gate_scale);
   return hipGetLastError();
 }
 

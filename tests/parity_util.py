@@ -34,7 +34,8 @@ def npi(t):
 
 
 def desc_for(cfg, T=None):
-    return L.make_desc(cfg.T if T is None else T, cfg.d, cfg.F, synth.act_dtype(cfg))
+    return L.make_desc(cfg.T if T is None else T, cfg.d, cfg.F, synth.act_dtype(cfg),
+                       gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
 
 
 class Buffers:
@@ -86,12 +87,13 @@ def run_forward(desc, inp, gamma, bias=None):
     return b, bias
 
 
-def check_routing(x64, wr64, b64, topk_gpu, gates_gpu, k=6):
+def check_routing(x64, wr64, b64, topk_gpu, gates_gpu, k=6, gate_norm="ratio", gate_scale=1.0):
     """Selection bit-exact outside oracle near-ties; gates to 1e-6 relative
-    (the oracle's gates for the GPU's selection).  Returns (oracle route
-    dict, stats)."""
+    (the oracle's gates for the GPU's selection, in the given normalisation).
+    Returns (oracle route dict, gates, stats)."""
     t0 = time.time()
-    r = O.route(x64, wr64, b64, n_routed=len(b64), k=k)
+    r = O.route(x64, wr64, b64, n_routed=len(b64), k=k, gate_norm=gate_norm,
+                gate_scale=gate_scale)
     n_total = wr64.shape[0]
     exempt = r["margin"] < TIE_MARGIN
     mism = np.any(topk_gpu != r["topk_idx"], axis=1)
@@ -101,7 +103,11 @@ def check_routing(x64, wr64, b64, topk_gpu, gates_gpu, k=6):
     # GPU picks are always a valid top-k set: distinct routed ids
     srt = np.sort(topk_gpu, axis=1)
     assert np.all(srt[:, 1:] != srt[:, :-1]) and topk_gpu.min() >= 0 and topk_gpu.max() < len(b64)
-    g_ref, _ = O.joint_gates(r["s"], topk_gpu, list(range(len(b64), n_total)))
+    shared = list(range(len(b64), n_total))
+    if gate_norm == "ratio":
+        g_ref, _ = O.joint_gates(r["s"], topk_gpu, shared, gate_scale)
+    else:
+        g_ref, _ = O.joint_gates_logsumexp(r["z"], topk_gpu, shared, gate_scale)
     rel = np.abs(gates_gpu - g_ref) / g_ref
     stats = {"exempt": int(exempt.sum()), "exempt_differ": int((mism & exempt).sum()),
              "gate_max_rel": float(rel.max()) if rel.size else 0.0,

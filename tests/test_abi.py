@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lib.moe_abi_version() == 1
+    assert lib.moe_abi_version() == 2
     for code in range(7):
         s = lib.moe_status_string(code)
         assert s and isinstance(s, bytes)
@@ -37,7 +37,8 @@ def test_version_and_status_strings():
 
 
 def desc(**kw):
-    base = dict(T=128, d=512, F=128, E=256, S=2, k=6, act=L.F32, weight=L.F32)
+    base = dict(T=128, d=512, F=128, E=256, S=2, k=6, act=L.F32, weight=L.F32,
+                gate_norm=L.GATE_RATIO, gate_scale=1.0)
     base.update(kw)
     return L.Desc(**base)
 
@@ -55,6 +56,10 @@ def ws_size(d, call):
     (dict(E=128), 5), (dict(S=1), 5), (dict(k=8), 5),
     (dict(d=384), 5), (dict(F=96), 5),
     (dict(T=1 << 29), 5),
+    (dict(gate_norm=2), 2), (dict(gate_norm=-1), 2), (dict(gate_scale=0.0), 2),
+    (dict(gate_scale=-8.0), 2), (dict(gate_scale=float("inf")), 2),
+    (dict(gate_scale=float("nan")), 2),
+    (dict(gate_norm=L.GATE_LOGSUMEXP, gate_scale=6.5), 0),
 ])
 def test_desc_validation(kw, code):
     st, _ = ws_size(desc(**kw), L.CALL_FORWARD)

@@ -135,6 +135,51 @@ def test_gate_invariants_and_contributor_count():
         assert list(r["idx"][t, 6:]) == [256, 257]
 
 
+def test_logsigmoid_against_library_and_closed_forms():
+    z = np.concatenate([np.linspace(-800, 800, 4001), [-1e-300, 0.0, 1e-300]])
+    np.testing.assert_allclose(O.logsigmoid(z), log_expit(z), rtol=1e-15, atol=1e-300)
+    assert O.logsigmoid(0.0) == pytest.approx(-np.log(2.0), rel=1e-16)
+    # far left: log sigmoid(z) = z - log1p(exp(z)) -> z; far right: -exp(-z)
+    assert O.logsigmoid(-700.0) == -700.0
+    assert O.logsigmoid(40.0) == pytest.approx(-np.exp(-40.0), rel=1e-15)
+
+
+def test_logsumexp_gates_against_ratio_and_scale():
+    # the two normalisations agree in exact arithmetic; the scale multiplies
+    x, w, b = _rand_router(seed=7)
+    r = O.route(x, w, b)
+    shared = [256, 257]
+    g_ratio, idx = O.joint_gates(r["s"], r["topk_idx"], shared)
+    g_lse, idx2 = O.joint_gates_logsumexp(r["z"], r["topk_idx"], shared)
+    assert np.array_equal(idx, idx2)
+    np.testing.assert_allclose(g_lse, g_ratio, rtol=1e-13, atol=0)
+    np.testing.assert_allclose(g_lse.sum(axis=1), 1.0, rtol=0, atol=1e-14)
+    g_lse8, _ = O.joint_gates_logsumexp(r["z"], r["topk_idx"], shared, scale=6.5)
+    np.testing.assert_allclose(g_lse8, 6.5 * g_lse, rtol=1e-15, atol=0)
+    g_ratio8, _ = O.joint_gates(r["s"], r["topk_idx"], shared, scale=6.5)
+    np.testing.assert_allclose(g_ratio8, 6.5 * g_ratio, rtol=1e-15, atol=0)
+    # route() picks the form; the selection is the same
+    r2 = O.route(x, w, b, gate_norm="logsumexp", gate_scale=6.5)
+    assert np.array_equal(r2["topk_idx"], r["topk_idx"])
+    np.testing.assert_allclose(r2["gates"], g_lse8, rtol=0, atol=0)
+    with pytest.raises(ValueError):
+        O.route(x, w, b, gate_norm="softmax")
+
+
+def test_logsumexp_gates_hand_example():
+    # one token, 2 routed of 3 plus one shared expert: z = [0, ln 3, -ln 3 | 0]
+    # keeps experts 1 and 0 (s = 3/4, 1/2), shared s = 1/2; sum = 7/4
+    z = np.array([[0.0, np.log(3.0), -np.log(3.0), 0.0]])
+    top = np.array([[1, 0]])
+    g, idx = O.joint_gates_logsumexp(z, top, [3], scale=8.0)
+    assert list(idx[0]) == [1, 0, 3]
+    np.testing.assert_allclose(g[0], 8.0 * np.array([3 / 7, 2 / 7, 2 / 7]), rtol=1e-15)
+    # extreme logits stay finite (log domain)
+    zx = np.array([[-900.0, 900.0, 0.0, -900.0]])
+    gx, _ = O.joint_gates_logsumexp(zx, np.array([[1, 2]]), [3])
+    assert np.all(np.isfinite(gx)) and gx[0, 0] == pytest.approx(2.0 / 3.0, rel=1e-15)
+
+
 def test_gates_match_log_domain_normalisation():
     # Hugging Face write-up: log-sigmoid -> logsumexp over the joint set of 8
     # equals the ratio of sigmoids (before its extra route scaling).

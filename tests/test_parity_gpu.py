@@ -29,8 +29,13 @@ SMALL = {
     "bf16_small": MoEConfig("bf16_small", T=300, d=512, F=256, act="bf16", bias_range=0.05),
     "bf16_tall": MoEConfig("bf16_tall", T=1500, d=256, F=128, act="bf16", bias_range=0.05),
     "bf16_one": MoEConfig("bf16_one", T=1, d=768, F=384, act="bf16", bias_range=0.05),
-    # >= 48 rows per routed expert on average: the 128-row tile path
+    # >= 48 rows per routed expert on average: the 256-row tile path
     "bf16_mt128": MoEConfig("bf16_mt128", T=2200, d=512, F=256, act="bf16", bias_range=0.05),
+    # gates by logsumexp over log-sigmoids, scaled ("Under The Hood: Inkling")
+    "bf16_lse": MoEConfig("bf16_lse", T=300, d=512, F=256, act="bf16", bias_range=0.05,
+                          gate_norm="logsumexp", gate_scale=6.5),
+    "bf16_lse_big": MoEConfig("bf16_lse_big", T=2500, d=768, F=384, act="bf16",
+                              bias_range=0.05, gate_norm="logsumexp", gate_scale=6.5),
 }
 
 
@@ -52,7 +57,8 @@ def test_full_parity_stagewise(name):
 
     x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
     topk = npi(b.topk)
-    r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates))
+    r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates),
+                                 gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
     log(f"  routing {st}")
     dp = check_dispatch(topk, b)
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
@@ -122,7 +128,7 @@ def sample_tokens(T, n, seed=0):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,nsample", [("B", 48), ("C", 12), ("D", 6)])
+@pytest.mark.parametrize("name,nsample", [("B", 48), ("C", 12), ("D", 6), ("I", 4)])
 def test_workload_parity(name, nsample):
     cfg = configs.get(name)
     log(f"[workload parity] {name}: {cfg.describe()}")
@@ -131,7 +137,8 @@ def test_workload_parity(name, nsample):
     b, bias_new = run_forward(desc, inp, cfg.gamma)
     x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
     topk = npi(b.topk)
-    r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates))
+    r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates),
+                                 gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
     log(f"  routing {st}")
     check_dispatch(topk, b)
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
