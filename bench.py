@@ -10,7 +10,8 @@ combine, bias update) over one batch already resident in HBM:
 * decode workload (reported alongside): the same layer at T=64;
 * skewed workload (reported alongside): the headline shape with a skewed
   router, 100 consecutive batches (fresh tokens each) and the balancing
-  bias updating after every batch;
+  bias updating after every batch; again with a hard per-expert capacity
+  of 1.25x the ideal load (drop rate per batch);
 * native-shape workload (reported alongside): hidden 6144, expert width
   3072, gates by logsumexp over log-sigmoids times a route scale, at the
   headline batch size.
@@ -45,6 +46,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--skewed-workload", default="E")
     ap.add_argument("--skewed-steps", type=int, default=100)
+    ap.add_argument("--capacity-workload", default="Ecap")
     ap.add_argument("--no-skewed", action="store_true")
     ap.add_argument("--native-workload", default="I")
     ap.add_argument("--no-native", action="store_true")
@@ -181,7 +183,12 @@ def time_skewed(cfg, steps, torch, L, synth):
     bias = inp["bias"].clone()
     routing = {"counts": counts}
     mean_load = cfg.T * cfg.k / cfg.E
-    ms, maxmean = [], []
+    cap = None
+    if cfg.capacity_factor > 0:     # rows an expert keeps: ceil(cf * k*T / E)
+        import math
+        import numpy as np
+        cap = math.ceil(float(np.float32(cfg.capacity_factor)) * float(cfg.k * cfg.T) / cfg.E)
+    ms, maxmean, dropped = [], [], []
     for s in range(steps + 1):          # batch 0 also warms up
         x = synth.make_x(cfg, device="cuda", step=s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -192,13 +199,16 @@ def time_skewed(cfg, steps, torch, L, synth):
         if s > 0:
             ms.append(e0.elapsed_time(e1))
         maxmean.append(counts.max().item() / mean_load)
+        if cap is not None:
+            dropped.append((counts - cap).clamp(min=0).sum().item() / (cfg.k * cfg.T))
     f_gu, f_dn = expert_flops(cfg)
     med = statistics.median(ms)
     del inp, w, ws, y
     torch.cuda.empty_cache()
     return {"workload": f"skewed MoE layer, {cfg.describe()}, router offset kappa="
                         f"{cfg.skew_kappa}, {steps} consecutive batches, bias step "
-                        f"{cfg.gamma}",
+                        f"{cfg.gamma}" + (f", capacity {cfg.capacity_factor} x ideal load"
+                                          if cap is not None else ", dropless"),
             "ms_per_step_median": round(med, 4),
             "ms_per_step_p10_p90": [round(sorted(ms)[len(ms) // 10], 4),
                                     round(sorted(ms)[(9 * len(ms)) // 10], 4)],
@@ -207,7 +217,13 @@ def time_skewed(cfg, steps, torch, L, synth):
             "max_over_mean_load": {"first": round(maxmean[0], 3),
                                    "middle": round(maxmean[len(maxmean) // 2], 3),
                                    "last": round(maxmean[-1], 3)},
-            "bias_range": [round(bias.min().item(), 5), round(bias.max().item(), 5)]}
+            "bias_range": [round(bias.min().item(), 5), round(bias.max().item(), 5)],
+            **({"capacity_rows": cap,
+                "drop_rate": {"first": round(dropped[0], 4),
+                              "middle": round(dropped[len(dropped) // 2], 4),
+                              "last": round(dropped[-1], 4),
+                              "mean": round(sum(dropped) / len(dropped), 4)}}
+               if cap is not None else {})}
 
 
 def decode_bytes(cfg, counts):
@@ -345,6 +361,8 @@ def main():
     if not args.no_skewed:
         result["skewed"] = time_skewed(configs.get(args.skewed_workload), args.skewed_steps,
                                        torch, L, synth)
+        result["capacity"] = time_skewed(configs.get(args.capacity_workload),
+                                         args.skewed_steps, torch, L, synth)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch)
     print(json.dumps(result), flush=True)

@@ -44,16 +44,29 @@
  *                            s + b, exact ties to the lower id).
  * - gates     fp32  [T, k+S] slots 0..k-1 the routed experts in rank order,
  *                            slots k..k+S-1 the shared experts.
- * - counts    int32 [E]      L_e, routed selections per expert.
- * - offsets   int32 [E+1]    exclusive prefix sum of counts.
- * - sorted_pair int32 [T*k]  pair numbers grouped by expert, ascending p
- *                            inside each expert (a stable permutation).
- * - pair_pos  int32 [T*k]    inverse permutation: pair p sits at row
- *                            pair_pos[p] of the expert-sorted buffers.
+ * - counts    int32 [E]      L_e, routed selections per expert (the demand,
+ *                            before any capacity limit).
+ * - offsets   int32 [E+1]    exclusive prefix sum of the kept rows per
+ *                            expert, min(L_e, C) (C below; L_e when there is
+ *                            no capacity limit).
+ * - sorted_pair int32 [T*k]  the kept pair numbers grouped by expert,
+ *                            ascending p inside each expert; entries from
+ *                            offsets[E] on are unspecified.
+ * - pair_pos  int32 [T*k]    pair p sits at row pair_pos[p] of the
+ *                            expert-sorted buffers, or -1 if it was dropped.
  * - h         act   [(k+S)*T, F]  SwiGLU activations: rows 0..T*k-1 routed
  *                            in sorted order, row k*T + s*T + t shared s.
  * - y_routed  act   [T*k, d] expert outputs in sorted order;
  *   y_shared  act   [S, T, d] shared-expert outputs.
+ *
+ * Capacity ("Inkling, Dissected" 02d: an expert processes at most a fixed
+ * number of tokens per batch; the overflow is dropped and the layer output
+ * is computed from the remaining contributions).  With capacity_factor
+ * cf > 0 each routed expert keeps C = ceil(cf * k * T / E) pairs (the
+ * product and quotient taken in double precision), the first C in
+ * ascending pair number, i.e. ascending token; a dropped pair contributes
+ * nothing to y (the other gates are not renormalised).  Shared experts have
+ * no limit.  cf = 0 means no limit (dropless).
  */
 #ifndef MOE_H
 #define MOE_H
@@ -110,12 +123,13 @@ typedef enum { MOE_GATE_RATIO = 0, MOE_GATE_LOGSUMEXP = 1 } moe_gate_norm;
  * S shared experts, k routed experts per token; act is the dtype of x, h,
  * y and the expert weights, weight must equal act.  The router weights and
  * the bias are always fp32.  gate_norm and gate_scale (finite, > 0) set the
- * gate normalisation above. */
+ * gate normalisation above; capacity_factor the per-expert capacity. */
 typedef struct {
   int32_t T, d, F, E, S, k;
   moe_dtype act, weight;
   int32_t gate_norm;  /* moe_gate_norm */
   float gate_scale;
+  float capacity_factor;  /* 0: no limit; else > 0 and finite (see above) */
 } moe_desc;
 
 /* Weights of one layer.  Expert matrices are [out, in] row-major:
@@ -170,7 +184,8 @@ moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router
 
 /* Dispatch: group the T*k (token, slot) pairs by expert ("Inkling,
  * Dissected" 02: each token visits its 6 chosen experts; 02e: L_e is the
- * number of tokens that selected e).  Histogram -> exclusive scan ->
+ * number of tokens that selected e), keeping at most C pairs per expert
+ * when the descriptor sets a capacity.  Histogram -> exclusive scan ->
  * stable scatter; deterministic.  Writes counts, offsets, sorted_pair and
  * pair_pos (layouts above). */
 moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx,
@@ -221,8 +236,9 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x,
 
 /* Combine ("Inkling, Dissected" 02b: the gate-weighted sum over the 8
  * contributors).  y[t] = sum_j gates[t,j] * y_routed[pair_pos[t*k+j]]
- * (j = 0..k-1 in rank order) + sum_s gates[t,k+s] * y_shared[s,t], in fp32
- * in exactly that order, rounded once to act.  Writes y [T, d]. */
+ * (j = 0..k-1 in rank order, skipping dropped pairs, pair_pos < 0) +
+ * sum_s gates[t,k+s] * y_shared[s,t], in fp32 in exactly that order,
+ * rounded once to act.  Writes y [T, d]. */
 moe_status moe_combine(const moe_desc* desc, const void* y_routed,
                        const void* y_shared, const float* gates,
                        const int32_t* pair_pos, void* y, hipStream_t stream);

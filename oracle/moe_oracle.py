@@ -168,24 +168,61 @@ def route(x, w_router, bias, n_routed=256, k=6, gate_norm="ratio", gate_scale=1.
             "gates": gates, "idx": idx}
 
 
-def dispatch(topk_idx, n_routed=256):
+def capacity(capacity_factor, k, T, n_routed):
+    """Pairs an expert keeps per batch ("Inkling, Dissected", 02d: a hard
+    capacity per expert; the lab of 02g sets it at 1.25x the ideal load):
+    C = ceil(cf * k*T / E), with cf taken as the float32 the descriptor
+    holds and the product and quotient in float64.  None (no limit) for
+    cf = 0.
+    """
+    cf = float(np.float32(capacity_factor))
+    if cf == 0.0:
+        return None
+    return int(np.ceil(cf * float(k * T) / float(n_routed)))
+
+
+def dispatch(topk_idx, n_routed=256, cap=None):
     """Expert-contiguous grouping of the (token, slot) pairs.
 
     A pair is numbered p = t*k + j (token t, slot j).  Returns
-    ``counts`` [n_routed] (the loads L_i), ``offsets`` [n_routed+1]
-    (exclusive prefix sum of counts), ``sorted_pair`` [T*k] (pair numbers
-    grouped by expert; within one expert in ascending p, hence ascending
-    token) and ``pair_pos`` [T*k], the inverse permutation.
+    ``counts`` [n_routed] (the loads L_i, the demand), ``kept``
+    [n_routed] (min(L_i, cap)), ``offsets`` [n_routed+1] (exclusive prefix
+    sum of kept), ``sorted_pair`` [sum kept] (the kept pair numbers grouped
+    by expert; within one expert in ascending p, hence ascending token) and
+    ``pair_pos`` [T*k], each pair's row in that order or -1 when the pair
+    was dropped ("Inkling, Dissected", 02d: overflow beyond an expert's
+    capacity is dropped).  Without ``cap`` nothing is dropped and pair_pos
+    is the inverse permutation.  Which pairs overflow is this module's
+    reading: an expert keeps its first ``cap`` pairs in ascending token
+    order.
     """
     flat = np.asarray(topk_idx, dtype=np.int64).ravel()
     counts = np.bincount(flat, minlength=n_routed)
-    offsets = np.concatenate([[0], np.cumsum(counts)])
-    sorted_pair = np.argsort(flat, kind="stable")
-    pair_pos = np.empty_like(sorted_pair)
-    pair_pos[sorted_pair] = np.arange(flat.size)
-    return {"counts": counts.astype(np.int64), "offsets": offsets.astype(np.int64),
+    order = np.argsort(flat, kind="stable")          # grouped, ascending p
+    start = np.concatenate([[0], np.cumsum(counts)])
+    rank = np.empty_like(order)
+    rank[order] = np.arange(flat.size) - start[flat[order]]   # rank inside its expert
+    kept = counts if cap is None else np.minimum(counts, cap)
+    offsets = np.concatenate([[0], np.cumsum(kept)])
+    keep = rank < (kept[flat])
+    sorted_pair = order[keep[order]]
+    pair_pos = np.full(flat.size, -1, dtype=np.int64)
+    pair_pos[keep] = offsets[flat[keep]] + rank[keep]
+    return {"counts": counts.astype(np.int64), "kept": kept.astype(np.int64),
+            "offsets": offsets.astype(np.int64),
             "sorted_pair": sorted_pair.astype(np.int64),
             "pair_pos": pair_pos.astype(np.int64)}
+
+
+def load_metrics(counts, kept, k, T):
+    """Router Balance Lab measures ("Inkling, Dissected", 02g): MaxVio, the
+    hottest expert's demand over the ideal load k*T/E, minus 1; and the drop
+    rate, the fraction of the k*T expert slots dropped at capacity."""
+    counts = np.asarray(counts, dtype=np.int64)
+    E = counts.size
+    max_vio = float(counts.max()) * E / (k * T) - 1.0
+    drop_rate = float(k * T - np.asarray(kept).sum()) / (k * T)
+    return {"max_vio": max_vio, "drop_rate": drop_rate}
 
 
 def silu(u):
@@ -213,8 +250,8 @@ def expert_ffn(x, weights, offsets, sorted_pair, k=6):
 
     ``weights`` maps ``w_gate``, ``w_up`` [E, F, d], ``w_down`` [E, d, F] and
     ``ws_gate``, ``ws_up``, ``ws_down`` (same with leading S) to arrays.
-    Returns ``y_routed`` [T*k, d] in sorted-pair order and ``y_shared``
-    [S, T, d].
+    Returns ``y_routed`` [T*k, d] in sorted-pair order (rows past the kept
+    pairs stay zero) and ``y_shared`` [S, T, d].
     """
     x = _f64(x)
     T, d = x.shape
@@ -240,14 +277,18 @@ def combine(y_routed, y_shared, gates, pair_pos, k=6):
     """y_t = sum_j g[t,j] Y[pair_pos[t*k+j]] + sum_s g[t,k+s] Y_s[s,t].
 
     Routed slots in rank order, then the shared experts in id order (02b:
-    the gate-weighted sum over the 8 contributors).
+    the gate-weighted sum over the 8 contributors).  A slot dropped at its
+    expert's capacity (pair_pos -1, 02d) contributes nothing; the other
+    gates keep their values.
     """
     gates = _f64(gates)
     T = gates.shape[0]
     pp = np.asarray(pair_pos).reshape(T, k)
     y = np.zeros((T, np.shape(y_routed)[1]))
+    yr = _f64(y_routed)
     for j in range(k):
-        y = y + gates[:, j:j + 1] * _f64(y_routed)[pp[:, j]]
+        live = pp[:, j] >= 0          # dropped pairs (pair_pos -1) add nothing
+        y[live] = y[live] + gates[live, j:j + 1] * yr[pp[live, j]]
     for s in range(len(y_shared)):
         y = y + gates[:, k + s:k + s + 1] * _f64(y_shared[s])
     return y
@@ -267,17 +308,19 @@ def bias_update(counts, gamma, bias, T, k=6):
     return (b + np.float32(gamma) * sgn).astype(np.float32)
 
 
-def moe_forward(x, w_router, weights, bias, gamma, k=6):
+def moe_forward(x, w_router, weights, bias, gamma, k=6, gate_norm="ratio", gate_scale=1.0,
+                capacity_factor=0.0):
     """The whole layer for one batch, followed by the bias update.
 
     Returns the router dict, the dispatch dict, ``y_routed``, ``y_shared``,
-    ``y`` [T, d] and the next bias ``bias_next`` (float32).
+    ``y`` [T, d] and the next bias ``bias_next`` (float32).  The bias
+    update counts the demand (every selection), dropped or not.
     """
     x = _f64(x)
     T = x.shape[0]
     E = np.shape(bias)[0]
-    r = route(x, w_router, bias, n_routed=E, k=k)
-    dp = dispatch(r["topk_idx"], n_routed=E)
+    r = route(x, w_router, bias, n_routed=E, k=k, gate_norm=gate_norm, gate_scale=gate_scale)
+    dp = dispatch(r["topk_idx"], n_routed=E, cap=capacity(capacity_factor, k, T, E))
     y_routed, y_shared = expert_ffn(x, weights, dp["offsets"], dp["sorted_pair"], k)
     y = combine(y_routed, y_shared, r["gates"], dp["pair_pos"], k)
     b_next = bias_update(dp["counts"], gamma, bias, T, k)
@@ -306,14 +349,15 @@ def moe_layer_per_token(x_t, experts, w_router, bias, k=6):
 
 
 def output_rows(tokens, x, topk_idx, gates, expert_weights, k=6, n_routed=256,
-                n_shared=2):
+                n_shared=2, pair_pos=None):
     """y_t for a few tokens, given their routing (for large workloads).
 
     ``expert_weights(e)`` returns (w_gate, w_up, w_down) of expert e (shared
     experts are ids n_routed..n_routed+n_shared-1).  Experts are visited in id
     order and each expert's weights are fetched once, so the cost is one
     weight conversion per distinct expert.  Contributions are added per
-    token in slot order, as ``combine`` does.
+    token in slot order, as ``combine`` does; with ``pair_pos`` given, routed
+    slots dropped at capacity (-1) are left out.
     """
     tokens = list(tokens)
     x = _f64(x)
@@ -322,6 +366,8 @@ def output_rows(tokens, x, topk_idx, gates, expert_weights, k=6, n_routed=256,
     need = {}
     for t in tokens:
         for j, e in enumerate(list(topk_idx[t]) + list(range(n_routed, n_routed + n_shared))):
+            if j < k and pair_pos is not None and pair_pos[t * k + j] < 0:
+                continue
             need.setdefault(int(e), []).append((t, j))
     contrib = {}
     for e in sorted(need):
@@ -333,5 +379,6 @@ def output_rows(tokens, x, topk_idx, gates, expert_weights, k=6, n_routed=256,
     out = np.zeros((len(tokens), x.shape[1]))
     for n, t in enumerate(tokens):
         for j in range(k + n_shared):
-            out[n] = out[n] + gates[t, j] * contrib[(t, j)]
+            if (t, j) in contrib:
+                out[n] = out[n] + gates[t, j] * contrib[(t, j)]
     return out

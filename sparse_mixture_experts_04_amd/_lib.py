@@ -37,7 +37,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("F", ctypes.c_int32),
                 ("E", ctypes.c_int32), ("S", ctypes.c_int32), ("k", ctypes.c_int32),
                 ("act", ctypes.c_int), ("weight", ctypes.c_int),
-                ("gate_norm", ctypes.c_int32), ("gate_scale", ctypes.c_float)]
+                ("gate_norm", ctypes.c_int32), ("gate_scale", ctypes.c_float),
+                ("capacity_factor", ctypes.c_float)]
 
 
 class Weights(ctypes.Structure):
@@ -100,10 +101,11 @@ def act_code(dtype):
 GATE_RATIO, GATE_LOGSUMEXP = 0, 1
 
 
-def make_desc(T, d, F, act_dtype, E=256, S=2, k=6, gate_norm="ratio", gate_scale=1.0):
+def make_desc(T, d, F, act_dtype, E=256, S=2, k=6, gate_norm="ratio", gate_scale=1.0,
+              capacity_factor=0.0):
     a = act_code(act_dtype)
     norm = {"ratio": GATE_RATIO, "logsumexp": GATE_LOGSUMEXP}[gate_norm]
-    return Desc(T, d, F, E, S, k, a, a, norm, gate_scale)
+    return Desc(T, d, F, E, S, k, a, a, norm, gate_scale, capacity_factor)
 
 
 def _act(desc):

@@ -10,6 +10,8 @@ stand-ins chosen to exercise the regimes that matter on one GPU:
 * ``C``  decode-sized: 64 tokens, bound by streaming expert weights;
 * ``D``  large batch: 16384 tokens at hidden 7168, bound by matrix cores;
 * ``E``  shape of ``D`` with a skewed router, run for 100 bias-update steps;
+* ``Ecap`` ``E`` with a hard capacity of 1.25x the ideal load per expert
+  (the Router Balance Lab's setting in "Inkling, Dissected" 02g);
 * ``I``  the configuration of "Under The Hood: Inkling" (hidden 6144, expert
   width 3072, gates normalised by logsumexp over log-sigmoids and scaled by
   route_scale = 8 times a global scale; the learned global scale is stood in
@@ -38,6 +40,7 @@ class MoEConfig:
     steps: int = 1         # bias-update steps the workload runs
     gate_norm: str = "ratio"   # "ratio" or "logsumexp"
     gate_scale: float = 1.0    # multiplier of every gate
+    capacity_factor: float = 0.0   # per-expert capacity in units of the ideal load (0: none)
     extra: dict = field(default_factory=dict)
 
     @property
@@ -59,6 +62,8 @@ CONFIGS = {
                    skew_kappa=8.0, steps=100),
     "I": MoEConfig("I", T=16384, d=6144, F=3072, act="bf16", bias_range=0.05,
                    gate_norm="logsumexp", gate_scale=8.0 * 0.8125),
+    "Ecap": MoEConfig("Ecap", T=16384, d=7168, F=2048, act="bf16", bias_range=0.0,
+                      skew_kappa=8.0, steps=100, capacity_factor=1.25),
 }
 
 

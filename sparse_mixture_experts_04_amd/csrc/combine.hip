@@ -2,7 +2,8 @@
 //
 // "Inkling, Dissected", 02 and 02b: the layer output is the gate-weighted
 // sum of the 6 chosen routed experts' outputs and the 2 shared experts'
-// outputs.  Each output element is summed in fp32 in a fixed order
+// outputs; a pair dropped at its expert's capacity (pair_pos < 0, 02d)
+// contributes nothing.  Each output element is summed in fp32 in a fixed order
 // (routed slots in rank order, then the shared experts), from rows found
 // through pair_pos, with no atomics: the result is deterministic.
 #include "common.h"
@@ -60,8 +61,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yr,
 #pragma unroll
   for (int j = 0; j < K; ++j) {
     const float g = gates[static_cast<size_t>(t) * (K + S) + j];
-    const size_t row = static_cast<size_t>(pair_pos[static_cast<size_t>(t) * K + j]);
-    Vec<T>::load(yr + row * d + c0, v);
+    const int pos = pair_pos[static_cast<size_t>(t) * K + j];
+    if (pos < 0) continue;  // dropped at the expert's capacity
+    Vec<T>::load(yr + static_cast<size_t>(pos) * d + c0, v);
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
   }

@@ -42,6 +42,7 @@ struct Shape {
   bool bf16;
   bool gate_logsumexp = false;  // gate normalisation (router only)
   float gate_scale = 1.0f;
+  int capacity = 0x7fffffff;     // pairs kept per routed expert
 };
 
 // Router columns are padded to a multiple of the router's column tile.

@@ -10,13 +10,16 @@
 //   1. dispatch_count   one block per segment of kDispatchSeg pairs counts
 //                       its pairs per expert in LDS;
 //   2. dispatch_scan    one block turns the segment counts into the loads,
-//                       the expert offsets and each segment's base per expert;
+//                       the offsets of the kept rows and each segment's
+//                       running count per expert;
 //   3. dispatch_scatter one wave per segment walks its pairs in order, 64 at a
 //                       time; lanes holding the same expert find each other
 //                       with 8 ballots (one per id bit), so a pair's rank is
-//                       its segment base + earlier pairs of that expert.
+//                       its segment's running count + earlier pairs of that
+//                       expert.
 // Within an expert the pairs therefore come out in ascending pair number,
-// i.e. ascending token.
+// i.e. ascending token.  Capacity ("Inkling, Dissected" 02d): a pair whose
+// rank reaches the expert's capacity is dropped (pair_pos = -1).
 #include "common.h"
 
 namespace moe {
@@ -40,9 +43,13 @@ __global__ __launch_bounds__(256) void dispatch_count(const int32_t* __restrict_
     seg_counts[static_cast<size_t>(blockIdx.x) * E + e] = hist[e];
 }
 
-// One block of 256 threads, thread e owns expert e (E <= 256).
+// One block of 256 threads, thread e owns expert e (E <= 256).  Turns the
+// segment counts into each segment's running count of expert e's earlier
+// pairs, writes the demand counts and the offsets of the kept rows
+// (min(count, capacity) per expert).
 __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ seg_counts, int nseg,
-                                                     int E, int32_t* __restrict__ counts,
+                                                     int E, int capacity,
+                                                     int32_t* __restrict__ counts,
                                                      int32_t* __restrict__ offsets) {
   __shared__ int sc[256];
   const int e = threadIdx.x;
@@ -55,7 +62,8 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ seg_c
       tot += c;
     }
   }
-  sc[e] = tot;
+  const int kept = tot < capacity ? tot : capacity;
+  sc[e] = kept;
   __syncthreads();
   for (int off = 1; off < 256; off <<= 1) {
     const int v = e >= off ? sc[e - off] : 0;
@@ -63,23 +71,26 @@ __global__ __launch_bounds__(256) void dispatch_scan(int32_t* __restrict__ seg_c
     sc[e] += v;
     __syncthreads();
   }
-  const int excl = sc[e] - tot;
   if (e < E) {
     counts[e] = tot;
-    offsets[e] = excl;
-    for (int s = 0; s < nseg; ++s) seg_counts[static_cast<size_t>(s) * E + e] += excl;
+    offsets[e] = sc[e] - kept;
   }
   if (e == E - 1) offsets[E] = sc[e];
 }
 
 __global__ __launch_bounds__(64) void dispatch_scatter(const int32_t* __restrict__ topk,
-                                                       long long npairs, int E,
+                                                       long long npairs, int E, int capacity,
                                                        const int32_t* __restrict__ seg_base,
+                                                       const int32_t* __restrict__ offsets,
                                                        int32_t* __restrict__ sorted_pair,
                                                        int32_t* __restrict__ pair_pos) {
   __shared__ int run[256];
+  __shared__ int off[256];
   const int lane = threadIdx.x;
-  for (int e = lane; e < E; e += 64) run[e] = seg_base[static_cast<size_t>(blockIdx.x) * E + e];
+  for (int e = lane; e < E; e += 64) {
+    run[e] = seg_base[static_cast<size_t>(blockIdx.x) * E + e];
+    off[e] = offsets[e];
+  }
   __syncthreads();
   const long long base = static_cast<long long>(blockIdx.x) * kDispatchSeg;
   for (int c = 0; c < kDispatchSeg; c += 64) {
@@ -96,10 +107,15 @@ __global__ __launch_bounds__(64) void dispatch_scatter(const int32_t* __restrict
     }
     int cnt = 0;
     if (valid) {
-      const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-      const int pos = run[e] + rank;
-      sorted_pair[pos] = static_cast<int32_t>(p);
-      pair_pos[p] = pos;
+      // rank of this pair among expert e's pairs (ascending p)
+      const int r = run[e] + __popcll(peers & ((1ull << lane) - 1ull));
+      if (r < capacity) {
+        const int pos = off[e] + r;
+        sorted_pair[pos] = static_cast<int32_t>(p);
+        pair_pos[p] = pos;
+      } else {
+        pair_pos[p] = -1;
+      }
       cnt = __popcll(peers);
     }
     __syncthreads();
@@ -115,10 +131,10 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* cou
   const long long npairs = static_cast<long long>(s.T) * s.k;
   const int nseg = dispatch_segments(s);
   if (nseg > 0) dispatch_count<<<nseg, 256, 0, st>>>(topk_idx, npairs, s.E, seg_counts);
-  dispatch_scan<<<1, 256, 0, st>>>(seg_counts, nseg, s.E, counts, offsets);
+  dispatch_scan<<<1, 256, 0, st>>>(seg_counts, nseg, s.E, s.capacity, counts, offsets);
   if (nseg > 0)
-    dispatch_scatter<<<nseg, 64, 0, st>>>(topk_idx, npairs, s.E, seg_counts, sorted_pair,
-                                          pair_pos);
+    dispatch_scatter<<<nseg, 64, 0, st>>>(topk_idx, npairs, s.E, s.capacity, seg_counts,
+                                          offsets, sorted_pair, pair_pos);
   return hipGetLastError();
 }
 

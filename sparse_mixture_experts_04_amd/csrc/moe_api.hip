@@ -22,6 +22,7 @@ moe_status check_desc(const moe_desc* d) {
   if ((d->act != MOE_F32 && d->act != MOE_BF16) || d->weight != d->act) return MOE_ERR_DTYPE;
   if (d->gate_norm != MOE_GATE_RATIO && d->gate_norm != MOE_GATE_LOGSUMEXP) return MOE_ERR_SHAPE;
   if (!(d->gate_scale > 0.0f) || !(d->gate_scale < INFINITY)) return MOE_ERR_SHAPE;
+  if (!(d->capacity_factor >= 0.0f) || !(d->capacity_factor < INFINITY)) return MOE_ERR_SHAPE;
   if (d->E != 256 || d->S != 2 || d->k != 6) return MOE_ERR_UNSUPPORTED;
   if (d->d % 256 != 0 || d->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
   const long long T = d->T;
@@ -42,6 +43,13 @@ Shape to_shape(const moe_desc* d) {
   s.bf16 = d->act == MOE_BF16;
   s.gate_logsumexp = d->gate_norm == MOE_GATE_LOGSUMEXP;
   s.gate_scale = d->gate_scale;
+  s.capacity = INT32_MAX;
+  if (d->capacity_factor > 0.0f) {
+    const double c = std::ceil(static_cast<double>(d->capacity_factor) *
+                               static_cast<double>(static_cast<long long>(d->k) * d->T) /
+                               static_cast<double>(d->E));
+    s.capacity = c < static_cast<double>(INT32_MAX) ? static_cast<int>(c) : INT32_MAX;
+  }
   return s;
 }
 

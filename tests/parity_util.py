@@ -35,7 +35,8 @@ def npi(t):
 
 def desc_for(cfg, T=None):
     return L.make_desc(cfg.T if T is None else T, cfg.d, cfg.F, synth.act_dtype(cfg),
-                       gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
+                       gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale,
+                       capacity_factor=cfg.capacity_factor)
 
 
 class Buffers:
@@ -116,13 +117,18 @@ def check_routing(x64, wr64, b64, topk_gpu, gates_gpu, k=6, gate_norm="ratio", g
     return r, g_ref, stats
 
 
-def check_dispatch(topk_gpu, b, E=256):
-    dp = O.dispatch(topk_gpu, n_routed=E)
+def check_dispatch(topk_gpu, b, E=256, cap=None):
+    dp = O.dispatch(topk_gpu, n_routed=E, cap=cap)
     assert np.array_equal(npi(b.counts), dp["counts"])
     assert np.array_equal(npi(b.offsets), dp["offsets"])
-    assert np.array_equal(npi(b.sorted_pair), dp["sorted_pair"])
+    n_kept = int(dp["offsets"][-1])
+    assert np.array_equal(npi(b.sorted_pair)[:n_kept], dp["sorted_pair"])
     assert np.array_equal(npi(b.pair_pos), dp["pair_pos"])
     return dp
+
+
+def cap_for(cfg, T=None):
+    return O.capacity(cfg.capacity_factor, cfg.k, cfg.T if T is None else T, cfg.E)
 
 
 def check_bias(counts_gpu, gamma, bias_in, bias_gpu, T, k=6):

@@ -38,7 +38,7 @@ def test_version_and_status_strings():
 
 def desc(**kw):
     base = dict(T=128, d=512, F=128, E=256, S=2, k=6, act=L.F32, weight=L.F32,
-                gate_norm=L.GATE_RATIO, gate_scale=1.0)
+                gate_norm=L.GATE_RATIO, gate_scale=1.0, capacity_factor=0.0)
     base.update(kw)
     return L.Desc(**base)
 
@@ -60,6 +60,8 @@ def ws_size(d, call):
     (dict(gate_scale=-8.0), 2), (dict(gate_scale=float("inf")), 2),
     (dict(gate_scale=float("nan")), 2),
     (dict(gate_norm=L.GATE_LOGSUMEXP, gate_scale=6.5), 0),
+    (dict(capacity_factor=-1.0), 2), (dict(capacity_factor=float("inf")), 2),
+    (dict(capacity_factor=float("nan")), 2), (dict(capacity_factor=1.25), 0),
 ])
 def test_desc_validation(kw, code):
     st, _ = ws_size(desc(**kw), L.CALL_FORWARD)

@@ -263,6 +263,75 @@ def test_dispatch_invariants_large():
         assert np.all(np.diff(seg) > 0)
 
 
+def test_capacity_dispatch_matches_explicit_loops():
+    # walk the pairs in ascending pair number; each expert keeps its first
+    # `cap` pairs ("Inkling, Dissected" 02d; drop order: ascending token)
+    rng = np.random.default_rng(11)
+    E, k, T = 8, 3, 41
+    top = np.stack([rng.choice(E, size=k, replace=False, p=np.r_[0.4, [0.6 / 7] * 7])
+                    for _ in range(T)])
+    for cap in (1, 5, 12, 1000):
+        dp = O.dispatch(top, n_routed=E, cap=cap)
+        seen = [0] * E
+        kept_pairs = {e: [] for e in range(E)}
+        dropped = []
+        for p in range(T * k):
+            e = top[p // k, p % k]
+            if seen[e] < cap:
+                kept_pairs[e].append(p)
+            else:
+                dropped.append(p)
+            seen[e] += 1
+        assert list(dp["counts"]) == seen
+        assert list(dp["kept"]) == [min(c, cap) for c in seen]
+        expect_sorted = [p for e in range(E) for p in kept_pairs[e]]
+        assert list(dp["sorted_pair"]) == expect_sorted
+        assert list(dp["offsets"]) == [sum(min(c, cap) for c in seen[:e]) for e in range(E + 1)]
+        for pos, p in enumerate(expect_sorted):
+            assert dp["pair_pos"][p] == pos
+        for p in dropped:
+            assert dp["pair_pos"][p] == -1
+    # a capacity at or above every load changes nothing
+    full = O.dispatch(top, n_routed=E)
+    big = O.dispatch(top, n_routed=E, cap=int(full["counts"].max()))
+    for key in ("counts", "offsets", "sorted_pair", "pair_pos"):
+        assert np.array_equal(full[key], big[key])
+
+
+def test_capacity_value_and_load_metrics():
+    # C = ceil(cf * k*T / E), cf rounded to float32 first
+    assert O.capacity(1.25, 6, 2048, 64) == 240
+    assert O.capacity(1.0, 6, 2048, 64) == 192
+    assert O.capacity(1.25, 6, 16384, 256) == 480
+    assert O.capacity(0.0, 6, 2048, 64) is None
+    assert O.capacity(1.1, 6, 100, 256) == 3           # 1.1f * 600 / 256 = 2.578...
+    assert O.capacity(1.0, 6, 1, 256) == 1             # 6/256 rounds up to one row
+    # MaxVio: hottest demand over the ideal load, minus 1; drop rate over k*T slots
+    E, k, T = 4, 2, 8                                   # ideal load 4
+    m = O.load_metrics([4, 4, 4, 4], [4, 4, 4, 4], k, T)
+    assert m == {"max_vio": 0.0, "drop_rate": 0.0}
+    m = O.load_metrics([8, 4, 2, 2], [5, 4, 2, 2], k, T)
+    assert m["max_vio"] == 1.0 and m["drop_rate"] == 3 / 16
+
+
+def test_combine_skips_dropped_slots():
+    rng = np.random.default_rng(12)
+    T, k, d = 5, 3, 4
+    yr = rng.normal(size=(T * k, d))
+    ys = rng.normal(size=(2, T, d))
+    g = rng.uniform(0.1, 1.0, size=(T, k + 2))
+    pp = rng.permutation(T * k)
+    pp[[1, 7, 8]] = -1
+    y = O.combine(yr, ys, g, pp, k)
+    for t in range(T):
+        want = np.zeros(d)
+        for j in range(k):
+            if pp[t * k + j] >= 0:
+                want = want + g[t, j] * yr[pp[t * k + j]]
+        want = want + g[t, k] * ys[0, t] + g[t, k + 1] * ys[1, t]
+        np.testing.assert_allclose(y[t], want, rtol=1e-15, atol=1e-15)
+
+
 # ---------------------------------------------- expert FFN + combine
 
 def _torch_swiglu(x, wg, wu, wd):

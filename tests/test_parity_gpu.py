@@ -14,9 +14,9 @@ from oracle import moe_oracle as O
 from sparse_mixture_experts_04_amd import configs, synth
 from sparse_mixture_experts_04_amd.configs import MoEConfig
 
-from parity_util import (Buffers, check_bias, check_dispatch, check_routing, desc_for,
-                         expert_getter, host_weights, log, np64, npi, rel_l2, run_forward,
-                         run_stages)
+from parity_util import (Buffers, cap_for, check_bias, check_dispatch, check_routing,
+                         desc_for, expert_getter, host_weights, log, np64, npi, rel_l2,
+                         run_forward, run_stages)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,6 +36,13 @@ SMALL = {
                           gate_norm="logsumexp", gate_scale=6.5),
     "bf16_lse_big": MoEConfig("bf16_lse_big", T=2500, d=768, F=384, act="bf16",
                               bias_range=0.05, gate_norm="logsumexp", gate_scale=6.5),
+    # per-expert capacity ("Inkling, Dissected" 02d): overflow pairs dropped
+    "bf16_cap": MoEConfig("bf16_cap", T=2200, d=512, F=256, act="bf16", bias_range=0.05,
+                          capacity_factor=1.0),
+    "bf16_cap_skew": MoEConfig("bf16_cap_skew", T=1500, d=256, F=128, act="bf16",
+                               bias_range=0.0, skew_kappa=8.0, capacity_factor=1.25),
+    "f32_cap": MoEConfig("f32_cap", T=128, d=512, F=128, act="f32", bias_range=0.1,
+                         wd_std_from_F=True, capacity_factor=0.75),
 }
 
 
@@ -60,7 +67,10 @@ def test_full_parity_stagewise(name):
     r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates),
                                  gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
     log(f"  routing {st}")
-    dp = check_dispatch(topk, b)
+    dp = check_dispatch(topk, b, cap=cap_for(cfg))
+    if cfg.capacity_factor:
+        m = O.load_metrics(dp["counts"], dp["kept"], cfg.k, cfg.T)
+        log(f"  capacity {cap_for(cfg)}: MaxVio {m['max_vio']:.2f}, dropped {m['drop_rate']:.3f}")
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
 
     hw = host_weights(inp)
@@ -128,7 +138,8 @@ def sample_tokens(T, n, seed=0):
     return sorted(picks)
 
 
-@pytest.mark.parametrize("name,nsample", [("B", 48), ("C", 12), ("D", 6), ("I", 4)])
+@pytest.mark.parametrize("name,nsample", [("B", 48), ("C", 12), ("D", 6), ("I", 4),
+                                          ("Ecap", 8)])
 def test_workload_parity(name, nsample):
     cfg = configs.get(name)
     log(f"[workload parity] {name}: {cfg.describe()}")
@@ -140,10 +151,10 @@ def test_workload_parity(name, nsample):
     r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates),
                                  gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
     log(f"  routing {st}")
-    check_dispatch(topk, b)
+    dp = check_dispatch(topk, b, cap=cap_for(cfg))
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
     toks = sample_tokens(cfg.T, nsample)
-    y_ref = O.output_rows(toks, x64, topk, g_ref, expert_getter(inp))
+    y_ref = O.output_rows(toks, x64, topk, g_ref, expert_getter(inp), pair_pos=dp["pair_pos"])
     e = rel_l2(np64(b.y)[toks], y_ref)
     log(f"  sampled {len(toks)} tokens: rel L2 {e:.2e}")
     assert e <= out_tol(cfg)
