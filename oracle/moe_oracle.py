@@ -30,7 +30,10 @@ Sources (page title, section):
   width) and "The routing strategy: sigmoid + shared expert sink" (top-6 over
   routed experts only; shared scores join the normalisation, written there
   as log-sigmoid followed by logsumexp over the joint set of 8, and the
-  weights are then scaled by route_scale times a learned global scale).
+  weights are then scaled by route_scale times a learned global scale) and
+  "Quantization: BF16 vs NVFP4" (FP4 weights with small-block scales, on
+  the routed experts only; the gates, the shared experts and the router
+  stay in high precision).
 
 Readings where the pages leave a step open:
 
@@ -223,6 +226,65 @@ def load_metrics(counts, kept, k, T):
     max_vio = float(counts.max()) * E / (k * T) - 1.0
     drop_rate = float(k * T - np.asarray(kept).sum()) / (k * T)
     return {"max_vio": max_vio, "drop_rate": drop_rate}
+
+
+# ------------------------------------------------- FP4 expert weights
+
+E2M1_VALUES = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])   # magnitudes of codes 0..7
+MX_BLOCK = 32
+
+
+def mxfp4_quantize(w):
+    """FP4 (E2M1) codes with one power-of-two scale per 32 consecutive
+    values of the last axis: the OCP microscaling format MXFP4, which the
+    MI355X converts in hardware.  It stands in for the NVFP4 of "Under The
+    Hood: Inkling", "Quantization: BF16 vs NVFP4" (FP4 values, small blocks,
+    per-block scales), whose 16-value blocks with FP8 scales are Blackwell's
+    format.
+
+    For a block with largest magnitude a: X = floor(log2 a) - 2 (2 is the
+    largest E2M1 exponent), clamped to [-127, 127], and X = -127 when a = 0.
+    Each value v becomes the E2M1 magnitude nearest to |v| / 2^X (ties to
+    the even code, magnitudes above 6 saturate to 6) with v's sign bit as
+    bit 3 of the code.  Returns (codes uint8 [..., K], X int64 [..., K/32]).
+    """
+    w = _f64(w)
+    K = w.shape[-1]
+    assert K % MX_BLOCK == 0
+    blocks = w.reshape(w.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    amax = np.abs(blocks).max(axis=-1)
+    _, e = np.frexp(amax)                      # amax = m * 2^e, m in [0.5, 1)
+    X = np.where(amax > 0, e.astype(np.int64) - 1 - 2, -127)
+    X = np.clip(X, -127, 127)
+    m = np.abs(blocks) * np.exp2(-X)[..., None].astype(np.float64)
+    dist = np.abs(m[..., None] - E2M1_VALUES)              # [..., 32, 8]
+    best = dist.min(axis=-1, keepdims=True)
+    cand = dist == best
+    # the nearest magnitude; on a tie the even code (lower of the two here)
+    even = cand & (np.arange(8) % 2 == 0)
+    mag = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    codes = mag + 8 * np.signbit(blocks)
+    return codes.reshape(w.shape).astype(np.uint8), X.astype(np.int64)
+
+
+def mxfp4_dequantize(codes, X):
+    """Values of MXFP4 codes: (-1)^bit3 * E2M1[code & 7] * 2^X, float64."""
+    codes = np.asarray(codes)
+    K = codes.shape[-1]
+    mag = E2M1_VALUES[codes & 7] * np.where(codes & 8, -1.0, 1.0)
+    blocks = mag.reshape(codes.shape[:-1] + (K // MX_BLOCK, MX_BLOCK))
+    return (blocks * np.exp2(np.asarray(X, dtype=np.float64))[..., None]).reshape(codes.shape)
+
+
+def mxfp4_pack(codes, X):
+    """Byte layout of one expert stack [E, N, K] of MXFP4 weights: nibbles
+    [E, N, K/2] with value 2i in the low nibble of byte i, and scale bytes
+    X + 127 laid out [E, K/32, N] (the scales of one K block of consecutive
+    weight rows are contiguous)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    packed = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    scales = (np.asarray(X) + 127).astype(np.uint8)
+    return packed, np.ascontiguousarray(np.swapaxes(scales, -1, -2))
 
 
 def silu(u):

@@ -454,3 +454,65 @@ def test_bias_update_single_step_exact():
     step = np.float32(1e-3)
     expect = np.where(counts < 1.5, b0 + step, b0 - step).astype(np.float32)
     assert np.array_equal(b1, expect)
+
+
+# ---------------------------------------------- FP4 (MXFP4) expert weights
+
+def _e2m1_from_bits(code):
+    # sign bit 3, exponent bits 2..1 (bias 1), mantissa bit 0; exponent 0 is subnormal
+    sgn = -1.0 if code & 8 else 1.0
+    e, m = (code >> 1) & 3, code & 1
+    return sgn * (m * 0.5 if e == 0 else 2.0 ** (e - 1) * (1 + m / 2))
+
+
+def test_mxfp4_value_table_from_bit_definition():
+    codes = np.arange(16, dtype=np.uint8).reshape(1, 16).repeat(2, axis=1)   # K = 32
+    for X in (-127, -3, 0, 5, 127):
+        got = O.mxfp4_dequantize(codes, np.array([[X]]))[0]
+        want = [_e2m1_from_bits(c) * 2.0 ** X for c in codes[0]]
+        assert np.array_equal(got, want)
+
+
+def test_mxfp4_scale_exponent_and_ties():
+    # a block whose largest magnitude lies in [4, 8) keeps scale 2^0, so the
+    # values below land on the grid as given; ties go to the even code
+    vals = [0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 7.0, -0.25, -5.0, 0.3, 6.0]
+    want = [0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0, 6.0, -0.0, -4.0, 0.5, 6.0]
+    w = np.zeros((1, 32))
+    w[0, :len(vals)] = vals
+    c, X = O.mxfp4_quantize(w)
+    assert X[0, 0] == 0
+    d = O.mxfp4_dequantize(c, X)[0, :len(vals)]
+    assert np.array_equal(d, want) and np.signbit(d[8])
+    # X = floor(log2 amax) - 2: amax 3.9 -> -1, 4.0 -> 0, 1e-3 -> -12; zeros -> -127
+    for amax, xw in ((3.9, -1), (4.0, 0), (7.99, 0), (8.0, 1), (1e-3, -12), (0.0, -127)):
+        w = np.zeros((1, 32))
+        w[0, 5] = amax
+        assert O.mxfp4_quantize(w)[1][0, 0] == xw, amax
+    # the exponent clamps at the top of the E8M0 range
+    w = np.zeros((1, 32)); w[0, 0] = 2.0 ** 200
+    assert O.mxfp4_quantize(w)[1][0, 0] == 127
+
+
+def test_mxfp4_error_bound_and_round_trip():
+    rng = np.random.default_rng(21)
+    w = rng.normal(size=(64, 256)) * np.exp2(rng.integers(-20, 20, size=(64, 1)))
+    c, X = O.mxfp4_quantize(w)
+    d = O.mxfp4_dequantize(c, X)
+    scale = np.repeat(np.exp2(X.astype(float)), 32, axis=1)
+    m = np.abs(w) / scale
+    # nearest grid point: half the local spacing, at most 1 below 6; saturation above 6
+    bound = np.where(m > 6.0, m - 6.0, np.where(m > 4, 1.0, np.where(m > 2, 0.5, 0.25))) * scale
+    assert np.all(np.abs(w - d) <= bound + 0.0)
+    # values already on the grid come back exactly
+    c2, X2 = O.mxfp4_quantize(d)
+    assert np.array_equal(O.mxfp4_dequantize(c2, X2), d)
+
+
+def test_mxfp4_pack_layout():
+    codes = np.arange(64, dtype=np.uint8).reshape(1, 1, 64) % 16   # E=1, N=1, K=64
+    X = np.array([[[3, -4]]])
+    packed, scales = O.mxfp4_pack(codes, X)
+    assert packed.shape == (1, 1, 32) and packed[0, 0, 0] == (0 | (1 << 4))
+    assert packed[0, 0, 7] == (14 | (15 << 4))
+    assert scales.shape == (1, 2, 1) and list(scales[0, :, 0]) == [130, 123]
