@@ -33,10 +33,12 @@
  * - Floating-point inputs holding NaN or Inf give undefined results.
  *   Out-of-range expert ids handed to moe_dispatch are skipped (they never
  *   cause out-of-bounds writes) and leave the outputs undefined.
- * - Supported shapes (v1): E = 256, S = 2, k = 6; act == weight, either
- *   MOE_F32 or MOE_BF16; d % 256 == 0; F % 128 == 0; 0 <= T and
- *   T * (k + S) * max(d, F) < 2^40, T * k < 2^31.  Anything else is
- *   MOE_ERR_UNSUPPORTED (or MOE_ERR_SHAPE for negative sizes).
+ * - Supported shapes: E = 256, S = 2, k = 6; act == weight, either
+ *   MOE_F32 or MOE_BF16, or act MOE_BF16 with weight MOE_MXFP4 for decode
+ *   batches (T * k < 48 * E, the batches whose experts hold a few rows);
+ *   d % 256 == 0; F % 128 == 0; 0 <= T and T * (k + S) * max(d, F) < 2^40,
+ *   T * k < 2^31.  Anything else is MOE_ERR_UNSUPPORTED (or MOE_ERR_SHAPE
+ *   for negative sizes, MOE_ERR_DTYPE for other dtype pairs).
  *
  * Intermediate layouts shared between calls:
  * - pair p = t * k + j is token t's slot-j routed choice (rank order).
@@ -91,7 +93,10 @@ typedef enum {
   MOE_ERR_HIP = 6          /* a kernel launch failed                     */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* MOE_MXFP4 is a weight format only (moe_desc.weight): the routed experts'
+ * matrices in FP4 with block scales (see moe_quantize_mxfp4); the shared
+ * experts stay in the act dtype. */
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_MXFP4 = 2 } moe_dtype;
 
 /* Which call a workspace size is asked for. */
 typedef enum {
@@ -135,7 +140,11 @@ typedef struct {
 /* Weights of one layer.  Expert matrices are [out, in] row-major:
  *   w_router [E+S, d] fp32  (rows E.. are the shared experts' vectors)
  *   w_gate, w_up [E, F, d]   w_down [E, d, F]        (act dtype)
- *   ws_gate, ws_up [S, F, d] ws_down [S, d, F]       (act dtype)        */
+ *   ws_gate, ws_up [S, F, d] ws_down [S, d, F]       (act dtype)
+ * With weight == MOE_MXFP4 the routed matrices are the outputs of
+ * moe_quantize_mxfp4: w_gate, w_up [E, F, d/2] and w_down [E, d, F/2]
+ * bytes of packed FP4 codes, and sc_gate, sc_up [E, d/32, F], sc_down
+ * [E, F/32, d] their scale bytes (NULL otherwise). */
 typedef struct {
   const float* w_router;
   const void* w_gate;
@@ -144,6 +153,9 @@ typedef struct {
   const void* ws_gate;
   const void* ws_up;
   const void* ws_down;
+  const uint8_t* sc_gate;
+  const uint8_t* sc_up;
+  const uint8_t* sc_down;
 } moe_weights;
 
 /* Optional routing outputs of moe_forward: each pointer may be NULL, in
@@ -248,6 +260,19 @@ moe_status moe_combine(const moe_desc* desc, const void* y_routed,
  * comparison is exact integer arithmetic).  gamma must be finite. */
 moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts,
                            float gamma, float* bias, hipStream_t stream);
+
+/* FP4 expert weights ("Under The Hood: Inkling", "Quantization: BF16 vs
+ * NVFP4": FP4 weights with small-block scales for the routed experts only).
+ * MI355X's own FP4 format is used, OCP MXFP4: E2M1 values with one
+ * power-of-two scale per 32 consecutive values along K.  For each block
+ * with largest magnitude a: X = floor(log2 a) - 2, clamped to [-127, 127]
+ * (-127 when a = 0); each value v becomes the E2M1 magnitude nearest to
+ * |v| / 2^X (ties to the even code; above 6 saturates to 6) with v's sign
+ * as bit 3.  Quantizes a bf16 stack w [E, N, K] (K % 32 == 0) into
+ * codes [E, N, K/2] (value 2i in the low nibble of byte i) and scales
+ * [E, K/32, N] (bytes X + 127).  Device pointers; asynchronous. */
+moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w,
+                              uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 /* The whole layer: router (with the incoming bias), dispatch, expert FFN,
  * combine, then the bias update in place (the next batch routes with the

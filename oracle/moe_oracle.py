@@ -257,12 +257,14 @@ def mxfp4_quantize(w):
     X = np.where(amax > 0, e.astype(np.int64) - 1 - 2, -127)
     X = np.clip(X, -127, 127)
     m = np.abs(blocks) * np.exp2(-X)[..., None].astype(np.float64)
-    dist = np.abs(m[..., None] - E2M1_VALUES)              # [..., 32, 8]
-    best = dist.min(axis=-1, keepdims=True)
-    cand = dist == best
-    # the nearest magnitude; on a tie the even code (lower of the two here)
-    even = cand & (np.arange(8) % 2 == 0)
-    mag = np.where(even.any(axis=-1), even.argmax(axis=-1), cand.argmax(axis=-1))
+    # the two grid magnitudes around m, then the nearer one; on a tie the
+    # even code; above the top of the grid, the top
+    hi = np.clip(np.searchsorted(E2M1_VALUES, m), 1, 7)     # E2M1[hi-1] < m <= E2M1[hi]
+    lo = hi - 1
+    d_lo = m - E2M1_VALUES[lo]
+    d_hi = E2M1_VALUES[hi] - m
+    mag = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    mag = np.where(m >= E2M1_VALUES[7], 7, mag)
     codes = mag + 8 * np.signbit(blocks)
     return codes.reshape(w.shape).astype(np.uint8), X.astype(np.int64)
 

@@ -14,7 +14,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
-F32, BF16 = 0, 1
+F32, BF16, MXFP4 = 0, 1, 2
 CALL_ROUTER, CALL_DISPATCH, CALL_GATE_UP, CALL_DOWN = 0, 1, 2, 3
 CALL_EXPERT_FFN, CALL_COMBINE, CALL_BIAS_UPDATE, CALL_FORWARD = 4, 5, 6, 7
 
@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE"
 SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router",
            "moe_dispatch", "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn",
            "moe_combine", "moe_bias_update", "moe_forward", "moe_expert_gate_up_marked",
-           "moe_expert_down_marked")
+           "moe_expert_down_marked", "moe_quantize_mxfp4")
 
 
 class MoEError(RuntimeError):
@@ -43,7 +43,8 @@ class Desc(ctypes.Structure):
 
 class Weights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in
-                ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")]
+                ("w_router", "w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down",
+                 "sc_gate", "sc_up", "sc_down")]
 
 
 class Routing(ctypes.Structure):
@@ -74,6 +75,7 @@ def _load(path=LIB_PATH):
         "moe_combine": (I, [D, P, P, P, P, P, P]),
         "moe_bias_update": (I, [D, P, ctypes.c_float, P, P]),
         "moe_forward": (I, [D, P, W, P, ctypes.c_float, P, ctypes.POINTER(Routing), P, Z, P]),
+        "moe_quantize_mxfp4": (I, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -102,10 +104,13 @@ GATE_RATIO, GATE_LOGSUMEXP = 0, 1
 
 
 def make_desc(T, d, F, act_dtype, E=256, S=2, k=6, gate_norm="ratio", gate_scale=1.0,
-              capacity_factor=0.0):
+              capacity_factor=0.0, fp4_weights=False):
+    """Layer descriptor; ``fp4_weights`` marks the routed experts' weights as
+    MXFP4 (quantize_mxfp4 outputs, bf16 activations only)."""
     a = act_code(act_dtype)
     norm = {"ratio": GATE_RATIO, "logsumexp": GATE_LOGSUMEXP}[gate_norm]
-    return Desc(T, d, F, E, S, k, a, a, norm, gate_scale, capacity_factor)
+    return Desc(T, d, F, E, S, k, a, MXFP4 if fp4_weights else a, norm, gate_scale,
+                capacity_factor)
 
 
 def _act(desc):
@@ -161,6 +166,42 @@ def make_weights(w_router, w_gate, w_up, w_down, ws_gate, ws_up, ws_down):
 def weights_from(inp):
     return make_weights(inp["w_router"], inp["w_gate"], inp["w_up"], inp["w_down"],
                         inp["ws_gate"], inp["ws_up"], inp["ws_down"])
+
+
+def quantize_mxfp4(w):
+    """moe_quantize_mxfp4 of a bf16 stack w [E, N, K]: returns (codes
+    uint8 [E, N, K/2], scales uint8 [E, K/32, N]) on w's device."""
+    E, N, K = w.shape
+    codes = torch.empty((E, N, K // 2), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, K // 32, N), dtype=torch.uint8, device=w.device)
+    st = lib.moe_quantize_mxfp4(E, N, K, _ptr(w, torch.bfloat16, (E, N, K), "w"),
+                                codes.data_ptr(), scales.data_ptr(), _stream(w.device))
+    _check("moe_quantize_mxfp4", st)
+    return codes, scales
+
+
+def fp4_weights(inp):
+    """Weights with the routed experts quantized to MXFP4 (the shared experts
+    and the router as given).  Returns (Weights, dict of the new tensors,
+    which must stay alive while the Weights are used)."""
+    q = {}
+    for n in ("w_gate", "w_up", "w_down"):
+        q[n], q["sc_" + n[2:]] = quantize_mxfp4(inp[n])
+    E, F, d = inp["w_gate"].shape
+    S = inp["ws_gate"].shape[0]
+    wt = Weights()
+    wt.w_router = _ptr(inp["w_router"], torch.float32, (E + S, d), "w_router")
+    wt.w_gate = _ptr(q["w_gate"], torch.uint8, (E, F, d // 2), "w_gate")
+    wt.w_up = _ptr(q["w_up"], torch.uint8, (E, F, d // 2), "w_up")
+    wt.w_down = _ptr(q["w_down"], torch.uint8, (E, d, F // 2), "w_down")
+    wt.sc_gate = _ptr(q["sc_gate"], torch.uint8, (E, d // 32, F), "sc_gate")
+    wt.sc_up = _ptr(q["sc_up"], torch.uint8, (E, d // 32, F), "sc_up")
+    wt.sc_down = _ptr(q["sc_down"], torch.uint8, (E, F // 32, d), "sc_down")
+    dt = torch.bfloat16
+    wt.ws_gate = _ptr(inp["ws_gate"], dt, (S, F, d), "ws_gate")
+    wt.ws_up = _ptr(inp["ws_up"], dt, (S, F, d), "ws_up")
+    wt.ws_down = _ptr(inp["ws_down"], dt, (S, d, F), "ws_down")
+    return wt, q
 
 
 # ------------------------------------------------------------------ calls

@@ -12,6 +12,8 @@ stand-ins chosen to exercise the regimes that matter on one GPU:
 * ``E``  shape of ``D`` with a skewed router, run for 100 bias-update steps;
 * ``Ecap`` ``E`` with a hard capacity of 1.25x the ideal load per expert
   (the Router Balance Lab's setting in "Inkling, Dissected" 02g);
+* ``Cfp4`` the decode batch of ``C`` with the routed experts' weights in FP4
+  (MXFP4 blocks of 32; "Under The Hood: Inkling", quantization);
 * ``I``  the configuration of "Under The Hood: Inkling" (hidden 6144, expert
   width 3072, gates normalised by logsumexp over log-sigmoids and scaled by
   route_scale = 8 times a global scale; the learned global scale is stood in
@@ -41,6 +43,7 @@ class MoEConfig:
     gate_norm: str = "ratio"   # "ratio" or "logsumexp"
     gate_scale: float = 1.0    # multiplier of every gate
     capacity_factor: float = 0.0   # per-expert capacity in units of the ideal load (0: none)
+    fp4_weights: bool = False      # routed experts' weights in MXFP4
     extra: dict = field(default_factory=dict)
 
     @property
@@ -64,6 +67,8 @@ CONFIGS = {
                    gate_norm="logsumexp", gate_scale=8.0 * 0.8125),
     "Ecap": MoEConfig("Ecap", T=16384, d=7168, F=2048, act="bf16", bias_range=0.0,
                       skew_kappa=8.0, steps=100, capacity_factor=1.25),
+    "Cfp4": MoEConfig("Cfp4", T=64, d=7168, F=2048, act="bf16", bias_range=0.0,
+                      fp4_weights=True),
 }
 
 

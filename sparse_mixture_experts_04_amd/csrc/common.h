@@ -43,6 +43,7 @@ struct Shape {
   bool gate_logsumexp = false;  // gate normalisation (router only)
   float gate_scale = 1.0f;
   int capacity = 0x7fffffff;     // pairs kept per routed expert
+  bool w_fp4 = false;            // routed expert weights in MXFP4
 };
 
 // Router columns are padded to a multiple of the router's column tile.
@@ -79,15 +80,21 @@ hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile
 
 // marks (optional, may be null): see launch_big; the 32-row path records
 // marks[0] and marks[1] together after its single launch.
+// scg, scu, scd: scales of the routed weights when they are FP4 (s.w_fp4),
+// else unused.
 hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
-                          const void* wsg, const void* wsu, const int32_t* offsets,
+                          const void* wsg, const void* wsu, const uint8_t* scg,
+                          const uint8_t* scu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start,
                           int row_tile, void* h, hipEvent_t* marks, hipStream_t st);
 
-hipError_t launch_down(const Shape& s, const void* wd, const void* wsd,
+hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
                        const void* h, void* y_routed, void* y_shared, hipEvent_t* marks,
                        hipStream_t st);
+
+hipError_t launch_quantize_mxfp4(long long E, int N, int K, const void* w, uint8_t* codes,
+                                 uint8_t* scales, hipStream_t st);
 
 hipError_t launch_combine(const Shape& s, const void* y_routed, const void* y_shared,
                           const float* gates, const int32_t* pair_pos, void* y,

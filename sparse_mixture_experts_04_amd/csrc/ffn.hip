@@ -234,13 +234,15 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   for (int g = tid; g <= G; g += 256) ts[g] = p.tile_start[g];
   __syncthreads();
 
-  const long long total = static_cast<long long>(ts[G]) * p.n_tiles;
+  // items of groups g_lo..G-1
+  const long long first = static_cast<long long>(ts[p.g_lo]) * p.n_tiles;
+  const long long total = static_cast<long long>(ts[G]) * p.n_tiles - first;
   const int xcd = blockIdx.x & 7;
   const int per_xcd = gridDim.x >> 3;
   const int slot = blockIdx.x >> 3;
   const long long chunk = (total + 7) / 8;
-  const long long beg = xcd * chunk;
-  const long long end = beg + chunk < total ? beg + chunk : total;
+  const long long beg = first + xcd * chunk;
+  const long long end = beg + chunk < first + total ? beg + chunk : first + total;
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
@@ -464,11 +466,14 @@ static hipError_t run_f32(const FfnArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
-                          const void* wsg, const void* wsu, const int32_t* offsets,
+                          const void* wsg, const void* wsu, const uint8_t* scg,
+                          const uint8_t* scu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start, int row_tile,
                           void* h, hipEvent_t* marks, hipStream_t st) {
   if (s.T == 0) return record_marks(marks, st);
   FfnArgs a{};
+  a.sc0 = scg;
+  a.sc1 = scu;
   a.a = x;
   a.w0 = wg;
   a.w1 = wu;
@@ -490,6 +495,12 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
   if (s.bf16) {
     a.n_tiles = s.F / 128;
     if (row_tile != 32) return launch_big(a, true, tile_start, 0, marks, st);
+    if (s.w_fp4) {  // routed experts in FP4, then the bf16 shared experts
+      hipError_t e = launch_fp4(a, true, st);
+      a.g_lo = s.E;
+      if (e == hipSuccess) e = run_bf16<32, true>(a, st);
+      return e == hipSuccess ? record_marks(marks, st) : e;
+    }
     hipError_t e = run_bf16<32, true>(a, st);
     return e == hipSuccess ? record_marks(marks, st) : e;
   }
@@ -498,11 +509,13 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
   return e == hipSuccess ? record_marks(marks, st) : e;
 }
 
-hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const int32_t* offsets,
-                       const int32_t* tile_start, int row_tile, const void* h, void* y_routed,
-                       void* y_shared, hipEvent_t* marks, hipStream_t st) {
+hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
+                       const int32_t* offsets, const int32_t* tile_start, int row_tile,
+                       const void* h, void* y_routed, void* y_shared, hipEvent_t* marks,
+                       hipStream_t st) {
   if (s.T == 0) return record_marks(marks, st);
   FfnArgs a{};
+  a.sc0 = scd;
   a.a = h;
   a.w0 = wd;
   a.ws0 = wsd;
@@ -520,6 +533,12 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const in
   if (s.bf16) {
     a.n_tiles = s.d / 256;
     if (row_tile != 32) return launch_big(a, false, tile_start, 1, marks, st);
+    if (s.w_fp4) {
+      hipError_t e = launch_fp4(a, false, st);
+      a.g_lo = s.E;
+      if (e == hipSuccess) e = run_bf16<32, false>(a, st);
+      return e == hipSuccess ? record_marks(marks, st) : e;
+    }
     hipError_t e = run_bf16<32, false>(a, st);
     return e == hipSuccess ? record_marks(marks, st) : e;
   }

@@ -81,6 +81,9 @@ struct FfnArgs {
   int T, K, N, E, S, k;   // N = weight rows per expert (F for gate/up, d for down)
   int ldo;                // row length of the output
   int n_tiles;            // column tiles
+  const uint8_t* sc0;     // FP4 routed weights: scales of w0 / w1 [E, K/32, N]
+  const uint8_t* sc1;
+  int g_lo;               // first group the 32-row bf16 kernel processes
 };
 
 
@@ -132,5 +135,8 @@ hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int whi
 // Tile plan of the large-batch GEMM: [row tiles per group, exclusive
 // prefix (G+1) | work counters 2 GEMMs x kXcds].
 inline int big_plan_ints(int G) { return (G + 1) + 2 * kXcds; }
+
+// Decode-batch GEMMs over the routed groups with FP4 weights (ffn_fp4.hip).
+hipError_t launch_fp4(const FfnArgs& a, bool gated, hipStream_t st);
 
 }  // namespace moe

@@ -19,7 +19,9 @@ moe_status check_desc(const moe_desc* d) {
   if (!d) return MOE_ERR_NULL;
   if (d->T < 0 || d->d <= 0 || d->F <= 0 || d->E <= 0 || d->S < 0 || d->k <= 0)
     return MOE_ERR_SHAPE;
-  if ((d->act != MOE_F32 && d->act != MOE_BF16) || d->weight != d->act) return MOE_ERR_DTYPE;
+  if (d->act != MOE_F32 && d->act != MOE_BF16) return MOE_ERR_DTYPE;
+  const bool fp4 = d->act == MOE_BF16 && d->weight == MOE_MXFP4;
+  if (d->weight != d->act && !fp4) return MOE_ERR_DTYPE;
   if (d->gate_norm != MOE_GATE_RATIO && d->gate_norm != MOE_GATE_LOGSUMEXP) return MOE_ERR_SHAPE;
   if (!(d->gate_scale > 0.0f) || !(d->gate_scale < INFINITY)) return MOE_ERR_SHAPE;
   if (!(d->capacity_factor >= 0.0f) || !(d->capacity_factor < INFINITY)) return MOE_ERR_SHAPE;
@@ -29,6 +31,8 @@ moe_status check_desc(const moe_desc* d) {
   if (T * d->k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   const long long wide = d->d > d->F ? d->d : d->F;
   if (T * (d->k + d->S) * wide >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
+  // FP4 routed weights: decode batches (the 32-row GEMM path) only
+  if (fp4 && T * d->k >= 48LL * d->E) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -41,6 +45,7 @@ Shape to_shape(const moe_desc* d) {
   s.S = d->S;
   s.k = d->k;
   s.bf16 = d->act == MOE_BF16;
+  s.w_fp4 = d->weight == MOE_MXFP4;
   s.gate_logsumexp = d->gate_norm == MOE_GATE_LOGSUMEXP;
   s.gate_scale = d->gate_scale;
   s.capacity = INT32_MAX;
@@ -141,8 +146,10 @@ moe_status check_ws(const Shape& s, moe_call call, const void* ws, size_t ws_byt
 
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-bool weights_ok(const moe_weights* w) {
-  return w && w->w_gate && w->w_up && w->w_down && w->ws_gate && w->ws_up && w->ws_down;
+bool weights_ok(const moe_weights* w, const Shape& s) {
+  if (!(w && w->w_gate && w->w_up && w->w_down && w->ws_gate && w->ws_up && w->ws_down))
+    return false;
+  return !s.w_fp4 || (w->sc_gate && w->sc_up && w->sc_down);
 }
 
 }  // namespace
@@ -208,7 +215,7 @@ moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_wei
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets) return MOE_ERR_NULL;
+  if (!weights_ok(w, s) || !offsets) return MOE_ERR_NULL;
   if (s.T > 0 && (!x || !sorted_pair || !h)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
@@ -216,7 +223,8 @@ moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_wei
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
-    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
+                       offsets, sorted_pair,
                        plan, mt, h, nullptr, stream);
   return hip_status(e);
 }
@@ -227,7 +235,7 @@ moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w, const int
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets) return MOE_ERR_NULL;
+  if (!weights_ok(w, s) || !offsets) return MOE_ERR_NULL;
   if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
@@ -235,7 +243,7 @@ moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w, const int
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
                     stream);
   return hip_status(e);
 }
@@ -247,7 +255,7 @@ moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x, const 
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1])
+  if (!weights_ok(w, s) || !offsets || !marks || !marks[0] || !marks[1])
     return MOE_ERR_NULL;
   if (s.T > 0 && (!x || !sorted_pair || !h)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
@@ -257,7 +265,8 @@ moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x, const 
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess) e = hipEventRecord(marks[0], stream);
   if (e == hipSuccess)
-    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
+                       offsets, sorted_pair,
                        plan, mt, h, marks + 1, stream);
   return hip_status(e);
 }
@@ -269,7 +278,7 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets || !marks || !marks[0] || !marks[1])
+  if (!weights_ok(w, s) || !offsets || !marks || !marks[0] || !marks[1])
     return MOE_ERR_NULL;
   if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
@@ -279,7 +288,7 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess) e = hipEventRecord(marks[0], stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared,
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed, y_shared,
                     marks + 1, stream);
   return hip_status(e);
 }
@@ -290,7 +299,7 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const moe_weights
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !offsets) return MOE_ERR_NULL;
+  if (!weights_ok(w, s) || !offsets) return MOE_ERR_NULL;
   if (s.T > 0 && (!x || !sorted_pair || !y_routed || !y_shared)) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_EXPERT_FFN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
@@ -299,10 +308,11 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const moe_weights
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
-    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, offsets, sorted_pair,
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
+                       offsets, sorted_pair,
                        plan, mt, h, nullptr, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
                     stream);
   return hip_status(e);
 }
@@ -326,13 +336,23 @@ moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts, float ga
   return hip_status(launch_bias_update(to_shape(desc), counts, gamma, bias, stream));
 }
 
+moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w, uint8_t* codes,
+                              uint8_t* scales, hipStream_t stream) {
+  if (E < 0 || N <= 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (E == 0) return MOE_OK;
+  if (!w || !codes || !scales) return MOE_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(w) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 16 != 0)
+    return MOE_ERR_UNSUPPORTED;
+  return hip_status(launch_quantize_mxfp4(E, N, K, w, codes, scales, stream));
+}
+
 moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
                        float gamma, void* y, const moe_routing* routing, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (!weights_ok(w) || !w->w_router || !bias) return MOE_ERR_NULL;
+  if (!weights_ok(w, s) || !w->w_router || !bias) return MOE_ERR_NULL;
   if (s.T > 0 && (!x || !y)) return MOE_ERR_NULL;
   if (!std::isfinite(gamma)) return MOE_ERR_SHAPE;
   if ((st = check_ws(s, MOE_CALL_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
@@ -355,10 +375,11 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
     e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg, stream);
   if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
   if (e == hipSuccess)
-    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, f.offsets,
+    e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
+                       f.offsets,
                        f.sorted_pair, f.plan, mt, f.h, nullptr, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, f.offsets, f.plan, mt, f.h, f.y_routed,
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, f.offsets, f.plan, mt, f.h, f.y_routed,
                     f.y_shared, nullptr, stream);
   if (e == hipSuccess)
     e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);

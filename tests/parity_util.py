@@ -36,7 +36,7 @@ def npi(t):
 def desc_for(cfg, T=None):
     return L.make_desc(cfg.T if T is None else T, cfg.d, cfg.F, synth.act_dtype(cfg),
                        gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale,
-                       capacity_factor=cfg.capacity_factor)
+                       capacity_factor=cfg.capacity_factor, fp4_weights=cfg.fp4_weights)
 
 
 class Buffers:
@@ -59,12 +59,12 @@ class Buffers:
         self.y = torch.zeros((T, d), dtype=act, device=dev)
 
 
-def run_stages(desc, inp, gamma):
+def run_stages(desc, inp, gamma, weights=None):
     """router -> dispatch -> gate_up -> down -> combine -> bias update, each
     through its own C entry point.  Returns the Buffers and the new bias."""
     dev = inp["x"].device
     b = Buffers(desc, dev)
-    w = L.weights_from(inp)
+    w = L.weights_from(inp) if weights is None else weights
     bias = inp["bias"].clone()
     L.router(desc, inp["x"], inp["w_router"], bias, b.topk, b.gates, b.margin)
     L.dispatch(desc, b.topk, b.counts, b.offsets, b.sorted_pair, b.pair_pos)
@@ -76,10 +76,10 @@ def run_stages(desc, inp, gamma):
     return b, bias
 
 
-def run_forward(desc, inp, gamma, bias=None):
+def run_forward(desc, inp, gamma, bias=None, weights=None):
     dev = inp["x"].device
     b = Buffers(desc, dev)
-    w = L.weights_from(inp)
+    w = L.weights_from(inp) if weights is None else weights
     bias = (inp["bias"] if bias is None else bias).clone()
     routing = {"topk_idx": b.topk, "gates": b.gates, "margin": b.margin, "counts": b.counts,
                "offsets": b.offsets, "sorted_pair": b.sorted_pair, "pair_pos": b.pair_pos}

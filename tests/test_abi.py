@@ -17,7 +17,7 @@ lib = L.lib
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_symbol():
@@ -62,6 +62,9 @@ def ws_size(d, call):
     (dict(gate_norm=L.GATE_LOGSUMEXP, gate_scale=6.5), 0),
     (dict(capacity_factor=-1.0), 2), (dict(capacity_factor=float("inf")), 2),
     (dict(capacity_factor=float("nan")), 2), (dict(capacity_factor=1.25), 0),
+    # FP4 routed weights: bf16 activations, decode batches only
+    (dict(act=L.BF16, weight=L.MXFP4, T=64), 0), (dict(act=L.BF16, weight=L.MXFP4, T=2047), 0),
+    (dict(act=L.BF16, weight=L.MXFP4, T=2048), 5), (dict(act=L.F32, weight=L.MXFP4), 3),
 ])
 def test_desc_validation(kw, code):
     st, _ = ws_size(desc(**kw), L.CALL_FORWARD)
@@ -136,3 +139,13 @@ def test_binding_rejects_host_tensors():
     with pytest.raises(TypeError):
         L.make_desc(4, 512, 128, torch.float16)
     assert d.T == 4
+
+
+def test_quantize_argument_checks():
+    P = ctypes.c_void_p(0x1000)
+    assert lib.moe_quantize_mxfp4(2, 8, 48, P, P, P, None) == 2       # K % 32
+    assert lib.moe_quantize_mxfp4(-1, 8, 64, P, P, P, None) == 2
+    assert lib.moe_quantize_mxfp4(2, 0, 64, P, P, P, None) == 2
+    assert lib.moe_quantize_mxfp4(2, 8, 64, None, P, P, None) == 1
+    assert lib.moe_quantize_mxfp4(2, 8, 64, ctypes.c_void_p(0x1004), P, P, None) == 5
+    assert lib.moe_quantize_mxfp4(0, 8, 64, None, None, None, None) == 0  # nothing to do
