@@ -7,7 +7,8 @@ combine, bias update) over one batch already resident in HBM:
 
 * headline workload: T=16384 tokens, d=7168, F=2048, 256 routed + 2 shared
   experts, top-6, bf16 weights and activations, fp32 router;
-* decode workload (reported alongside): the same layer at T=64;
+* decode workload (reported alongside): the same layer at T=64, with bf16
+  weights and with the routed experts' weights in FP4 (MXFP4);
 * skewed workload (reported alongside): the headline shape with a skewed
   router, 100 consecutive batches (fresh tokens each) and the balancing
   bias updating after every batch; again with a hard per-expert capacity
@@ -43,6 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="D", help="headline workload (D)")
     ap.add_argument("--decode-workload", default="C")
+    ap.add_argument("--fp4-decode-workload", default="Cfp4")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--skewed-workload", default="E")
     ap.add_argument("--skewed-steps", type=int, default=100)
@@ -67,8 +69,13 @@ def expert_flops(cfg):
 def setup(cfg, torch, L, synth):
     inp = synth.make_inputs(cfg, device="cuda")
     desc = L.make_desc(cfg.T, cfg.d, cfg.F, synth.act_dtype(cfg), gate_norm=cfg.gate_norm,
-                       gate_scale=cfg.gate_scale)
-    w = L.weights_from(inp)
+                       gate_scale=cfg.gate_scale, capacity_factor=cfg.capacity_factor,
+                       fp4_weights=cfg.fp4_weights)
+    if cfg.fp4_weights:         # quantized once, outside the timed region
+        w, q = L.fp4_weights(inp)
+        inp.update({"fp4_" + k: v for k, v in q.items()})   # keep them alive
+    else:
+        w = L.weights_from(inp)
     y = torch.empty((cfg.T, cfg.d), dtype=synth.act_dtype(cfg), device="cuda")
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
     ws = L.alloc_workspace(desc, L.CALL_FORWARD, "cuda")
@@ -230,9 +237,10 @@ def decode_bytes(cfg, counts):
     n_active = int((counts > 0).sum())
     esz = 2 if cfg.act == "bf16" else 4
     per_expert = 3 * cfg.F * cfg.d * esz
+    routed = 3 * cfg.F * cfg.d * (0.5 + 1 / 32) if cfg.fp4_weights else per_expert
     router = (cfg.E + cfg.S) * cfg.d * 4
     xy = 2 * cfg.T * cfg.d * esz
-    return n_active * per_expert + cfg.S * per_expert + router + xy, n_active
+    return int(n_active * routed + cfg.S * per_expert + router + xy), n_active
 
 
 def cpu_baseline(cfg, inp, ntok, torch):
@@ -345,6 +353,21 @@ def main():
                          "bytes": nbytes, "active_experts": n_active,
                          "scope": "whole moe_forward step"}}
         del d_inp, d_ws
+        torch.cuda.empty_cache()
+        fc = configs.get(args.fp4_decode_workload)
+        f_inp, _, _, f_ws, f_counts, f_ms, _ = time_forward(fc, max(args.steps, 20),
+                                                            args.warmup, torch, L, synth)
+        f_bytes, f_active = decode_bytes(fc, f_counts.cpu())
+        f_gbs = f_bytes / (f_ms / 1e3) / 1e9
+        result["decode_fp4"] = {
+            "workload": f"decode MoE layer, {fc.describe()}, routed experts' weights MXFP4 "
+                        f"(E2M1, power-of-two scale per 32), shared experts bf16, fp32 router",
+            "tokens_s": round(fc.T / (f_ms / 1e3), 1), "ms_per_step": round(f_ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(f_gbs, 1), "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": round(f_gbs / PEAK_HBM_GBS, 4),
+                         "bytes": f_bytes, "active_experts": f_active,
+                         "scope": "whole moe_forward step"}}
+        del f_inp, f_ws
         torch.cuda.empty_cache()
     if not args.no_native:
         nc = configs.get(args.native_workload)
