@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-skewed", action="store_true")
     ap.add_argument("--native-workload", default="I")
     ap.add_argument("--no-native", action="store_true")
+    ap.add_argument("--lab-workload", default="Lab")
+    ap.add_argument("--no-lab", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
@@ -233,6 +235,47 @@ def time_skewed(cfg, steps, torch, L, synth):
                if cap is not None else {})}
 
 
+def balance_lab(cfg, torch, gammas=(0.0, 0.01, 0.05)):
+    """The Router Balance Lab ("Inkling, Dissected", 02g) on the GPU: for
+    each bias step gamma, the bias starts at zero and runs the workload's
+    steps over fresh batches; the lab's measures (MaxVio, drop rate, layer
+    quality) are averaged over the run.  A step is moe_router ->
+    moe_dispatch (capacity) -> moe_bias_update; its time is measured
+    separately, without the measures, with HIP events."""
+    from sparse_mixture_experts_04_amd import synth
+    from sparse_mixture_experts_04_amd.lab import BalanceLab
+    w = synth.make_lab_router(cfg).to("cuda")
+    xs = [synth.make_lab_x(cfg, i, device="cuda") for i in range(cfg.steps)]
+    runs = {}
+    for g in gammas:
+        lab = BalanceLab(cfg, w, g, "cuda")
+        meas = []
+        for x in xs:
+            lab.step(x)
+            meas.append(lab.measures(x))
+        meas = torch.stack(meas).cpu()
+        mean, last = meas.mean(dim=0).tolist(), meas[-1].tolist()
+        runs[f"gamma={g}"] = {"max_vio": round(mean[0], 4), "drop_rate": round(mean[1], 5),
+                              "quality": round(mean[2], 5),
+                              "last_step": [round(v, 5) for v in last]}
+    lab = BalanceLab(cfg, w, cfg.gamma, "cuda")
+    for x in xs[:5]:
+        lab.step(x)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for x in xs:
+        lab.step(x)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / len(xs)
+    return {"workload": f"Router Balance Lab, {cfg.describe()}, frozen router, "
+                        f"Zipf-lumpy tokens (head/tail {cfg.lab_head_tail:g}), capacity "
+                        f"{cfg.capacity_factor} x ideal, {cfg.steps} steps, routing only",
+            "measures_mean_over_steps": runs,
+            "ms_per_step": round(ms, 4), "tokens_s": round(cfg.T / (ms / 1e3), 1)}
+
+
 def decode_bytes(cfg, counts):
     n_active = int((counts > 0).sum())
     esz = 2 if cfg.act == "bf16" else 4
@@ -386,6 +429,8 @@ def main():
                                        torch, L, synth)
         result["capacity"] = time_skewed(configs.get(args.capacity_workload),
                                          args.skewed_steps, torch, L, synth)
+    if not args.no_lab:
+        result["balance_lab"] = balance_lab(configs.get(args.lab_workload), torch)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch)
     print(json.dumps(result), flush=True)

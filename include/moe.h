@@ -33,12 +33,16 @@
  * - Floating-point inputs holding NaN or Inf give undefined results.
  *   Out-of-range expert ids handed to moe_dispatch are skipped (they never
  *   cause out-of-bounds writes) and leave the outputs undefined.
- * - Supported shapes: E = 256, S = 2, k = 6; act == weight, either
- *   MOE_F32 or MOE_BF16, or act MOE_BF16 with weight MOE_MXFP4 for decode
- *   batches (T * k < 48 * E, the batches whose experts hold a few rows);
- *   d % 256 == 0; F % 128 == 0; 0 <= T and T * (k + S) * max(d, F) < 2^40,
- *   T * k < 2^31.  Anything else is MOE_ERR_UNSUPPORTED (or MOE_ERR_SHAPE
- *   for negative sizes, MOE_ERR_DTYPE for other dtype pairs).
+ * - Supported shapes: E in {64, 128, 256}, S in {0, 1, 2}, k = 6;
+ *   act == weight, either MOE_F32 or MOE_BF16, or act MOE_BF16 with weight
+ *   MOE_MXFP4 for decode batches (T * k < 48 * E, the batches whose experts
+ *   hold a few rows); d % 32 == 0, and for the calls that run the expert
+ *   GEMMs (gate/up, down, expert_ffn, forward and their workspace sizes)
+ *   also d % 256 == 0 and F % 128 == 0; 0 <= T and
+ *   T * (k + S) * max(d, F) < 2^40, T * k < 2^31.  Anything else is
+ *   MOE_ERR_UNSUPPORTED (or MOE_ERR_SHAPE for negative sizes, MOE_ERR_DTYPE
+ *   for other dtype pairs).  With S = 0 the shared-expert pointers
+ *   (ws_gate, ws_up, ws_down, y_shared) may be NULL.
  *
  * Intermediate layouts shared between calls:
  * - pair p = t * k + j is token t's slot-j routed choice (rank order).

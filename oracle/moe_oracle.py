@@ -43,7 +43,10 @@ Readings where the pages leave a step open:
 * the bias updates after the forward that used it;
 * SwiGLU expert: y = W_down (silu(W_gate x) * (W_up x)), silu(u) = u*sigmoid(u),
   no bias terms, weights stored [out, in];
-* loads count routed selections only.
+* loads count routed selections only;
+* the Router Balance Lab's layer quality weights each surviving expert by
+  its gate times its affinity, against the unbiased, uncapacitated top-k
+  (``layer_quality``).
 
 Every function here is pinned by ``tests/test_oracle.py``; none is left
 unpinned.
@@ -226,6 +229,58 @@ def load_metrics(counts, kept, k, T):
     max_vio = float(counts.max()) * E / (k * T) - 1.0
     drop_rate = float(k * T - np.asarray(kept).sum()) / (k * T)
     return {"max_vio": max_vio, "drop_rate": drop_rate}
+
+
+def layer_quality(s, topk_idx, pair_pos, k=6):
+    """Router Balance Lab's layer quality ("Inkling, Dissected", 02g): the
+    true affinity that the surviving weighted mixture captures, as a
+    fraction of what an uncapacitated, unbiased router captures.
+
+    This module's reading: a token's mixture over a set of routed experts
+    weights expert j by g_j = s_j / sum of s over the set (the gates of
+    02b); the mixture captures sum of g_j * s_j over the pairs that
+    survived capacity (a dropped pair contributes nothing, and the other
+    gates are not renormalised).  The uncapacitated oracle uses the top-k by
+    s alone (no bias, nothing dropped).  Quality = captured / oracle, both
+    summed over the batch.  ``s`` holds the routed experts' affinities
+    [T, n_routed]; ``pair_pos`` is dispatch's (-1 for a dropped pair).
+    """
+    s = _f64(s)
+    T = s.shape[0]
+    top = np.asarray(topk_idx, dtype=np.int64).reshape(T, k)
+    kept = np.asarray(pair_pos, dtype=np.int64).reshape(T, k) >= 0
+    g, _ = joint_gates(s, top, [])
+    sel = np.take_along_axis(s, top, axis=1)
+    captured = float(np.sum(np.where(kept, g * sel, 0.0)))
+    top0, _ = select_topk(s, k)
+    g0, _ = joint_gates(s, top0, [])
+    best = float(np.sum(g0 * np.take_along_axis(s, top0, axis=1)))
+    return captured / best
+
+
+def balance_lab(x_of_step, w_router, bias, gamma, capacity_factor, steps, k=6):
+    """The Router Balance Lab's loop ("Inkling, Dissected", 02g): a frozen
+    router, one fresh batch per step, hard capacity, and the selection-only
+    bias of 02e updated from each step's demand.  ``x_of_step(i)`` returns
+    step i's tokens.  Returns one record per step: the bias the step routed
+    with, the counts, MaxVio, drop rate and layer quality.  No shared
+    experts (w_router has one row per routed expert); gates by ratio.
+    """
+    b = np.asarray(bias, dtype=np.float32).copy()
+    E = b.size
+    out = []
+    for i in range(steps):
+        x = _f64(x_of_step(i))
+        T = x.shape[0]
+        r = route(x, w_router, b, n_routed=E, k=k)
+        dp = dispatch(r["topk_idx"], n_routed=E, cap=capacity(capacity_factor, k, T, E))
+        rec = {"bias": b, "topk_idx": r["topk_idx"], "margin": r["margin"],
+               "counts": dp["counts"]}
+        rec.update(load_metrics(dp["counts"], dp["kept"], k, T))
+        rec["quality"] = layer_quality(r["s"], r["topk_idx"], dp["pair_pos"], k)
+        out.append(rec)
+        b = bias_update(dp["counts"], gamma, b, T, k)
+    return out
 
 
 # ------------------------------------------------- FP4 expert weights

@@ -14,6 +14,11 @@ stand-ins chosen to exercise the regimes that matter on one GPU:
   (the Router Balance Lab's setting in "Inkling, Dissected" 02g);
 * ``Cfp4`` the decode batch of ``C`` with the routed experts' weights in FP4
   (MXFP4 blocks of 32; "Under The Hood: Inkling", quantization);
+* ``Lab`` the Router Balance Lab of "Inkling, Dissected" 02g: 64 experts,
+  no shared experts, d = 32, 2048 tokens per batch drawn around Zipf-lumpy
+  expert home directions, a frozen router, capacity 1.25x, 100 routing
+  steps with gamma = 0.01 (routing only: the lab has no expert FFNs, and F
+  is a placeholder);
 * ``I``  the configuration of "Under The Hood: Inkling" (hidden 6144, expert
   width 3072, gates normalised by logsumexp over log-sigmoids and scaled by
   route_scale = 8 times a global scale; the learned global scale is stood in
@@ -44,6 +49,10 @@ class MoEConfig:
     gate_scale: float = 1.0    # multiplier of every gate
     capacity_factor: float = 0.0   # per-expert capacity in units of the ideal load (0: none)
     fp4_weights: bool = False      # routed experts' weights in MXFP4
+    # Router Balance Lab inputs (tokens around expert "home" directions):
+    lab_head_tail: float = 0.0     # home-cluster frequency of expert 0 over expert E-1 (0: off)
+    lab_jitter: float = 1.0        # token jitter, in units of the home direction's length
+    lab_kappa: float = 4.0         # router weights = lab_kappa * home directions
     extra: dict = field(default_factory=dict)
 
     @property
@@ -67,6 +76,8 @@ CONFIGS = {
                    gate_norm="logsumexp", gate_scale=8.0 * 0.8125),
     "Ecap": MoEConfig("Ecap", T=16384, d=7168, F=2048, act="bf16", bias_range=0.0,
                       skew_kappa=8.0, steps=100, capacity_factor=1.25),
+    "Lab": MoEConfig("Lab", T=2048, d=32, F=128, E=64, S=0, act="f32", bias_range=0.0,
+                     gamma=0.01, steps=100, capacity_factor=1.25, lab_head_tail=30.0),
     "Cfp4": MoEConfig("Cfp4", T=64, d=7168, F=2048, act="bf16", bias_range=0.0,
                       fp4_weights=True),
 }

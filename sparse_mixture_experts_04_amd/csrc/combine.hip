@@ -77,23 +77,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yr,
   Vec<T>::store(y + static_cast<size_t>(t) * d + c0, acc);
 }
 
+template <typename T, int S>
+static void run_combine(const Shape& s, const void* y_routed, const void* y_shared,
+                        const float* gates, const int32_t* pair_pos, void* y, hipStream_t st) {
+  constexpr int V = Vec<T>::N;
+  const int nchunk = (s.d + 256 * V - 1) / (256 * V);
+  const long long blocks = static_cast<long long>(s.T) * nchunk;
+  combine_kernel<T, 6, S><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
+      static_cast<const T*>(y_routed), static_cast<const T*>(y_shared), gates, pair_pos, s.T,
+      s.d, nchunk, static_cast<T*>(y));
+}
+
+template <typename T>
+static void run_combine_s(const Shape& s, const void* y_routed, const void* y_shared,
+                          const float* gates, const int32_t* pair_pos, void* y, hipStream_t st) {
+  if (s.S == 0) run_combine<T, 0>(s, y_routed, y_shared, gates, pair_pos, y, st);
+  else if (s.S == 1) run_combine<T, 1>(s, y_routed, y_shared, gates, pair_pos, y, st);
+  else run_combine<T, 2>(s, y_routed, y_shared, gates, pair_pos, y, st);
+}
+
 hipError_t launch_combine(const Shape& s, const void* y_routed, const void* y_shared,
                           const float* gates, const int32_t* pair_pos, void* y,
                           hipStream_t st) {
   if (s.T == 0) return hipSuccess;
-  if (s.bf16) {
-    const int nchunk = (s.d + 256 * 8 - 1) / (256 * 8);
-    const long long blocks = static_cast<long long>(s.T) * nchunk;
-    combine_kernel<bf16_t, 6, 2><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
-        static_cast<const bf16_t*>(y_routed), static_cast<const bf16_t*>(y_shared), gates,
-        pair_pos, s.T, s.d, nchunk, static_cast<bf16_t*>(y));
-  } else {
-    const int nchunk = (s.d + 256 * 4 - 1) / (256 * 4);
-    const long long blocks = static_cast<long long>(s.T) * nchunk;
-    combine_kernel<float, 6, 2><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
-        static_cast<const float*>(y_routed), static_cast<const float*>(y_shared), gates,
-        pair_pos, s.T, s.d, nchunk, static_cast<float*>(y));
-  }
+  if (s.bf16) run_combine_s<bf16_t>(s, y_routed, y_shared, gates, pair_pos, y, st);
+  else run_combine_s<float>(s, y_routed, y_shared, gates, pair_pos, y, st);
   return hipGetLastError();
 }
 

@@ -25,14 +25,24 @@ moe_status check_desc(const moe_desc* d) {
   if (d->gate_norm != MOE_GATE_RATIO && d->gate_norm != MOE_GATE_LOGSUMEXP) return MOE_ERR_SHAPE;
   if (!(d->gate_scale > 0.0f) || !(d->gate_scale < INFINITY)) return MOE_ERR_SHAPE;
   if (!(d->capacity_factor >= 0.0f) || !(d->capacity_factor < INFINITY)) return MOE_ERR_SHAPE;
-  if (d->E != 256 || d->S != 2 || d->k != 6) return MOE_ERR_UNSUPPORTED;
-  if (d->d % 256 != 0 || d->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((d->E != 64 && d->E != 128 && d->E != 256) || d->S > 2 || d->k != 6)
+    return MOE_ERR_UNSUPPORTED;
+  if (d->d % 32 != 0) return MOE_ERR_UNSUPPORTED;
   const long long T = d->T;
   if (T * d->k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
   const long long wide = d->d > d->F ? d->d : d->F;
   if (T * (d->k + d->S) * wide >= (1LL << 40)) return MOE_ERR_UNSUPPORTED;
   // FP4 routed weights: decode batches (the 32-row GEMM path) only
   if (fp4 && T * d->k >= 48LL * d->E) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// The expert GEMMs' tiles need d % 256 == 0 and F % 128 == 0 (the router,
+// dispatch, combine and bias update only d % 32 == 0).
+moe_status check_ffn_desc(const moe_desc* d) {
+  const moe_status st = check_desc(d);
+  if (st != MOE_OK) return st;
+  if (d->d % 256 != 0 || d->F % 128 != 0) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -147,8 +157,8 @@ moe_status check_ws(const Shape& s, moe_call call, const void* ws, size_t ws_byt
 moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 bool weights_ok(const moe_weights* w, const Shape& s) {
-  if (!(w && w->w_gate && w->w_up && w->w_down && w->ws_gate && w->ws_up && w->ws_down))
-    return false;
+  if (!(w && w->w_gate && w->w_up && w->w_down)) return false;
+  if (s.S > 0 && !(w->ws_gate && w->ws_up && w->ws_down)) return false;
   return !s.w_fp4 || (w->sc_gate && w->sc_up && w->sc_down);
 }
 
@@ -173,9 +183,11 @@ const char* moe_status_string(moe_status st) {
 
 moe_status moe_workspace_size(const moe_desc* desc, moe_call call, size_t* bytes) {
   if (!bytes) return MOE_ERR_NULL;
-  const moe_status st = check_desc(desc);
+  if (call < MOE_CALL_ROUTER || call > MOE_CALL_FORWARD) return desc ? MOE_ERR_SHAPE : MOE_ERR_NULL;
+  const bool ffn = call == MOE_CALL_GATE_UP || call == MOE_CALL_DOWN ||
+                   call == MOE_CALL_EXPERT_FFN || call == MOE_CALL_FORWARD;
+  const moe_status st = ffn ? check_ffn_desc(desc) : check_desc(desc);
   if (st != MOE_OK) return st;
-  if (call < MOE_CALL_ROUTER || call > MOE_CALL_FORWARD) return MOE_ERR_SHAPE;
   *bytes = ws_bytes_for(to_shape(desc), call);
   return MOE_OK;
 }
@@ -212,7 +224,7 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* 
 moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_weights* w,
                               const int32_t* offsets, const int32_t* sorted_pair, void* h,
                               void* ws, size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_desc(desc);
+  moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !offsets) return MOE_ERR_NULL;
@@ -232,11 +244,11 @@ moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_wei
 moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w, const int32_t* offsets,
                            const void* h, void* y_routed, void* y_shared, void* ws,
                            size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_desc(desc);
+  moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !offsets) return MOE_ERR_NULL;
-  if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
+  if (s.T > 0 && (!h || !y_routed || (s.S > 0 && !y_shared))) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
@@ -252,7 +264,7 @@ moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x, const 
                                      const int32_t* offsets, const int32_t* sorted_pair, void* h,
                                      void* ws, size_t ws_bytes, hipEvent_t* marks,
                                      hipStream_t stream) {
-  moe_status st = check_desc(desc);
+  moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !offsets || !marks || !marks[0] || !marks[1])
@@ -275,12 +287,12 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
                                   const int32_t* offsets, const void* h, void* y_routed,
                                   void* y_shared, void* ws, size_t ws_bytes, hipEvent_t* marks,
                                   hipStream_t stream) {
-  moe_status st = check_desc(desc);
+  moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !offsets || !marks || !marks[0] || !marks[1])
     return MOE_ERR_NULL;
-  if (s.T > 0 && (!h || !y_routed || !y_shared)) return MOE_ERR_NULL;
+  if (s.T > 0 && (!h || !y_routed || (s.S > 0 && !y_shared))) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
@@ -296,11 +308,12 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
 moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const moe_weights* w,
                           const int32_t* offsets, const int32_t* sorted_pair, void* y_routed,
                           void* y_shared, void* ws, size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_desc(desc);
+  moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !offsets) return MOE_ERR_NULL;
-  if (s.T > 0 && (!x || !sorted_pair || !y_routed || !y_shared)) return MOE_ERR_NULL;
+  if (s.T > 0 && (!x || !sorted_pair || !y_routed || (s.S > 0 && !y_shared)))
+    return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_EXPERT_FFN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
@@ -323,7 +336,8 @@ moe_status moe_combine(const moe_desc* desc, const void* y_routed, const void* y
   const moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
-  if (s.T > 0 && (!y_routed || !y_shared || !gates || !pair_pos || !y)) return MOE_ERR_NULL;
+  if (s.T > 0 && (!y_routed || (s.S > 0 && !y_shared) || !gates || !pair_pos || !y))
+    return MOE_ERR_NULL;
   return hip_status(launch_combine(s, y_routed, y_shared, gates, pair_pos, y, stream));
 }
 
@@ -349,7 +363,7 @@ moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w, ui
 moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
                        float gamma, void* y, const moe_routing* routing, void* ws,
                        size_t ws_bytes, hipStream_t stream) {
-  moe_status st = check_desc(desc);
+  moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !w->w_router || !bias) return MOE_ERR_NULL;

@@ -90,11 +90,10 @@ __device__ __forceinline__ void router_load_x(const void* __restrict__ xv, const
 template <int NXP>
 __global__ __launch_bounds__(256) void router_logits(
     const void* __restrict__ xv, const bf16_t* __restrict__ planes, int T, int d, int npad,
-    int nks, double* __restrict__ partial) {
+    int nks, int chunk, double* __restrict__ partial) {
   constexpr int KS = 32;
   constexpr int LDSW = KS + 8;
-  constexpr int STEPS_PER_CHUNK = kRouterChunk / KS;
-  static_assert(kRouterChunk % KS == 0, "chunk must hold whole K steps");
+  const int steps_per_chunk = chunk / KS;
   __shared__ __attribute__((aligned(16))) bf16_t sB[2][3][64][LDSW];
 
   const int tid = threadIdx.x;
@@ -104,11 +103,11 @@ __global__ __launch_bounds__(256) void router_logits(
   const int tok0 = blockIdx.x * 128 + wm * 64;
   const int col0 = blockIdx.y * 64;
 
-  const int nch = d / kRouterChunk;
+  const int nch = d / chunk;
   const int ch_b = static_cast<int>(static_cast<long long>(blockIdx.z) * nch / nks);
   const int ch_e = static_cast<int>(static_cast<long long>(blockIdx.z + 1) * nch / nks);
-  const int kbeg = ch_b * kRouterChunk;
-  const int nsteps = (ch_e - ch_b) * STEPS_PER_CHUNK;
+  const int kbeg = ch_b * chunk;
+  const int nsteps = (ch_e - ch_b) * steps_per_chunk;
 
   // B staging: each thread moves the same 16-byte chunk of the 3 planes.
   const size_t pstride = static_cast<size_t>(npad) * d;
@@ -219,12 +218,12 @@ constexpr int kRouterStageElems = (128 + 3 * 64) * 32;  // x rows, then 3 planes
 
 __global__ __launch_bounds__(256) void router_logits_bf16(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, int T, int d, int npad,
-    int nks, double* __restrict__ partial) {
+    int nks, int chunk, double* __restrict__ partial) {
   constexpr int KS = 32;
   constexpr int RS = kRouterRing;
   constexpr int SE = kRouterStageElems;
   constexpr int LPW = 5;  // 1 KiB loads per wave per stage: 8 for x, 12 for the planes
-  constexpr int STEPS_PER_CHUNK = kRouterChunk / KS;
+  const int steps_per_chunk = chunk / KS;
   __shared__ __attribute__((aligned(1024))) bf16_t ring[RS * SE];
 
   const int tid = threadIdx.x;
@@ -234,11 +233,11 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
   const int tok0 = blockIdx.x * 128;
   const int col0 = blockIdx.y * 64;
 
-  const int nch = d / kRouterChunk;
+  const int nch = d / chunk;
   const int ch_b = static_cast<int>(static_cast<long long>(blockIdx.z) * nch / nks);
   const int ch_e = static_cast<int>(static_cast<long long>(blockIdx.z + 1) * nch / nks);
-  const int kbeg = ch_b * kRouterChunk;
-  const int nsteps = (ch_e - ch_b) * STEPS_PER_CHUNK;
+  const int kbeg = ch_b * chunk;
+  const int nsteps = (ch_e - ch_b) * steps_per_chunk;
 
   // load j (16 LDS rows) of a stage: j < 8 x rows 16j.., else plane
   // (j - 8) / 4, rows 16 ((j - 8) % 4)..; lane l fills slot l % 4 of row
@@ -251,15 +250,15 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
 #pragma unroll
   for (int q = 0; q < LPW; ++q) {
     const int j = wave * LPW + q;
-    const int chunk = (cbase ^ ((j & 1) << 1)) * 8;
+    const int cofs = (cbase ^ ((j & 1) << 1)) * 8;
     if (j < 8) {
       int r = tok0 + j * 16 + lrow;
       r = r < T ? r : T - 1;
-      src[q] = x + static_cast<size_t>(r) * d + kbeg + chunk;
+      src[q] = x + static_cast<size_t>(r) * d + kbeg + cofs;
     } else {
       const int jb = j - 8;
       src[q] = planes + (jb >> 2) * pstride +
-               static_cast<size_t>(col0 + (jb & 3) * 16 + lrow) * d + kbeg + chunk;
+               static_cast<size_t>(col0 + (jb & 3) * 16 + lrow) * d + kbeg + cofs;
     }
     dst_off[q] = static_cast<uint32_t>(j * 512 * sizeof(bf16_t));
   }
@@ -344,11 +343,11 @@ __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// One wave per token.  E = 256: lane l owns routed experts l, l+64, l+128,
-// l+192; lanes 0..S-1 also own the shared experts E+lane.  K routed picks in
+// One wave per token.  E = 64 * EPL: lane l owns routed experts l, l+64,
+// ...; lanes 0..S-1 also own the shared experts E+lane.  K routed picks in
 // rank order (descending key, exact ties to the lower id), then one more
 // round for the first expert left out (the margin).
-template <int K, int S>
+template <int K, int S, int EPL>
 __global__ __launch_bounds__(256) void router_select(
     const double* __restrict__ partial, int nks, int T, int npad, int E,
     const float* __restrict__ bias, int32_t* __restrict__ topk, float* __restrict__ gates,
@@ -357,10 +356,10 @@ __global__ __launch_bounds__(256) void router_select(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together; no block barrier below
 
-  double sv[4], zv[4], key[4];
-  bool taken[4];
+  double sv[EPL], zv[EPL], key[EPL];
+  bool taken[EPL];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
+  for (int q = 0; q < EPL; ++q) {
     const int c = lane + 64 * q;
     double z = 0.0;
     for (int ks = 0; ks < nks; ++ks) z += partial[(static_cast<size_t>(ks) * T + t) * npad + c];
@@ -387,7 +386,7 @@ __global__ __launch_bounds__(256) void router_select(
     double bk = -INFINITY;
     int bi = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < EPL; ++q) {
       const int c = lane + 64 * q;
       if (!taken[q] && better(key[q], c, bk, bi)) {
         bk = key[q];
@@ -409,19 +408,16 @@ __global__ __launch_bounds__(256) void router_select(
       const int q = bi >> 6;
       const int owner = bi & 63;
       double my = sv[0], mz = zv[0];
-      my = q == 1 ? sv[1] : my;
-      my = q == 2 ? sv[2] : my;
-      my = q == 3 ? sv[3] : my;
-      mz = q == 1 ? zv[1] : mz;
-      mz = q == 2 ? zv[2] : mz;
-      mz = q == 3 ? zv[3] : mz;
+#pragma unroll
+      for (int qq = 1; qq < EPL; ++qq) {
+        my = q == qq ? sv[qq] : my;
+        mz = q == qq ? zv[qq] : mz;
+      }
       s_sel[r] = __shfl(my, owner);
       z_sel[r] = __shfl(mz, owner);
       if (lane == owner) {
-        taken[0] = taken[0] || q == 0;
-        taken[1] = taken[1] || q == 1;
-        taken[2] = taken[2] || q == 2;
-        taken[3] = taken[3] || q == 3;
+#pragma unroll
+        for (int qq = 0; qq < EPL; ++qq) taken[qq] = taken[qq] || q == qq;
       }
       i_sel[r] = bi;
       k_last = bk;
@@ -474,12 +470,32 @@ __global__ __launch_bounds__(256) void router_select(
 
 // ------------------------------------------------------------------ host
 
+int router_chunk(const Shape& s) { return s.d % kRouterChunk == 0 ? kRouterChunk : 32; }
+
 int router_ksplits(const Shape& s) {
   const int tiles = ((s.T + 127) / 128) * (router_cols_padded(s) / kRouterColTile);
-  const int nch = s.d / kRouterChunk;
+  const int nch = s.d / router_chunk(s);
   int want = (1280 + tiles - 1) / (tiles > 0 ? tiles : 1);  // ~2.5 waves of 2 workgroups per CU
   if (want < 1) want = 1;
   return want < nch ? want : nch;
+}
+
+template <int S, int EPL>
+static void launch_select(const Shape& s, const double* partial, int nks, int npad,
+                          const float* bias, int32_t* topk_idx, float* gates, float* margin,
+                          hipStream_t st) {
+  router_select<6, S, EPL><<<(s.T + 3) / 4, 256, 0, st>>>(partial, nks, s.T, npad, s.E, bias,
+                                                          topk_idx, gates, margin,
+                                                          s.gate_logsumexp, s.gate_scale);
+}
+
+template <int S>
+static void launch_select_e(const Shape& s, const double* partial, int nks, int npad,
+                            const float* bias, int32_t* topk_idx, float* gates, float* margin,
+                            hipStream_t st) {
+  if (s.E == 64) launch_select<S, 1>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
+  else if (s.E == 128) launch_select<S, 2>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
+  else launch_select<S, 4>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
 }
 
 hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
@@ -492,15 +508,16 @@ hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
   if (blocks > 4096) blocks = 4096;
   router_split_planes<<<blocks, 256, 0, st>>>(w_router, s.E + s.S, s.d, npad, wplanes);
   const int nks = router_ksplits(s);
+  const int chunk = router_chunk(s);
   dim3 grid((s.T + 127) / 128, npad / kRouterColTile, nks);
   if (s.bf16)
     router_logits_bf16<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), wplanes, s.T, s.d,
-                                              npad, nks, partial);
+                                              npad, nks, chunk, partial);
   else
-    router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, partial);
-  router_select<6, 2><<<(s.T + 3) / 4, 256, 0, st>>>(partial, nks, s.T, npad, s.E, bias,
-                                                      topk_idx, gates, margin,
-                                                      s.gate_logsumexp, s.gate_scale);
+    router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, chunk, partial);
+  if (s.S == 0) launch_select_e<0>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
+  else if (s.S == 1) launch_select_e<1>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
+  else launch_select_e<2>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
   return hipGetLastError();
 }
 

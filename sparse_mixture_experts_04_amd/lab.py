@@ -1,0 +1,76 @@
+"""Router Balance Lab on the GPU ("Inkling, Dissected", 02g).
+
+A frozen router, one fresh batch per step, a hard capacity per expert and
+the selection-only bias of 02e: each step is moe_router -> moe_dispatch
+(capacity-limited) -> moe_bias_update through the C ABI, on buffers
+allocated once.  The lab's measures are taken on the step's outputs:
+
+* MaxVio: the hottest expert's demand over the ideal load k*T/E, minus 1;
+* drop rate: the fraction of the k*T expert slots dropped at capacity;
+* layer quality: the gate-weighted affinity of the surviving pairs
+  (g_j = s_j over the sum of s over the token's picks, a dropped pair
+  contributing nothing) over that of the unbiased, uncapacitated top-k,
+  summed over the batch.
+
+The measures read the affinities s = sigmoid(x . w_i) in float64 with torch
+on the device; they are bookkeeping around the step, never part of it.
+"""
+import torch
+
+from . import _lib as L
+
+
+class BalanceLab:
+    """Buffers and calls of the lab's routing step for one workload."""
+
+    def __init__(self, cfg, w_router, gamma, device, capacity_factor=None):
+        if cfg.S != 0:
+            raise ValueError("the balance lab has no shared experts")
+        cf = cfg.capacity_factor if capacity_factor is None else capacity_factor
+        self.cfg = cfg
+        self.gamma = float(gamma)
+        self.desc = L.make_desc(cfg.T, cfg.d, cfg.F, torch.float32, E=cfg.E, S=0, k=cfg.k,
+                                capacity_factor=cf)
+        T, E, k = cfg.T, cfg.E, cfg.k
+        i32, f32 = torch.int32, torch.float32
+        self.w_router = w_router
+        self.bias = torch.zeros(E, dtype=f32, device=device)
+        self.topk = torch.empty((T, k), dtype=i32, device=device)
+        self.gates = torch.empty((T, k), dtype=f32, device=device)
+        self.counts = torch.empty(E, dtype=i32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=device)
+        self.sorted_pair = torch.empty(T * k, dtype=i32, device=device)
+        self.pair_pos = torch.empty(T * k, dtype=i32, device=device)
+        self.ws_router = L.alloc_workspace(self.desc, L.CALL_ROUTER, device)
+        self.ws_dispatch = L.alloc_workspace(self.desc, L.CALL_DISPATCH, device)
+        self.w64 = w_router.to(torch.float64)
+
+    def reset(self, bias=None):
+        if bias is None:
+            self.bias.zero_()
+        else:
+            self.bias.copy_(bias)
+
+    def step(self, x):
+        """Route x with the current bias, dispatch under capacity, then move
+        the bias by gamma against this step's demand."""
+        L.router(self.desc, x, self.w_router, self.bias, self.topk, self.gates,
+                 ws=self.ws_router)
+        L.dispatch(self.desc, self.topk, self.counts, self.offsets, self.sorted_pair,
+                   self.pair_pos, ws=self.ws_dispatch)
+        L.bias_update(self.desc, self.counts, self.gamma, self.bias)
+
+    def measures(self, x):
+        """(max_vio, drop_rate, quality) of the last step on tokens x, as
+        float64 device scalars (no host synchronisation)."""
+        T, E, k = self.cfg.T, self.cfg.E, self.cfg.k
+        slots = float(k * T)
+        max_vio = self.counts.max().to(torch.float64) * (E / slots) - 1.0
+        kept = (self.pair_pos >= 0).view(T, k)
+        drop_rate = 1.0 - kept.sum().to(torch.float64) / slots
+        s = torch.sigmoid(x.to(torch.float64) @ self.w64.T)
+        sel = torch.gather(s, 1, self.topk.long())
+        captured = (self.gates.to(torch.float64) * sel * kept).sum()   # the router's own gates
+        best = torch.topk(s, k, dim=1).values
+        oracle = (best * best / best.sum(dim=1, keepdim=True)).sum()
+        return torch.stack([max_vio, drop_rate, captured / oracle])

@@ -20,6 +20,15 @@ stream and the result does not depend on generation order):
   ``u`` a seeded unit vector, ``c_i = kappa * r_i ** -s`` with ``r_i`` a seeded
   permutation of the ranks 1..E.
 
+* balance-lab workloads (``lab_head_tail > 0``): E home directions
+  ``c_j`` (rows N(0, I) scaled to unit length), router ``w_router =
+  lab_kappa * c`` (routed rows only); each step's tokens pick a home
+  cluster j with probability proportional to ``(j + 1) ** -a``,
+  ``a = ln(lab_head_tail) / ln(E)`` (so expert 0's cluster is
+  ``lab_head_tail`` times as common as expert E-1's), and
+  ``x_t = c_j + lab_jitter * N(0, I / d)``.  Drawn on the CPU (the same
+  values whatever the device), then moved.
+
 Values are drawn in fp32 and rounded to nearest-even into bf16 where the
 workload is bf16.  N(0, v) means variance v.
 """
@@ -117,3 +126,27 @@ def make_inputs(cfg: MoEConfig, device="cpu"):
            "bias": make_bias(cfg, device)}
     inp.update(make_expert_weights(cfg, device))
     return inp
+
+
+def lab_directions(cfg: MoEConfig):
+    g = _gen("cpu", cfg.name, "lab_home")
+    c = torch.randn((cfg.E, cfg.d), generator=g, dtype=torch.float64)
+    return c / c.norm(dim=1, keepdim=True)
+
+
+def make_lab_router(cfg: MoEConfig, device="cpu"):
+    """Frozen router of a balance-lab workload: [E, d] fp32."""
+    return (cfg.lab_kappa * lab_directions(cfg)).to(torch.float32).to(device)
+
+
+def make_lab_x(cfg: MoEConfig, step: int, device="cpu", T: int = None):
+    """Tokens of step ``step`` of a balance-lab workload: [T, d] fp32."""
+    T = cfg.T if T is None else T
+    c = lab_directions(cfg)
+    a = math.log(cfg.lab_head_tail) / math.log(cfg.E)
+    p = torch.arange(1, cfg.E + 1, dtype=torch.float64).pow(-a)
+    g = _gen("cpu", cfg.name, "lab_tokens", step)
+    home = torch.multinomial(p, T, replacement=True, generator=g)
+    noise = torch.randn((T, cfg.d), generator=g, dtype=torch.float64)
+    x = c[home] + noise * (cfg.lab_jitter / math.sqrt(cfg.d))
+    return x.to(torch.float32).to(device)

@@ -35,7 +35,7 @@ def npi(t):
 
 def desc_for(cfg, T=None):
     return L.make_desc(cfg.T if T is None else T, cfg.d, cfg.F, synth.act_dtype(cfg),
-                       gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale,
+                       E=cfg.E, S=cfg.S, k=cfg.k, gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale,
                        capacity_factor=cfg.capacity_factor, fp4_weights=cfg.fp4_weights)
 
 

@@ -53,8 +53,9 @@ def ws_size(d, call):
 @pytest.mark.parametrize("kw,code", [
     (dict(T=-1), 2), (dict(d=0), 2), (dict(k=0), 2),
     (dict(act=L.BF16), 3), (dict(act=7, weight=7), 3),
-    (dict(E=128), 5), (dict(S=1), 5), (dict(k=8), 5),
-    (dict(d=384), 5), (dict(F=96), 5),
+    (dict(E=128), 0), (dict(E=64, S=0), 0), (dict(S=1), 0),
+    (dict(E=96), 5), (dict(E=512), 5), (dict(S=3), 5), (dict(k=8), 5),
+    (dict(d=384), 5), (dict(F=96), 5), (dict(d=48), 5),
     (dict(T=1 << 29), 5),
     (dict(gate_norm=2), 2), (dict(gate_norm=-1), 2), (dict(gate_scale=0.0), 2),
     (dict(gate_scale=-8.0), 2), (dict(gate_scale=float("inf")), 2),
@@ -69,6 +70,20 @@ def ws_size(d, call):
 def test_desc_validation(kw, code):
     st, _ = ws_size(desc(**kw), L.CALL_FORWARD)
     assert st == code
+
+
+def test_routing_calls_accept_narrow_embeddings():
+    """The router, dispatch, combine and bias update need d % 32 == 0; the
+    expert GEMMs d % 256 == 0 and F % 128 == 0."""
+    d = desc(E=64, S=0, d=32, F=96, T=2048, capacity_factor=1.25)
+    for call in (L.CALL_ROUTER, L.CALL_DISPATCH, L.CALL_COMBINE, L.CALL_BIAS_UPDATE):
+        assert ws_size(d, call)[0] == 0
+    for call in (L.CALL_GATE_UP, L.CALL_DOWN, L.CALL_EXPERT_FFN, L.CALL_FORWARD):
+        assert ws_size(d, call)[0] == 5
+    # no shared experts: y_shared may be NULL; a NULL routed output still fails
+    P = ctypes.c_void_p(0x1000)
+    assert lib.moe_combine(ctypes.byref(d), P, None, P, P, None, None) == 1
+    assert lib.moe_combine(ctypes.byref(d), None, None, P, P, P, None) == 1
 
 
 def test_null_desc_and_null_out():

@@ -1,0 +1,122 @@
+"""GPU parity of the Router Balance Lab workload ("Inkling, Dissected",
+02g) and of the routing entry points at narrow embeddings.
+
+The lab's step is moe_router -> moe_dispatch (capacity 1.25x) ->
+moe_bias_update at 64 routed experts, no shared experts, d = 32.  Every
+step is checked against the oracle fed the bias the GPU routed with
+(selection outside near-ties, gates, dispatch, the bias bit for bit, and the
+lab's measures); the whole GPU trajectory is then checked against the
+oracle's own, independent trajectory.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe_oracle as O
+from sparse_mixture_experts_04_amd import _lib as L
+from sparse_mixture_experts_04_amd import configs, synth
+from sparse_mixture_experts_04_amd.configs import MoEConfig
+from sparse_mixture_experts_04_amd.lab import BalanceLab
+
+from parity_util import (Buffers, check_bias, check_dispatch, check_routing, log, np64, npi)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+@pytest.mark.parametrize("gamma,steps", [(0.01, 100), (0.0, 12), (0.05, 30)])
+def test_balance_lab_trajectory(gamma, steps):
+    cfg = configs.get("Lab")
+    T, E, k = cfg.T, cfg.E, cfg.k
+    log(f"[lab] gamma={gamma} steps={steps}: {cfg.describe()} cap {cfg.capacity_factor}")
+    w = synth.make_lab_router(cfg)
+    w64 = w.numpy().astype(np.float64)
+    xs = [synth.make_lab_x(cfg, i) for i in range(steps)]
+    lab = BalanceLab(cfg, w.to(DEV), gamma, DEV)
+    cap = O.capacity(cfg.capacity_factor, k, T, E)
+    flips = 0
+    gpu = []
+    for i in range(steps):
+        x = xs[i].to(DEV)
+        b_in = lab.bias.clone()
+        lab.step(x)
+        m = lab.measures(x).cpu().numpy()
+        topk = npi(lab.topk)
+        r, _, st = check_routing(np64(xs[i]), w64, np64(b_in), topk, np64(lab.gates), k=k)
+        flips += st["exempt_differ"]
+        dp = check_dispatch(topk, lab, E=E, cap=cap)
+        check_bias(npi(lab.counts), gamma, b_in, lab.bias, T, k)
+        ref = O.load_metrics(dp["counts"], dp["kept"], k, T)
+        q = O.layer_quality(r["s"], topk, dp["pair_pos"], k)
+        assert abs(m[0] - ref["max_vio"]) <= 1e-12 and abs(m[1] - ref["drop_rate"]) <= 1e-12
+        assert abs(m[2] - q) <= 1e-6, (m[2], q)
+        gpu.append((b_in.cpu().numpy(), m))
+    orc = O.balance_lab(lambda i: xs[i].numpy(), w64, np.zeros(E, np.float32), gamma,
+                        cfg.capacity_factor, steps, k=k)
+    mean_gpu = np.mean([g[1] for g in gpu], axis=0)
+    mean_orc = np.array([np.mean([o[key] for o in orc])
+                         for key in ("max_vio", "drop_rate", "quality")])
+    log(f"  near-tie flips {flips}; mean MaxVio/drop/quality gpu {np.round(mean_gpu, 4)} "
+        f"oracle {np.round(mean_orc, 4)}")
+    if flips == 0:
+        # no legitimate near-tie went the other way: the trajectories agree
+        for (b_gpu, m), o in zip(gpu, orc):
+            assert np.array_equal(b_gpu.view(np.uint32), o["bias"].view(np.uint32))
+            assert abs(m[2] - o["quality"]) <= 1e-6
+    else:
+        assert np.all(np.abs(mean_gpu - mean_orc) <= [0.02, 0.002, 0.002])
+
+
+ROUTING_ONLY = {
+    # d % 32 == 0 but not 256: the router splits K in 32-wide chunks
+    "e64_s0_d32_bf16": MoEConfig("e64_s0_d32_bf16", T=333, d=32, F=128, E=64, S=0,
+                                 act="bf16", bias_range=0.05, capacity_factor=1.25),
+    "e128_s1_d96_f32": MoEConfig("e128_s1_d96_f32", T=517, d=96, F=128, E=128, S=1,
+                                 act="f32", bias_range=0.1),
+    "e64_s2_d160_lse": MoEConfig("e64_s2_d160_lse", T=1000, d=160, F=128, E=64, S=2,
+                                 act="bf16", bias_range=0.05, gate_norm="logsumexp",
+                                 gate_scale=3.0, capacity_factor=1.0),
+    "e256_s2_d288_f32": MoEConfig("e256_s2_d288_f32", T=130, d=288, F=128, act="f32",
+                                  bias_range=0.1),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTING_ONLY))
+def test_routing_entry_points_narrow_d(name):
+    """Router, dispatch, combine (on seeded expert outputs) and the bias
+    update at embeddings the expert GEMMs do not take."""
+    cfg = ROUTING_ONLY[name]
+    log(f"[routing] {name}: {cfg.describe()}")
+    T, E, S, k, d = cfg.T, cfg.E, cfg.S, cfg.k, cfg.d
+    act = synth.act_dtype(cfg)
+    desc = L.make_desc(T, d, cfg.F, act, E=E, S=S, k=k, gate_norm=cfg.gate_norm,
+                       gate_scale=cfg.gate_scale, capacity_factor=cfg.capacity_factor)
+    x = synth.make_x(cfg).to(DEV)
+    w = synth.make_router(cfg).to(DEV)
+    bias0 = synth.make_bias(cfg).to(DEV)
+    b = Buffers(desc, DEV)
+    b.y_routed = synth.normal((T * k, d), 1.0, DEV, cfg.name, "y_routed", 0, act)
+    b.y_shared = synth.normal((S, T, d), 1.0, DEV, cfg.name, "y_shared", 0, act)
+    bias = bias0.clone()
+    L.router(desc, x, w, bias, b.topk, b.gates, b.margin)
+    L.dispatch(desc, b.topk, b.counts, b.offsets, b.sorted_pair, b.pair_pos)
+    L.combine(desc, b.y_routed, b.y_shared, b.gates, b.pair_pos, b.y)
+    L.bias_update(desc, b.counts, cfg.gamma, bias)
+    torch.cuda.synchronize()
+    topk = npi(b.topk)
+    _, _, st = check_routing(np64(x), np64(w), np64(bias0), topk, np64(b.gates), k=k,
+                             gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
+    cap = O.capacity(cfg.capacity_factor, k, T, E)
+    dp = check_dispatch(topk, b, E=E, cap=cap)
+    check_bias(npi(b.counts), cfg.gamma, bias0, bias, T, k)
+    # combine on the GPU's own gates and expert rows, element by element:
+    # fp32 accumulation, then one rounding to the output dtype
+    yr, ys, g = np64(b.y_routed), np64(b.y_shared), np64(b.gates)
+    ref = O.combine(yr, ys, g, dp["pair_pos"], k)
+    mag = O.combine(np.abs(yr), np.abs(ys), np.abs(g), dp["pair_pos"], k)
+    got = np64(b.y)
+    ulp = 2.0 ** -8 if act == torch.bfloat16 else 0.0
+    err = np.abs(got - ref) - (ulp * np.abs(ref) + 1e-6 * mag)
+    log(f"  routing {st}; dropped {int(T * k - dp['offsets'][-1])} pairs")
+    assert np.all(err <= 0.0), float(err.max())

@@ -314,6 +314,75 @@ def test_capacity_value_and_load_metrics():
     assert m["max_vio"] == 1.0 and m["drop_rate"] == 3 / 16
 
 
+def test_layer_quality_hand_example():
+    """02g's quality: gate-weighted affinity of the surviving pairs over the
+    unbiased, uncapacitated top-k's, summed over the batch.  One token with
+    s = (0.8, 0.6, 0.2), k = 2: the unbiased pick {0, 1} captures
+    (0.64 + 0.36) / 1.4 = 1/1.4."""
+    s = np.array([[0.8, 0.6, 0.2]])
+    ref = 1.0 / 1.4
+    # bias swapped expert 1 for 2, nothing dropped: (0.64 + 0.04) / 1.0
+    assert abs(O.layer_quality(s, [[0, 2]], [0, 1], k=2) - 0.68 / ref) < 1e-15
+    # expert 2's pair dropped: its share is lost, expert 0's gate stays 0.8
+    assert abs(O.layer_quality(s, [[0, 2]], [0, -1], k=2) - 0.64 / ref) < 1e-15
+    # unbiased pick with expert 0 dropped: only 0.6 * 0.6 / 1.4 survives
+    assert abs(O.layer_quality(s, [[0, 1]], [-1, 0], k=2) - 0.36) < 1e-15
+    # slot order does not matter
+    assert abs(O.layer_quality(s, [[2, 0]], [1, 0], k=2) - 0.68 / ref) < 1e-15
+    # a batch is a ratio of sums, not a mean of ratios: a second token with
+    # equal affinities 0.5 captures 0.5 whatever it picks
+    s2 = np.array([[0.8, 0.6, 0.2], [0.5, 0.5, 0.5]])
+    q = O.layer_quality(s2, [[0, 2], [1, 2]], [0, 1, 2, 3], k=2)
+    assert abs(q - (0.68 + 0.5) / (ref + 0.5)) < 1e-15
+
+
+def test_layer_quality_limits():
+    rng = np.random.default_rng(5)
+    s = rng.uniform(0.05, 0.95, size=(300, 64))
+    top, _ = O.select_topk(s, 6)
+    # unbiased and nothing dropped: exactly the oracle
+    assert O.layer_quality(s, top, np.arange(300 * 6), k=6) == 1.0
+    # everything dropped: nothing captured
+    assert O.layer_quality(s, top, np.full(300 * 6, -1), k=6) == 0.0
+    # dropping pairs of the unbiased selection only loses what they carried
+    pp = np.arange(300 * 6)
+    pp[::7] = -1
+    q = O.layer_quality(s, top, pp, k=6)
+    assert 0.8 < q < 0.9
+
+
+def test_balance_lab_two_step_toy():
+    """Four experts, k = 2, four identical tokens, capacity 1.0 x ideal
+    (C = 2): step 0 piles every token on experts 0 and 1 (MaxVio 1, half
+    the slots dropped, tokens 2 and 3 lose both pairs); the bias then moves
+    by gamma = 0.3 against the load and step 1 picks experts 2 and 0."""
+    E, k, T = 4, 2, 4
+    z = np.array([2.0, 1.9, 0.0, -1.0])
+    x = np.tile(z, (T, 1))
+    w = np.eye(E)
+    recs = O.balance_lab(lambda i: x, w, np.zeros(E, np.float32), 0.3, 1.0, 2, k=k)
+    sg = [1.0 / (1.0 + math.exp(-v)) for v in z]
+    # step 0
+    r0 = recs[0]
+    assert np.array_equal(r0["counts"], [4, 4, 0, 0])
+    assert r0["max_vio"] == 1.0 and r0["drop_rate"] == 0.5
+    assert np.array_equal(r0["topk_idx"], np.tile([0, 1], (T, 1)))
+    assert abs(r0["quality"] - 0.5) < 1e-15
+    # step 1: keys s - 0.3, s - 0.3, s + 0.3, s + 0.3
+    r1 = recs[1]
+    assert np.array_equal(r1["bias"], np.float32([-0.3, -0.3, 0.3, 0.3]))
+    assert np.array_equal(r1["topk_idx"], np.tile([2, 0], (T, 1)))
+    assert np.array_equal(r1["counts"], [4, 0, 4, 0])
+    assert r1["max_vio"] == 1.0 and r1["drop_rate"] == 0.5
+    got = (sg[2] ** 2 + sg[0] ** 2) / (sg[2] + sg[0])
+    best = (sg[0] ** 2 + sg[1] ** 2) / (sg[0] + sg[1])
+    assert abs(r1["quality"] - 2 * got / (4 * best)) < 1e-14
+    # without a bias step the trajectory stands still
+    still = O.balance_lab(lambda i: x, w, np.zeros(E, np.float32), 0.0, 1.0, 3, k=k)
+    assert all(np.array_equal(r["counts"], [4, 4, 0, 0]) for r in still)
+    assert all(not r["bias"].any() for r in still)
+
+
 def test_combine_skips_dropped_slots():
     rng = np.random.default_rng(12)
     T, k, d = 5, 3, 4

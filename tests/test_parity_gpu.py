@@ -43,6 +43,16 @@ SMALL = {
                                bias_range=0.0, skew_kappa=8.0, capacity_factor=1.25),
     "f32_cap": MoEConfig("f32_cap", T=128, d=512, F=128, act="f32", bias_range=0.1,
                          wd_std_from_F=True, capacity_factor=0.75),
+    # other expert counts: 64 or 128 routed experts, 0 to 2 shared
+    "e64_s0": MoEConfig("e64_s0", T=256, d=256, F=128, E=64, S=0, act="bf16",
+                        bias_range=0.05),
+    "e128_s1_big": MoEConfig("e128_s1_big", T=2048, d=256, F=256, E=128, S=1, act="bf16",
+                             bias_range=0.05),
+    "e64_s2_f32_cap": MoEConfig("e64_s2_f32_cap", T=200, d=256, F=128, E=64, S=2, act="f32",
+                                bias_range=0.1, wd_std_from_F=True, capacity_factor=1.0),
+    "e128_s0_lse_cap": MoEConfig("e128_s0_lse_cap", T=1200, d=512, F=128, E=128, S=0,
+                                 act="bf16", bias_range=0.05, gate_norm="logsumexp",
+                                 gate_scale=2.5, capacity_factor=1.25),
 }
 
 
@@ -67,7 +77,7 @@ def test_full_parity_stagewise(name):
     r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates),
                                  gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
     log(f"  routing {st}")
-    dp = check_dispatch(topk, b, cap=cap_for(cfg))
+    dp = check_dispatch(topk, b, E=cfg.E, cap=cap_for(cfg))
     if cfg.capacity_factor:
         m = O.load_metrics(dp["counts"], dp["kept"], cfg.k, cfg.T)
         log(f"  capacity {cap_for(cfg)}: MaxVio {m['max_vio']:.2f}, dropped {m['drop_rate']:.3f}")
