@@ -82,16 +82,22 @@ hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile
 // marks[0] and marks[1] together after its single launch.
 // scg, scu, scd: scales of the routed weights when they are FP4 (s.w_fp4),
 // else unused.
+// part: shared_partial_floats(s) floats of workspace (null when 0).
 hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
                           const void* wsg, const void* wsu, const uint8_t* scg,
                           const uint8_t* scu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start,
-                          int row_tile, void* h, hipEvent_t* marks, hipStream_t st);
+                          int row_tile, void* h, float* part, hipEvent_t* marks,
+                          hipStream_t st);
 
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
-                       const void* h, void* y_routed, void* y_shared, hipEvent_t* marks,
-                       hipStream_t st);
+                       const void* h, void* y_routed, void* y_shared, float* part,
+                       hipEvent_t* marks, hipStream_t st);
+
+// fp32 floats of the K-slice partials the shared experts need with FP4
+// routed weights (0 otherwise); the gate/up and down launches share them.
+size_t shared_partial_floats(const Shape& s);
 
 hipError_t launch_quantize_mxfp4(long long E, int N, int K, const void* w, uint8_t* codes,
                                  uint8_t* scales, hipStream_t st);

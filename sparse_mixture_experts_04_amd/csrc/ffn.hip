@@ -234,15 +234,17 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   for (int g = tid; g <= G; g += 256) ts[g] = p.tile_start[g];
   __syncthreads();
 
-  // items of groups g_lo..G-1
+  // items of groups g_lo..G-1, each tile cut into ksplit K slices (slice
+  // index innermost, so the slices of a tile run side by side)
+  const int ksplit = p.ksplit > 1 ? p.ksplit : 1;
   const long long first = static_cast<long long>(ts[p.g_lo]) * p.n_tiles;
-  const long long total = static_cast<long long>(ts[G]) * p.n_tiles - first;
+  const long long total = (static_cast<long long>(ts[G]) * p.n_tiles - first) * ksplit;
   const int xcd = blockIdx.x & 7;
   const int per_xcd = gridDim.x >> 3;
   const int slot = blockIdx.x >> 3;
   const long long chunk = (total + 7) / 8;
-  const long long beg = first + xcd * chunk;
-  const long long end = beg + chunk < first + total ? beg + chunk : first + total;
+  const long long beg = xcd * chunk;
+  const long long end = beg + chunk < total ? beg + chunk : total;
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
@@ -252,10 +254,14 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   const int lrow = lane >> 3;
   const int lchunk[2] = {((lane & 7) ^ lrow) * 8, ((lane & 7) ^ lrow ^ 1) * 8};
   static_assert(C::B_LOADS % 2 == 0, "B load parity follows q");
-  const int nk = p.K / C::BK;
+  const int nk_all = p.K / C::BK;
 
   for (long long it = beg + slot; it < end; it += per_xcd) {
-    const Item item = decode_item(it, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
+    const int ks = static_cast<int>(it % ksplit);
+    const Item item = decode_item(first + it / ksplit, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
+    const int kb = ks * nk_all / ksplit;                 // this slice's K steps
+    const int nk = (ks + 1) * nk_all / ksplit - kb;
+    const size_t koff = static_cast<size_t>(kb) * C::BK;
     const int g = item.g;
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
@@ -270,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
       if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
                                   : static_cast<size_t>(rr);
       else src_row = row_base + rr;
-      t.a_src[q] = A + src_row * p.K + lchunk[(wave * C::A_LOADS + q) & 1];
+      t.a_src[q] = A + src_row * p.K + koff + lchunk[(wave * C::A_LOADS + q) & 1];
     }
     const size_t wstride = static_cast<size_t>(p.N) * p.K;
     const int ge = routed ? g : g - p.E;
@@ -283,12 +289,12 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
       const int col = item.n * C::NOUT + wave * 32 + lrow;
       const bf16_t* wg = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
       const bf16_t* wu = static_cast<const bf16_t*>(routed ? p.w1 : p.ws1) + ge * wstride;
-      t.b_src0 = wg + static_cast<size_t>(col) * p.K;
-      t.b_src1 = wu + static_cast<size_t>(col) * p.K;
+      t.b_src0 = wg + static_cast<size_t>(col) * p.K + koff;
+      t.b_src1 = wu + static_cast<size_t>(col) * p.K + koff;
     } else {
       const int col = item.n * C::NOUT + wave * C::B_LOADS * 8 + lrow;
       const bf16_t* wd = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
-      t.b_src0 = wd + static_cast<size_t>(col) * p.K;
+      t.b_src0 = wd + static_cast<size_t>(col) * p.K + koff;
       t.b_src1 = t.b_src0;
     }
 
@@ -316,6 +322,26 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
 
     // ---- epilogue.  32x32 accumulator layout: lane l holds column l%32 and
     // rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
+    if (p.part) {
+      // a K slice of a shared tile: fp32 accumulators as they are (weight
+      // row order of the tile, no activation); shared_reduce_kernel sums
+      // the slices
+      const size_t ldp = static_cast<size_t>(p.n_tiles) * C::NB;
+      float* prow0 = p.part + (static_cast<size_t>(ks) * p.S * p.T +
+                               static_cast<size_t>(g - p.E) * p.T + item.m0) * ldp;
+#pragma unroll
+      for (int i = 0; i < C::BM; ++i) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = wm * C::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (row >= item.rows) continue;
+#pragma unroll
+          for (int j = 0; j < C::BN; ++j)
+            prow0[row * ldp + item.n * C::NB + wn * C::WN + j * 32 + (lane & 31)] = acc[i][j][r];
+        }
+      }
+      continue;
+    }
     bf16_t* out = static_cast<bf16_t*>(routed ? p.out_routed : p.out_shared);
     const size_t orow0 = routed ? static_cast<size_t>(p.offsets[g]) + item.m0
                                 : static_cast<size_t>(g - p.E) * p.T + item.m0;
@@ -446,6 +472,54 @@ static int device_cus() {
   return cus > 0 ? cus : 256;
 }
 
+// Sum of the K-slice partials of the shared experts' tiles, in slice
+// order, then what the kernel's epilogue does: SwiGLU of each gate/up
+// column pair (GATED; a tile's 256 weight rows hold, for each 32-column
+// group w of the 128 outputs, the W_gate rows then the W_up rows) or the
+// bf16 rounding of the down output.  One thread per output element.
+template <bool GATED>
+__global__ __launch_bounds__(256) void shared_reduce_kernel(const float* __restrict__ part,
+                                                            int ksplit, int rows, int ldp,
+                                                            int nout, bf16_t* __restrict__ out) {
+  const long long n = static_cast<long long>(rows) * nout;
+  const long long stride = static_cast<long long>(gridDim.x) * blockDim.x;
+  const size_t slice = static_cast<size_t>(rows) * ldp;
+  for (long long i = static_cast<long long>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+       i += stride) {
+    const int row = static_cast<int>(i / nout);
+    const int c = static_cast<int>(i % nout);
+    const float* pr = part + static_cast<size_t>(row) * ldp;
+    if (GATED) {
+      const int col = (c >> 7) * 256 + ((c >> 5) & 3) * 64 + (c & 31);
+      float gt = 0.0f, up = 0.0f;
+      for (int ks = 0; ks < ksplit; ++ks) {
+        gt += pr[ks * slice + col];
+        up += pr[ks * slice + col + 32];
+      }
+      out[i] = f32_to_bf16(gt / (1.0f + __expf(-gt)) * up);
+    } else {
+      float v = 0.0f;
+      for (int ks = 0; ks < ksplit; ++ks) v += pr[ks * slice + c];
+      out[i] = f32_to_bf16(v);
+    }
+  }
+}
+
+size_t shared_partial_floats(const Shape& s) {
+  if (!s.w_fp4 || !s.bf16 || s.S == 0) return 0;
+  const size_t rows = static_cast<size_t>(s.S) * s.T;
+  const int kg = shared_ksplit(s, s.F / 128, s.d / 64);
+  const int kd = shared_ksplit(s, s.d / 256, s.F / 64);
+  const size_t g = kg > 1 ? kg * rows * 2 * s.F : 0;
+  const size_t d = kd > 1 ? kd * rows * s.d : 0;
+  return g > d ? g : d;
+}
+
+// The shared experts alone on the 32-row bf16 kernel (FP4 routed weights),
+// K-sliced when their tiles are too few to fill the chip.
+template <bool GATED>
+static hipError_t run_shared_bf16(FfnArgs a, const Shape& s, float* part, hipStream_t st);
+
 template <int MT, bool GATED>
 static hipError_t run_bf16(const FfnArgs& a, hipStream_t st) {
   int grid = device_cus();
@@ -460,6 +534,25 @@ static hipError_t record_marks(hipEvent_t* marks, hipStream_t st) {
 }
 
 template <bool GATED>
+static hipError_t run_shared_bf16(FfnArgs a, const Shape& s, float* part, hipStream_t st) {
+  if (s.S == 0) return hipSuccess;
+  a.g_lo = s.E;
+  a.ksplit = shared_ksplit(s, a.n_tiles, a.K / 64);
+  a.part = a.ksplit > 1 ? part : nullptr;
+  if (a.ksplit > 1 && !part) return hipErrorInvalidValue;
+  hipError_t e = run_bf16<32, GATED>(a, st);
+  if (e != hipSuccess || !a.part) return e;
+  const int rows = s.S * s.T;
+  const int nout = GATED ? s.F : s.d;
+  const long long n = static_cast<long long>(rows) * nout;
+  const long long blocks = (n + 255) / 256;
+  shared_reduce_kernel<GATED><<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0,
+                                st>>>(part, a.ksplit, rows, a.n_tiles * 256, nout,
+                                      static_cast<bf16_t*>(a.out_shared));
+  return hipGetLastError();
+}
+
+template <bool GATED>
 static hipError_t run_f32(const FfnArgs& a, hipStream_t st) {
   ffn_f32_kernel<GATED><<<device_cus() * 4, 256, 0, st>>>(a);
   return hipGetLastError();
@@ -469,7 +562,7 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
                           const void* wsg, const void* wsu, const uint8_t* scg,
                           const uint8_t* scu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start, int row_tile,
-                          void* h, hipEvent_t* marks, hipStream_t st) {
+                          void* h, float* part, hipEvent_t* marks, hipStream_t st) {
   if (s.T == 0) return record_marks(marks, st);
   FfnArgs a{};
   a.sc0 = scg;
@@ -497,8 +590,7 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
     if (row_tile != 32) return launch_big(a, true, tile_start, 0, marks, st);
     if (s.w_fp4) {  // routed experts in FP4, then the bf16 shared experts
       hipError_t e = launch_fp4(a, true, st);
-      a.g_lo = s.E;
-      if (e == hipSuccess) e = run_bf16<32, true>(a, st);
+      if (e == hipSuccess) e = run_shared_bf16<true>(a, s, part, st);
       return e == hipSuccess ? record_marks(marks, st) : e;
     }
     hipError_t e = run_bf16<32, true>(a, st);
@@ -511,8 +603,8 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
 
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
-                       const void* h, void* y_routed, void* y_shared, hipEvent_t* marks,
-                       hipStream_t st) {
+                       const void* h, void* y_routed, void* y_shared, float* part,
+                       hipEvent_t* marks, hipStream_t st) {
   if (s.T == 0) return record_marks(marks, st);
   FfnArgs a{};
   a.sc0 = scd;
@@ -535,8 +627,7 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const ui
     if (row_tile != 32) return launch_big(a, false, tile_start, 1, marks, st);
     if (s.w_fp4) {
       hipError_t e = launch_fp4(a, false, st);
-      a.g_lo = s.E;
-      if (e == hipSuccess) e = run_bf16<32, false>(a, st);
+      if (e == hipSuccess) e = run_shared_bf16<false>(a, s, part, st);
       return e == hipSuccess ? record_marks(marks, st) : e;
     }
     hipError_t e = run_bf16<32, false>(a, st);

@@ -84,7 +84,21 @@ struct FfnArgs {
   const uint8_t* sc0;     // FP4 routed weights: scales of w0 / w1 [E, K/32, N]
   const uint8_t* sc1;
   int g_lo;               // first group the 32-row bf16 kernel processes
+  int ksplit;             // 32-row bf16 kernel, shared groups only: K slices per tile
+  float* part;            // ksplit > 1: fp32 partial tiles [ksplit][S*T][n_tiles*256]
 };
+
+// K slices of the shared experts' tiles when the 32-row bf16 kernel runs
+// them alone (FP4 routed weights): enough items to cover 256 workgroups,
+// at most 4 slices and never more than the K steps (nk) of a tile.
+inline int shared_ksplit(const Shape& s, int n_tiles, int nk) {
+  const long long items = static_cast<long long>(s.S) * ((s.T + 31) / 32) * n_tiles;
+  if (items <= 0) return 1;
+  long long k = (256 + items - 1) / items;
+  k = k > 4 ? 4 : k;
+  k = k > nk ? nk : k;
+  return static_cast<int>(k < 1 ? 1 : k);
+}
 
 
 // ---------------------------------------------------------- LDS helpers

@@ -97,6 +97,7 @@ int32_t* carve_plan(Carver& c, const Shape& s) {
   const int big = big_plan_ints(s.E + s.S);
   return c.take<int32_t>(small > big ? small : big);
 }
+float* carve_part(Carver& c, const Shape& s) { return c.take<float>(shared_partial_floats(s)); }
 void* carve_h(Carver& c, const Shape& s) {
   return c.take<char>(static_cast<size_t>(s.k + s.S) * s.T * s.F * esize(s));
 }
@@ -114,6 +115,7 @@ struct FwdWs {
   void* h;
   void* y_routed;
   void* y_shared;
+  float* part;
 };
 FwdWs carve_forward(Carver& c, const Shape& s) {
   FwdWs w;
@@ -130,6 +132,7 @@ FwdWs carve_forward(Carver& c, const Shape& s) {
   w.h = carve_h(c, s);
   w.y_routed = c.take<char>(kT * s.d * esize(s));
   w.y_shared = c.take<char>(static_cast<size_t>(s.S) * s.T * s.d * esize(s));
+  w.part = carve_part(c, s);
   return w;
 }
 
@@ -139,8 +142,8 @@ size_t ws_bytes_for(const Shape& s, moe_call call) {
     case MOE_CALL_ROUTER: carve_router(c, s); break;
     case MOE_CALL_DISPATCH: carve_dispatch(c, s); break;
     case MOE_CALL_GATE_UP:
-    case MOE_CALL_DOWN: carve_plan(c, s); break;
-    case MOE_CALL_EXPERT_FFN: carve_plan(c, s); carve_h(c, s); break;
+    case MOE_CALL_DOWN: carve_plan(c, s); carve_part(c, s); break;
+    case MOE_CALL_EXPERT_FFN: carve_plan(c, s); carve_h(c, s); carve_part(c, s); break;
     case MOE_CALL_FORWARD: carve_forward(c, s); break;
     default: break;
   }
@@ -232,12 +235,12 @@ moe_status moe_expert_gate_up(const moe_desc* desc, const void* x, const moe_wei
   if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
+  float* part = carve_part(c, s);
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
-                       offsets, sorted_pair,
-                       plan, mt, h, nullptr, stream);
+                       offsets, sorted_pair, plan, mt, h, part, nullptr, stream);
   return hip_status(e);
 }
 
@@ -252,11 +255,12 @@ moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w, const int
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
+  float* part = carve_part(c, s);
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
-                    stream);
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed,
+                    y_shared, part, nullptr, stream);
   return hip_status(e);
 }
 
@@ -273,13 +277,13 @@ moe_status moe_expert_gate_up_marked(const moe_desc* desc, const void* x, const 
   if ((st = check_ws(s, MOE_CALL_GATE_UP, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
+  float* part = carve_part(c, s);
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess) e = hipEventRecord(marks[0], stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
-                       offsets, sorted_pair,
-                       plan, mt, h, marks + 1, stream);
+                       offsets, sorted_pair, plan, mt, h, part, marks + 1, stream);
   return hip_status(e);
 }
 
@@ -296,12 +300,13 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
   if ((st = check_ws(s, MOE_CALL_DOWN, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
+  float* part = carve_part(c, s);
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess) e = hipEventRecord(marks[0], stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed, y_shared,
-                    marks + 1, stream);
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed,
+                    y_shared, part, marks + 1, stream);
   return hip_status(e);
 }
 
@@ -318,15 +323,15 @@ moe_status moe_expert_ffn(const moe_desc* desc, const void* x, const moe_weights
   Carver c{static_cast<char*>(ws)};
   int32_t* plan = carve_plan(c, s);
   void* h = carve_h(c, s);
+  float* part = carve_part(c, s);
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_tile_plan(s, offsets, mt, plan, stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
-                       offsets, sorted_pair,
-                       plan, mt, h, nullptr, stream);
+                       offsets, sorted_pair, plan, mt, h, part, nullptr, stream);
   if (e == hipSuccess)
-    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed, y_shared, nullptr,
-                    stream);
+    e = launch_down(s, w->w_down, w->ws_down, w->sc_down, offsets, plan, mt, h, y_routed,
+                    y_shared, part, nullptr, stream);
   return hip_status(e);
 }
 
@@ -390,11 +395,10 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
   if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
-                       f.offsets,
-                       f.sorted_pair, f.plan, mt, f.h, nullptr, stream);
+                       f.offsets, f.sorted_pair, f.plan, mt, f.h, f.part, nullptr, stream);
   if (e == hipSuccess)
     e = launch_down(s, w->w_down, w->ws_down, w->sc_down, f.offsets, f.plan, mt, f.h, f.y_routed,
-                    f.y_shared, nullptr, stream);
+                    f.y_shared, f.part, nullptr, stream);
   if (e == hipSuccess)
     e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
   if (e == hipSuccess && gamma != 0.0f) e = launch_bias_update(s, f.counts, gamma, bias, stream);

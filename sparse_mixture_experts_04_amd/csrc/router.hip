@@ -339,6 +339,24 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
 
 // ------------------------------------------------------------- selection
 
+// z = sum of the K-split partial logits in split order.  The loads of a
+// group of 8 splits are issued together (small batches split K up to 28
+// ways); the additions stay in split order.
+__device__ __forceinline__ double sum_partials(const double* __restrict__ partial, size_t kstride,
+                                               int nks, size_t off) {
+  double z = 0.0;
+  int ks = 0;
+  for (; ks + 8 <= nks; ks += 8) {
+    double v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = partial[(ks + j) * kstride + off];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) z += v[j];
+  }
+  for (; ks < nks; ++ks) z += partial[ks * kstride + off];
+  return z;
+}
+
 __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
@@ -358,22 +376,19 @@ __global__ __launch_bounds__(256) void router_select(
 
   double sv[EPL], zv[EPL], key[EPL];
   bool taken[EPL];
+  const size_t kstride = static_cast<size_t>(T) * npad;
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     const int c = lane + 64 * q;
-    double z = 0.0;
-    for (int ks = 0; ks < nks; ++ks) z += partial[(static_cast<size_t>(ks) * T + t) * npad + c];
-    const double s = 1.0 / (1.0 + exp(-z));
+    zv[q] = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + c);
+    const double s = 1.0 / (1.0 + exp(-zv[q]));
     sv[q] = s;
-    zv[q] = z;
     key[q] = s + static_cast<double>(bias[c]);
     taken[q] = false;
   }
   double s_shared = 0.0, z_shared = 0.0;
   if (lane < S) {
-    double z = 0.0;
-    for (int ks = 0; ks < nks; ++ks)
-      z += partial[(static_cast<size_t>(ks) * T + t) * npad + E + lane];
+    const double z = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + E + lane);
     s_shared = 1.0 / (1.0 + exp(-z));
     z_shared = z;
   }

@@ -72,6 +72,14 @@ SMALL = {
                             fp4_weights=True),
     "fp4_cap": MoEConfig("fp4_cap", T=300, d=256, F=128, act="bf16", bias_range=0.05,
                          fp4_weights=True, capacity_factor=1.0),
+    # shared experts' K slices: 4 uneven ones for down (6 K steps), 1 and 2
+    # at the largest decode batch, none without shared experts
+    "fp4_uneven": MoEConfig("fp4_uneven", T=64, d=512, F=384, act="bf16", bias_range=0.05,
+                            fp4_weights=True),
+    "fp4_t2047": MoEConfig("fp4_t2047", T=2047, d=256, F=256, act="bf16", bias_range=0.05,
+                           fp4_weights=True),
+    "fp4_e64_s0": MoEConfig("fp4_e64_s0", T=100, d=256, F=128, E=64, S=0, act="bf16",
+                            bias_range=0.05, fp4_weights=True),
 }
 
 
@@ -87,7 +95,7 @@ def test_fp4_layer_full_parity(name):
     topk = npi(b.topk)
     _, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates))
     cap = O.capacity(cfg.capacity_factor, cfg.k, cfg.T, cfg.E)
-    dp = check_dispatch(topk, b, cap=cap)
+    dp = check_dispatch(topk, b, E=cfg.E, cap=cap)
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
     hw = _fp4_oracle_weights(inp)
     yr_ref, ys_ref = O.expert_ffn(x64, hw, dp["offsets"], dp["sorted_pair"], cfg.k)
@@ -98,6 +106,13 @@ def test_fp4_layer_full_parity(name):
     e_y = rel_l2(np64(b.y), y_ref)
     log(f"  routing {st}; rel L2 y_routed {e_yr:.2e} y_shared {e_ys:.2e} y {e_y:.2e}")
     assert e_yr <= 2e-2 and e_ys <= 2e-2 and e_y <= 2e-2
+    # the shared experts' hidden rows (K-sliced with fp32 partials when the
+    # shared tiles are few) against the oracle's SwiGLU
+    T, k = cfg.T, cfg.k
+    for s_ in range(cfg.S):
+        h_ref = O.swiglu_hidden(x64, hw["ws_gate"][s_], hw["ws_up"][s_])
+        e_h = rel_l2(np64(b.h)[k * T + s_ * T:k * T + (s_ + 1) * T], h_ref)
+        assert e_h <= 1e-2, (s_, e_h)
     # the fused entry point gives the same bits
     bf, _ = run_forward(desc, inp, cfg.gamma, weights=wq)
     for nm in ("topk", "counts", "offsets", "pair_pos", "y"):
