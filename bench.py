@@ -15,7 +15,10 @@ combine, bias update) over one batch already resident in HBM:
   of 1.25x the ideal load (drop rate per batch);
 * native-shape workload (reported alongside): hidden 6144, expert width
   3072, gates by logsumexp over log-sigmoids times a route scale, at the
-  headline batch size.
+  headline batch size;
+* Router Balance Lab (reported alongside): 64 experts, d = 32, 2048
+  Zipf-lumpy tokens per step, capacity 1.25x, 100 routing steps at bias
+  steps 0, 0.01 and 0.05, with MaxVio, drop rate and layer quality.
 
 Prints one JSON line.  ``value`` is tokens/s of the headline workload;
 ``roofline`` is for its dominant kernel, the grouped gate/up GEMM (matrix

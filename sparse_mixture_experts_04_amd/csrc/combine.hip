@@ -1,9 +1,10 @@
-// Combine: y_t = sum over the 8 contributors of g * expert output.
+// Combine: y_t = sum over the k + S contributors of g * expert output.
 //
 // "Inkling, Dissected", 02 and 02b: the layer output is the gate-weighted
-// sum of the 6 chosen routed experts' outputs and the 2 shared experts'
-// outputs; a pair dropped at its expert's capacity (pair_pos < 0, 02d)
-// contributes nothing.  Each output element is summed in fp32 in a fixed order
+// sum of the chosen routed experts' outputs (6 of them) and the shared
+// experts' outputs (2 in the layer of the pages; 0 to 2 here); a pair
+// dropped at its expert's capacity (pair_pos < 0, 02d) contributes
+// nothing.  Each output element is summed in fp32 in a fixed order
 // (routed slots in rank order, then the shared experts), from rows found
 // through pair_pos, with no atomics: the result is deterministic.
 #include "common.h"

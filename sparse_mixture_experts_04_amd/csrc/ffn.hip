@@ -2,7 +2,8 @@
 //
 // "Under The Hood: Inkling", "MoE: the expert configuration": each routed
 // expert is a SwiGLU FFN and the shared experts have the same width;
-// "Inkling, Dissected", 02: the 2 shared experts process every token.
+// "Inkling, Dissected", 02: the shared experts (2 in the pages' layer)
+// process every token.
 //
 // Work is a list of groups g = 0..E+S-1: routed expert g owns the rows
 // offsets[g]..offsets[g+1] of the expert-sorted pair order; shared expert
