@@ -55,6 +55,7 @@ def parse():
     ap.add_argument("--no-skewed", action="store_true")
     ap.add_argument("--native-workload", default="I")
     ap.add_argument("--no-native", action="store_true")
+    ap.add_argument("--no-ep-share", action="store_true")
     ap.add_argument("--lab-workload", default="Lab")
     ap.add_argument("--no-lab", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -279,6 +280,52 @@ def balance_lab(cfg, torch, gammas=(0.0, 0.01, 0.05)):
             "ms_per_step": round(ms, 4), "tokens_s": round(cfg.T / (ms / 1e3), 1)}
 
 
+def ep_share(cfg, inp, w, torch, L, synth, steps):
+    """The expert GEMMs at one GPU's share of 8-way expert parallelism over
+    8 x T tokens: 32 routed experts (ids 96..127) with k*T/32 rows each,
+    gathered from the local token buffer by a seeded permutation (the rows an
+    all-to-all would deliver), and the shared experts on the T local tokens.
+    One moe_expert_ffn call (tile plan, gate/up + SwiGLU, down)."""
+    E, k, T, S = cfg.E, cfg.k, cfg.T, cfg.S
+    P = k * T
+    counts = torch.zeros(E, dtype=torch.int64)
+    counts[96:128] = P // 32
+    offsets = torch.zeros(E + 1, dtype=torch.int32)
+    offsets[1:] = torch.cumsum(counts, 0).to(torch.int32)
+    offsets = offsets.cuda()
+    g = torch.Generator(device="cpu")
+    g.manual_seed(8)
+    sorted_pair = torch.randperm(P, generator=g).to(torch.int32).cuda()
+    act = synth.act_dtype(cfg)
+    y_routed = torch.empty((P, cfg.d), dtype=act, device="cuda")
+    y_shared = torch.empty((S, T, cfg.d), dtype=act, device="cuda")
+    desc = L.make_desc(T, cfg.d, cfg.F, act)
+    ws = L.alloc_workspace(desc, L.CALL_EXPERT_FFN, "cuda")
+
+    def call():
+        L.expert_ffn(desc, inp["x"], w, offsets, sorted_pair, y_routed, y_shared, ws=ws)
+
+    for _ in range(2):
+        call()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 6.0 * cfg.d * cfg.F * (P + S * T)
+    del y_routed, y_shared, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"expert GEMMs at one GPU's share of 8-way expert parallelism: 32 "
+                        f"routed experts x {P // 32} rows + {S} shared experts x {T} rows, "
+                        f"d={cfg.d}, F={cfg.F}, bf16",
+            "ms_per_call": round(ms, 4),
+            "tflops": round(flops / (ms / 1e3) / 1e12, 1),
+            "mfma_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def decode_bytes(cfg, counts):
     n_active = int((counts > 0).sum())
     esz = 2 if cfg.act == "bf16" else 4
@@ -383,6 +430,9 @@ def main():
     max_load = counts.max().item()
     result["max_over_mean_load"] = round(max_load / (cfg.T * cfg.k / cfg.E), 3)
     del ws
+    torch.cuda.empty_cache()
+    if not args.no_ep_share:
+        result["ep_share"] = ep_share(cfg, inp, w, torch, L, synth, max(3, min(args.steps, 10)))
     if not args.no_decode:
         dc = configs.get(args.decode_workload)
         dinp = time_forward(dc, max(args.steps, 20), args.warmup, torch, L, synth)

@@ -236,3 +236,49 @@ def test_expert_ffn_tile_boundaries(T):
     e_all, e_sh = rel_l2(yr, yr_ref), rel_l2(np64(b.y_shared), ys_ref)
     log(f"  T={T}: y_routed {e_all:.2e} y_shared {e_sh:.2e}")
     assert e_all <= 2e-2 and e_sh <= 2e-2
+
+
+def test_expert_ffn_ep_share_sampled():
+    """The expert GEMMs at one GPU's share of 8-way expert parallelism: 32
+    routed experts (ids 96..127) holding 3072 rows each, i.e. the 98,304
+    (token, expert) pairs that 8 GPUs of 16,384 tokens send to one GPU, and
+    the shared experts on the GPU's own 16,384 tokens, at d=7168, F=2048.
+    Sampled rows against the oracle's SwiGLU of the same rows."""
+    cfg = configs.get("D")
+    inp = synth.make_inputs(cfg, device=DEV)
+    E, k, T = cfg.E, cfg.k, cfg.T
+    P = k * T
+    counts = np.zeros(E, dtype=np.int64)
+    counts[96:128] = P // 32
+    offsets = np.concatenate([[0], np.cumsum(counts)])
+    rng = np.random.default_rng(8)
+    sorted_pair = rng.permutation(P)
+    desc = desc_for(cfg)
+    b = Buffers(desc, DEV)
+    from sparse_mixture_experts_04_amd import _lib as L
+    L.expert_ffn(desc, inp["x"], L.weights_from(inp),
+                 torch.tensor(offsets, dtype=torch.int32, device=DEV),
+                 torch.tensor(sorted_pair, dtype=torch.int32, device=DEV), b.y_routed, b.y_shared)
+    torch.cuda.synchronize()
+    get = expert_getter(inp)
+    worst = 0.0
+    for e in (96, 111, 127):
+        lo = int(offsets[e])
+        rows = [0, 1, 31, 32, 255, 256, 1535, 1536, 3071]
+        toks = sorted_pair[lo + np.array(rows)] // k
+        wg, wu, wd = get(e)
+        ref = O.swiglu(np64(inp["x"][torch.tensor(toks, device=DEV)]), wg, wu, wd)
+        got = np64(b.y_routed[lo + torch.tensor(rows, device=DEV)])
+        for i in range(len(rows)):
+            worst = max(worst, rel_l2(got[i], ref[i]))
+    for s_ in range(cfg.S):
+        toks = [0, 1, 8191, 16383]
+        wg, wu, wd = get(E + s_)
+        ref = O.swiglu(np64(inp["x"][torch.tensor(toks, device=DEV)]), wg, wu, wd)
+        got = np64(b.y_shared[s_][torch.tensor(toks, device=DEV)])
+        for i in range(len(toks)):
+            worst = max(worst, rel_l2(got[i], ref[i]))
+    log(f"  EP share: worst sampled row rel L2 {worst:.2e}")
+    assert worst <= 2e-2
+    del inp, b
+    torch.cuda.empty_cache()
