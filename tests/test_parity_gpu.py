@@ -196,6 +196,52 @@ def test_skewed_bias_trajectory_lockstep():
     torch.cuda.empty_cache()
 
 
+@pytest.mark.parametrize("cf", [0.0, 1.25])
+def test_skewed_bias_trajectory_100_steps(cf):
+    """The skewed router's 100 bias steps at a size the oracle runs in
+    seconds (T=2048, d=512, 256 routed + 2 shared experts, kappa = 8), with
+    and without capacity: every step against the oracle fed the GPU's bias,
+    then the GPU's whole bias trajectory against the oracle's own."""
+    cfg = MoEConfig(f"E_small_{cf}", T=2048, d=512, F=128, act="bf16", bias_range=0.0,
+                    skew_kappa=8.0, steps=100, capacity_factor=cf)
+    log(f"[skewed 100 steps] {cfg.describe()} cf={cf}")
+    T, E, k = cfg.T, cfg.E, cfg.k
+    desc = desc_for(cfg)
+    wr = synth.make_router(cfg)
+    wr64 = wr.numpy().astype(np.float64)
+    xs = [synth.make_x(cfg, "cpu", i) for i in range(cfg.steps)]
+    cap = cap_for(cfg)
+    b = Buffers(desc, DEV)
+    from sparse_mixture_experts_04_amd import _lib as L
+    w_dev = wr.to(DEV)
+    bias = torch.zeros(E, dtype=torch.float32, device=DEV)
+    flips, traj = 0, []
+    for i in range(cfg.steps):
+        x = xs[i].to(DEV)
+        b_in = bias.clone()
+        L.router(desc, x, w_dev, bias, b.topk, b.gates, b.margin)
+        L.dispatch(desc, b.topk, b.counts, b.offsets, b.sorted_pair, b.pair_pos)
+        L.bias_update(desc, b.counts, cfg.gamma, bias)
+        torch.cuda.synchronize()
+        topk = npi(b.topk)
+        _, _, st = check_routing(np64(xs[i]), wr64, np64(b_in), topk, np64(b.gates))
+        flips += st["exempt_differ"]
+        check_dispatch(topk, b, E=E, cap=cap)
+        check_bias(npi(b.counts), cfg.gamma, b_in, bias, T)
+        traj.append(b_in.cpu().numpy())
+    ob = np.zeros(E, np.float32)
+    first_diff = None
+    for i in range(cfg.steps):
+        if first_diff is None and not np.array_equal(ob.view(np.uint32), traj[i].view(np.uint32)):
+            first_diff = i
+        r = O.route(np64(xs[i]), wr64, ob, n_routed=E, k=k)
+        dp = O.dispatch(r["topk_idx"], n_routed=E, cap=cap)
+        ob = O.bias_update(dp["counts"], cfg.gamma, ob, T, k)
+    log(f"  near-tie flips {flips}; first step where the trajectories differ: {first_diff}")
+    if flips == 0:
+        assert first_diff is None
+
+
 @pytest.mark.parametrize("T", [1200, 3000])
 def test_expert_ffn_tile_boundaries(T):
     # Hand-picked per-expert row counts around every tile size the GEMMs use
