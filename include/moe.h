@@ -90,10 +90,11 @@ extern "C" {
 typedef enum {
   MOE_OK = 0,
   MOE_ERR_NULL = 1,        /* a required pointer is NULL                 */
-  MOE_ERR_SHAPE = 2,       /* negative size, or a non-finite gamma       */
-  MOE_ERR_DTYPE = 3,       /* unknown dtype, or act != weight            */
+  MOE_ERR_SHAPE = 2,       /* negative size, non-finite gamma, or a bad
+                              gate_norm, gate_scale or capacity_factor */
+  MOE_ERR_DTYPE = 3,       /* unknown dtype or dtype pair                */
   MOE_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than required    */
-  MOE_ERR_UNSUPPORTED = 5, /* valid but outside the v1 shape limits      */
+  MOE_ERR_UNSUPPORTED = 5, /* valid but outside the supported shapes     */
   MOE_ERR_HIP = 6          /* a kernel launch failed                     */
 } moe_status;
 

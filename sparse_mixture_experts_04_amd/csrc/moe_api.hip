@@ -175,8 +175,9 @@ const char* moe_status_string(moe_status st) {
   switch (st) {
     case MOE_OK: return "ok";
     case MOE_ERR_NULL: return "a required pointer is NULL";
-    case MOE_ERR_SHAPE: return "invalid size or non-finite gamma";
-    case MOE_ERR_DTYPE: return "unsupported dtype (act and weight must both be f32 or bf16)";
+    case MOE_ERR_SHAPE: return "invalid size, gamma, gate normalisation or capacity factor";
+    case MOE_ERR_DTYPE:
+      return "unsupported dtype (act and weight both f32, both bf16, or bf16 with MXFP4 weights)";
     case MOE_ERR_WORKSPACE: return "workspace missing or too small";
     case MOE_ERR_UNSUPPORTED: return "shape outside the supported limits";
     case MOE_ERR_HIP: return "HIP kernel launch failed";
