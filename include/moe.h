@@ -65,9 +65,9 @@
  * - y_routed  act   [T*k, d] expert outputs in sorted order;
  *   y_shared  act   [S, T, d] shared-expert outputs.
  *
- * Capacity ("Inkling, Dissected" 02d: an expert processes at most a fixed
- * number of tokens per batch; the overflow is dropped and the layer output
- * is computed from the remaining contributions).  With capacity_factor
+ * Capacity ("Inkling, Dissected" 02d: each expert takes a bounded number
+ * of tokens per batch; pairs beyond it are dropped and the output is built
+ * from the pairs that were kept).  With capacity_factor
  * cf > 0 each routed expert keeps C = ceil(cf * k * T / E) pairs (the
  * product and quotient taken in double precision), the first C in
  * ascending pair number, i.e. ascending token; a dropped pair contributes

@@ -232,15 +232,16 @@ def load_metrics(counts, kept, k, T):
 
 
 def layer_quality(s, topk_idx, pair_pos, k=6):
-    """Router Balance Lab's layer quality ("Inkling, Dissected", 02g): the
-    true affinity that the surviving weighted mixture captures, as a
-    fraction of what an uncapacitated, unbiased router captures.
+    """Router Balance Lab's layer quality ("Inkling, Dissected", 02g): how
+    much of the tokens' affinity the gate-weighted experts still deliver
+    after capacity drops, relative to a router with neither bias nor
+    capacity limit.
 
     This module's reading: a token's mixture over a set of routed experts
     weights expert j by g_j = s_j / sum of s over the set (the gates of
     02b); the mixture captures sum of g_j * s_j over the pairs that
     survived capacity (a dropped pair contributes nothing, and the other
-    gates are not renormalised).  The uncapacitated oracle uses the top-k by
+    gates are not renormalised).  The reference router takes the top-k by
     s alone (no bias, nothing dropped).  Quality = captured / oracle, both
     summed over the batch.  ``s`` holds the routed experts' affinities
     [T, n_routed]; ``pair_pos`` is dispatch's (-1 for a dropped pair).
@@ -448,23 +449,39 @@ def moe_forward(x, w_router, weights, bias, gamma, k=6, gate_norm="ratio", gate_
 
 
 def moe_layer_per_token(x_t, experts, w_router, bias, k=6):
-    """One token's forward, step by step as the page's NumPy sketch states.
-
-    ("Inkling, Dissected", 02b.)  ``experts`` is a list of callables, routed
-    experts first and the shared experts last.  Used on small inputs to
-    cross-check the grouped ``expert_ffn`` + ``combine``.
+    """One token through the layer of "Inkling, Dissected" 02b, spelled out
+    with plain per-expert loops and none of the batch helpers above:
+    affinity of every expert, the k routed experts with the largest biased
+    score picked one at a time (the lower id first on exact ties), one
+    normalisation over them and the shared experts, the weighted sum of
+    their outputs.  ``experts`` is a list of callables, routed experts
+    first and the shared experts last.  Used on small inputs to cross-check
+    the grouped ``route`` + ``expert_ffn`` + ``combine``.
     """
     x_t = _f64(x_t)
+    w = _f64(w_router)
     n_routed = len(bias)
-    s = sigmoid(_f64(w_router) @ x_t)
-    key = s[:n_routed] + _f64(bias)
-    top, _ = select_topk(key[None, :], k)
-    idx = list(top[0]) + list(range(n_routed, len(s)))
-    g = s[idx] / s[idx].sum()
-    out = np.zeros_like(x_t)
-    for g_k, e in zip(g, idx):
-        out = out + g_k * experts[e](x_t)
-    return out
+    affinity = []
+    for e in range(w.shape[0]):
+        z = float(np.dot(w[e], x_t))
+        affinity.append(1.0 / (1.0 + np.exp(-z)) if z >= 0 else np.exp(z) / (1.0 + np.exp(z)))
+    left = list(range(n_routed))
+    picked = []
+    while len(picked) < k:
+        best = left[0]
+        for e in left[1:]:
+            if affinity[e] + float(bias[e]) > affinity[best] + float(bias[best]):
+                best = e
+        picked.append(best)
+        left.remove(best)
+    contributors = picked + list(range(n_routed, w.shape[0]))
+    total = 0.0
+    for e in contributors:
+        total += affinity[e]
+    y = np.zeros_like(x_t)
+    for e in contributors:
+        y = y + (affinity[e] / total) * experts[e](x_t)
+    return y
 
 
 def output_rows(tokens, x, topk_idx, gates, expert_weights, k=6, n_routed=256,

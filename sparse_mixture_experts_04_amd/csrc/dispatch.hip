@@ -3,7 +3,7 @@
 // "Inkling, Dissected", 02: each token visits the 6 routed experts it chose;
 // 02e: the load L_e is the number of tokens that selected expert e, the
 // ideal load is the total selections divided by the number of experts, and
-// after each batch b_e moves by gamma * sign(ideal - L_e).
+// once a batch is done b_e moves by gamma * sign(ideal - L_e).
 //
 // The grouping is histogram -> exclusive scan -> stable scatter, with no
 // atomic deciding any output position:

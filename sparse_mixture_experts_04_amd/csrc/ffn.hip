@@ -1,7 +1,7 @@
 // Expert MLPs as grouped GEMMs: gate/up with a fused SwiGLU, then down.
 //
-// "Under The Hood: Inkling", "MoE: the expert configuration": each routed
-// expert is a SwiGLU FFN and the shared experts have the same width;
+// "Under The Hood: Inkling", "MoE: the expert configuration": routed
+// experts are SwiGLU MLPs, and the shared experts use the same width;
 // "Inkling, Dissected", 02: the shared experts (2 in the pages' layer)
 // process every token.
 //

@@ -53,7 +53,7 @@ def test_worked_example_page_02c():
     np.testing.assert_allclose(key[0], g["biased"]["scores_printed"], atol=1.5e-3)
     top_b, _ = O.select_topk(key, k)
     assert list(top_b[0]) == g["biased"]["top"]
-    # gates of the new pair come from the raw affinities, not the biased keys
+    # the new pair's gates use the affinities without the bias
     gates_b, _ = O.joint_gates(s, top_b, [])
     np.testing.assert_allclose(gates_b[0], g["biased"]["gates_printed"], atol=1.5e-3)
 
@@ -471,7 +471,7 @@ def test_down_projection_linearity():
     assert np.array_equal(y2, 2.0 * y1)
 
 
-def test_grouped_matches_per_token_transcription():
+def test_grouped_matches_per_token_loops():
     T, d, F = 24, 16, 8
     x, w, b = _rand_router(T=T, d=d, seed=14)
     weights = _rand_weights(256, 2, d, F, seed=15)
