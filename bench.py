@@ -377,6 +377,54 @@ def cpu_baseline(cfg, inp, ntok, torch):
                        f"experts, combine, bias update)")}
 
 
+def section(result, key, fn):
+    """Run one reported-alongside measurement; an exception is recorded in
+    the JSON line under the section's key (and printed to stderr) instead of
+    losing the line."""
+    import traceback
+    try:
+        result[key] = fn()
+    except Exception as e:  # noqa: BLE001 - reported, not hidden
+        traceback.print_exc(file=sys.stderr)
+        result[key] = {"error": f"{type(e).__name__}: {e}"}
+
+
+def decode(dc, args, torch, L, synth):
+    """A decode workload (bf16 or FP4 routed weights) against HBM bandwidth."""
+    steps = max(args.steps, 20)
+    inp, desc, w, ws, counts, ms, _ = time_forward(dc, steps, args.warmup, torch, L, synth)
+    stages = None
+    if not dc.fp4_weights:
+        stages, _, _ = time_stages(dc, inp, desc, w, 10, torch, L, synth)
+    nbytes, n_active = decode_bytes(dc, counts.cpu())
+    gbs = nbytes / (ms / 1e3) / 1e9
+    weights = ("routed experts' weights MXFP4 (E2M1, power-of-two scale per 32), shared "
+               "experts bf16" if dc.fp4_weights else "bf16 weights")
+    out = {"workload": f"decode MoE layer, {dc.describe()}, {weights}, fp32 router",
+           "tokens_s": round(dc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4)}
+    if stages is not None:
+        out["stage_ms"] = {k: round(v, 4) for k, v in stages.items()}
+    out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                       "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                       "active_experts": n_active, "scope": "whole moe_forward step"}
+    del inp, ws
+    torch.cuda.empty_cache()
+    return out
+
+
+def native(nc, args, torch, L, synth):
+    """The layer at the native shape with logsumexp gates."""
+    inp, _, _, ws, _, ms, _ = time_forward(nc, max(5, min(args.steps, 10)), args.warmup,
+                                           torch, L, synth)
+    f_gu, f_dn = expert_flops(nc)
+    del inp, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"MoE layer at the native shape, {nc.describe()}, gates "
+                        f"{nc.gate_norm} x {nc.gate_scale}, fp32 router",
+            "tokens_s": round(nc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "mfma_frac": round((f_gu + f_dn) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -432,60 +480,26 @@ def main():
     del ws
     torch.cuda.empty_cache()
     if not args.no_ep_share:
-        result["ep_share"] = ep_share(cfg, inp, w, torch, L, synth, max(3, min(args.steps, 10)))
+        section(result, "ep_share",
+                lambda: ep_share(cfg, inp, w, torch, L, synth, max(3, min(args.steps, 10))))
     if not args.no_decode:
-        dc = configs.get(args.decode_workload)
-        dinp = time_forward(dc, max(args.steps, 20), args.warmup, torch, L, synth)
-        d_inp, d_desc, d_w, d_ws, d_counts, d_ms, d_ms_ev = dinp
-        d_stages, _, _ = time_stages(dc, d_inp, d_desc, d_w, 10, torch, L, synth)
-        nbytes, n_active = decode_bytes(dc, d_counts.cpu())
-        gbs = nbytes / (d_ms / 1e3) / 1e9
-        result["decode"] = {
-            "workload": f"decode MoE layer, {dc.describe()}, fp32 router",
-            "tokens_s": round(dc.T / (d_ms / 1e3), 1), "ms_per_step": round(d_ms, 4),
-            "stage_ms": {k: round(v, 4) for k, v in d_stages.items()},
-            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4),
-                         "bytes": nbytes, "active_experts": n_active,
-                         "scope": "whole moe_forward step"}}
-        del d_inp, d_ws
-        torch.cuda.empty_cache()
-        fc = configs.get(args.fp4_decode_workload)
-        f_inp, _, _, f_ws, f_counts, f_ms, _ = time_forward(fc, max(args.steps, 20),
-                                                            args.warmup, torch, L, synth)
-        f_bytes, f_active = decode_bytes(fc, f_counts.cpu())
-        f_gbs = f_bytes / (f_ms / 1e3) / 1e9
-        result["decode_fp4"] = {
-            "workload": f"decode MoE layer, {fc.describe()}, routed experts' weights MXFP4 "
-                        f"(E2M1, power-of-two scale per 32), shared experts bf16, fp32 router",
-            "tokens_s": round(fc.T / (f_ms / 1e3), 1), "ms_per_step": round(f_ms, 4),
-            "roofline": {"bound": "hbm", "achieved": round(f_gbs, 1), "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": round(f_gbs / PEAK_HBM_GBS, 4),
-                         "bytes": f_bytes, "active_experts": f_active,
-                         "scope": "whole moe_forward step"}}
-        del f_inp, f_ws
-        torch.cuda.empty_cache()
+        section(result, "decode", lambda: decode(configs.get(args.decode_workload), args,
+                                                 torch, L, synth))
+        section(result, "decode_fp4", lambda: decode(configs.get(args.fp4_decode_workload),
+                                                     args, torch, L, synth))
     if not args.no_native:
-        nc = configs.get(args.native_workload)
-        n_inp, _, _, n_ws, _, n_ms, _ = time_forward(nc, max(5, min(args.steps, 10)),
-                                                     args.warmup, torch, L, synth)
-        f_gu_n, f_dn_n = expert_flops(nc)
-        result["native"] = {
-            "workload": f"MoE layer at the native shape, {nc.describe()}, gates "
-                        f"{nc.gate_norm} x {nc.gate_scale}, fp32 router",
-            "tokens_s": round(nc.T / (n_ms / 1e3), 1), "ms_per_step": round(n_ms, 4),
-            "mfma_frac": round((f_gu_n + f_dn_n) / (n_ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
-        del n_inp, n_ws
-        torch.cuda.empty_cache()
+        section(result, "native", lambda: native(configs.get(args.native_workload), args,
+                                                 torch, L, synth))
     if not args.no_skewed:
-        result["skewed"] = time_skewed(configs.get(args.skewed_workload), args.skewed_steps,
-                                       torch, L, synth)
-        result["capacity"] = time_skewed(configs.get(args.capacity_workload),
-                                         args.skewed_steps, torch, L, synth)
+        section(result, "skewed", lambda: time_skewed(configs.get(args.skewed_workload),
+                                                      args.skewed_steps, torch, L, synth))
+        section(result, "capacity", lambda: time_skewed(configs.get(args.capacity_workload),
+                                                        args.skewed_steps, torch, L, synth))
     if not args.no_lab:
-        result["balance_lab"] = balance_lab(configs.get(args.lab_workload), torch)
+        section(result, "balance_lab", lambda: balance_lab(configs.get(args.lab_workload), torch))
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch)
+        section(result, "cpu_baseline",
+                lambda: cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch))
     print(json.dumps(result), flush=True)
 
 
