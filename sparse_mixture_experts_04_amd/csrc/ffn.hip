@@ -14,10 +14,13 @@
 //
 // XCD-aware order: workgroup w runs on XCD w % 8.  The item list is cut into
 // 8 contiguous chunks, one per XCD, and the 32 workgroups of an XCD take
-// consecutive items of their chunk.  Items of one group are ordered column
-// tile outer, row tile inner, so the workgroups running together on an XCD
-// share a weight tile (read from HBM once) and the group's activation rows
-// stay in that XCD's L2.
+// consecutive items of their chunk from a counter; a workgroup whose chunk
+// is used up takes what the other chunks have left (claim_item).  Items of
+// one group are ordered column tile outer, row tile inner, so the
+// workgroups running together on an XCD share a weight tile (read from HBM
+// once) and the group's activation rows stay in that XCD's L2.  (The FP4
+// kernel keeps a static slot order: its items are short and HBM-bound, and
+// a counter per item made it 15% slower.)
 #include "ffn_common.h"
 
 namespace moe {
@@ -25,8 +28,8 @@ namespace moe {
 // ------------------------------------------------------------- tile plan
 
 // tile_start[g] = first row tile of group g; tile_start[E+S] = total.  The
-// 2 * kXcds work counters that follow (one set for the gate/up GEMM, one for
-// the down GEMM that reuses this plan) are zeroed.
+// kCtrSets * kXcds work counters that follow (one set for the gate/up GEMM,
+// one for the down GEMM that reuses this plan) are zeroed.
 __global__ __launch_bounds__(512) void tile_plan_kernel(const int32_t* __restrict__ offsets,
                                                         int E, int S, int T, int MT,
                                                         int32_t* __restrict__ tile_start) {
@@ -47,7 +50,7 @@ __global__ __launch_bounds__(512) void tile_plan_kernel(const int32_t* __restric
   }
   if (g < G) tile_start[g] = sc[g] - nt;
   if (g == G - 1) tile_start[G] = sc[g];
-  if (g < 2 * kXcds) tile_start[G + 1 + g] = 0;
+  if (g < kCtrSets * kXcds) tile_start[G + 1 + g] = 0;
 }
 
 hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile,
@@ -241,11 +244,7 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   const long long first = static_cast<long long>(ts[p.g_lo]) * p.n_tiles;
   const long long total = (static_cast<long long>(ts[G]) * p.n_tiles - first) * ksplit;
   const int xcd = blockIdx.x & 7;
-  const int per_xcd = gridDim.x >> 3;
-  const int slot = blockIdx.x >> 3;
-  const long long chunk = (total + 7) / 8;
-  const long long beg = xcd * chunk;
-  const long long end = beg + chunk < total ? beg + chunk : total;
+  __shared__ long long s_item;
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
@@ -257,7 +256,12 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   static_assert(C::B_LOADS % 2 == 0, "B load parity follows q");
   const int nk_all = p.K / C::BK;
 
-  for (long long it = beg + slot; it < end; it += per_xcd) {
+  for (;;) {
+    // persistent: the next item of this XCD's chunk, then of the others'
+    if (tid == 0) s_item = claim_item(p.counters, xcd, total);
+    __syncthreads();
+    const long long it = s_item;
+    if (it < 0) break;
     const int ks = static_cast<int>(it % ksplit);
     const Item item = decode_item(first + it / ksplit, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
     const int kb = ks * nk_all / ksplit;                 // this slice's K steps
@@ -588,7 +592,9 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
   a.ldo = s.F;
   if (s.bf16) {
     a.n_tiles = s.F / 128;
-    if (row_tile != 32) return launch_big(a, true, tile_start, 0, marks, st);
+    if (row_tile != 32) return launch_big(a, true, tile_start, kCtrGateUp, marks, st);
+    int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1;
+    a.counters = ctr + kCtrGateUp * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {  // routed experts in FP4, then the bf16 shared experts
       hipError_t e = launch_fp4(a, true, st);
       if (e == hipSuccess) e = run_shared_bf16<true>(a, s, part, st);
@@ -625,7 +631,9 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const ui
   a.ldo = s.d;
   if (s.bf16) {
     a.n_tiles = s.d / 256;
-    if (row_tile != 32) return launch_big(a, false, tile_start, 1, marks, st);
+    if (row_tile != 32) return launch_big(a, false, tile_start, kCtrDown, marks, st);
+    int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1;
+    a.counters = ctr + kCtrDown * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {
       hipError_t e = launch_fp4(a, false, st);
       if (e == hipSuccess) e = run_shared_bf16<false>(a, s, part, st);

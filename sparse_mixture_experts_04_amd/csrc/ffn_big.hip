@@ -25,7 +25,10 @@
 // * Scheduling: persistent workgroups; the item list is cut into one
 //   contiguous chunk per XCD and the workgroups of an XCD take the next item
 //   of their chunk from a counter, so consecutive items (sharing weight and
-//   activation tiles) run together on one XCD and uneven items balance.
+//   activation tiles) run together on one XCD and uneven items balance.  A
+//   workgroup whose chunk is used up takes the remaining items of the other
+//   XCDs' chunks from their counters (7% faster at T=16384: the chunks hold
+//   equal item counts but unequal work).
 #include "ffn_common.h"
 
 namespace moe {
@@ -197,7 +200,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
   // stages the output tile for coalesced stores
   __shared__ __attribute__((aligned(1024))) bf16_t lds[(C::NSA + C::NSB) * C::STAGE_ELEMS];
   __shared__ int ts[512];
-  __shared__ int s_next;
+  __shared__ long long s_item;
   bf16_t* const sA[C::NSA] = {lds, lds + C::STAGE_ELEMS, lds + 2 * C::STAGE_ELEMS};
   bf16_t* sB[C::NSB];
 #pragma unroll
@@ -214,9 +217,6 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
 
   const long long total = static_cast<long long>(ts[G]) * p.n_tiles;
   const int xcd = blockIdx.x % kXcds;
-  const long long chunk = (total + kXcds - 1) / kXcds;
-  const long long beg = xcd * chunk;
-  const long long len = (beg + chunk < total ? beg + chunk : total) - beg;
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
@@ -229,12 +229,12 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
   const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
 
   for (;;) {
-    if (tid == 0) s_next = atomicAdd(&counters[xcd], 1);
+    // the next item of this XCD's chunk, then of the others' (claim_item)
+    if (tid == 0) s_item = claim_item(counters, xcd, total);
     __syncthreads();  // also: every wave is done with the previous item's LDS
-    const int local = s_next;
-    if (local >= len) break;
-    const Item item =
-        decode_item(beg + local, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E, true);
+    const long long gitem = s_item;
+    if (gitem < 0) break;
+    const Item item = decode_item(gitem, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E, true);
     const int g = item.g;
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
@@ -360,7 +360,7 @@ __global__ __launch_bounds__(512) void tile_plan_big_kernel(const int32_t* __res
   }
   if (g < G) plan[g] = sf[g] - nt;
   if (g == G - 1) plan[G] = sf[g];
-  if (g < 2 * kXcds) plan[G + 1 + g] = 0;
+  if (g < kCtrSets * kXcds) plan[G + 1 + g] = 0;
 }
 
 hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,

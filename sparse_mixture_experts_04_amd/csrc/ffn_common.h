@@ -86,7 +86,30 @@ struct FfnArgs {
   int g_lo;               // first group the 32-row bf16 kernel processes
   int ksplit;             // 32-row bf16 kernel, shared groups only: K slices per tile
   float* part;            // ksplit > 1: fp32 partial tiles [ksplit][S*T][n_tiles*256]
+  int32_t* counters;      // 32-row kernels: kXcds work counters, zero at launch
 };
+
+// Work counters after the last entry of a tile plan (zeroed by the kernel
+// that writes the plan): one set of kXcds for the gate/up GEMM and one for
+// the down GEMM that reuses the plan.
+enum { kCtrGateUp = 0, kCtrDown = 1, kCtrSets = 2 };
+
+// Next work item of a persistent workgroup on XCD `xcd`: the next index of
+// that XCD's contiguous chunk of [0, total), or once it is used up the next
+// unclaimed index of another XCD's chunk, or -1 when all are taken.  Each
+// counter hands out every index once.
+__device__ __forceinline__ long long claim_item(int32_t* counters, int xcd, long long total) {
+  const long long chunk = (total + kXcds - 1) / kXcds;
+  for (int h = 0; h < kXcds; ++h) {
+    const int x = (xcd + h) % kXcds;
+    const long long bx = x * chunk;
+    const long long lx = (bx + chunk < total ? bx + chunk : total) - bx;
+    if (lx <= 0) continue;
+    const int v = atomicAdd(&counters[x], 1);
+    if (v < lx) return bx + v;
+  }
+  return -1;
+}
 
 // K slices of the shared experts' tiles when the 32-row bf16 kernel runs
 // them alone (FP4 routed weights): enough items to cover 256 workgroups,

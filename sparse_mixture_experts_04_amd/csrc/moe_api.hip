@@ -11,7 +11,7 @@ using namespace moe;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kPlanCounters = 2 * kXcds;  // GEMM work counters after the tile plan
+constexpr int kPlanCounters = kCtrSets * kXcds;  // GEMM work counters after the tile plan
 
 size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
