@@ -101,6 +101,10 @@ __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* s
   }
 }
 
+// The weight fragment is the MFMA's first operand, so each accumulator block
+// is the transposed product (output columns down the lane's registers, tile
+// rows across lanes): a lane then holds 4 consecutive output columns of one
+// row, which the epilogue writes as one 8-byte word.
 __device__ __forceinline__ void big_mfma(const BigFrags& f, int nv,
                                          f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
   using C = BigCfg;
@@ -111,7 +115,7 @@ __device__ __forceinline__ void big_mfma(const BigFrags& f, int nv,
       if (i < nv)
 #pragma unroll
         for (int j = 0; j < C::BN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[kk][i], f.b[kk][j], acc[i][j],
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j],
                                                               0, 0, 0);
 }
 
@@ -293,38 +297,62 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     wait_vm<0>();
     __syncthreads();
 
-    // ---- epilogue: accumulators (lane l holds column l%32 and rows
-    // 8*(r/4) + 4*(l/32) + r%4 of each 32x32 block) -> bf16 tile in LDS ->
-    // 16-byte coalesced global stores of the valid rows.
+    // ---- epilogue: block (i, j) holds the transposed product: lane l ->
+    // tile row (2i + wm) * 32 + l % 32, registers 4q..4q+3 -> output
+    // columns 8q + 4 (l / 32) + 0..3 of column block j.  Each lane writes
+    // 8 bytes at a time into the LDS tile, whose 16-byte chunk c of row r
+    // sits in slot c ^ (r % CPR); then 16-byte coalesced global stores.
     constexpr int NOUT = GATED ? C::NB / 2 : C::NB;
+    constexpr int CPR = NOUT / 8;  // 16-byte chunks per row
     bf16_t* tile = lds;  // [MT][NOUT]
 #pragma unroll
     for (int i = 0; i < C::BM; ++i) {
+      const int row = (2 * i + wm) * 32 + (lane & 31);
+      bf16_t* trow = tile + row * NOUT + 4 * (lane >> 5);
+      const int sw = row & (CPR - 1);
+      if (GATED) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = (2 * i + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-        if (GATED) {
-          const float gt = acc[i][0][r];
-          const float up = acc[i][1][r];
-          tile[row * NOUT + wn * 32 + (lane & 31)] =
-              f32_to_bf16(gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up);
-        } else {
+        for (int q = 0; q < 4; ++q) {
+          uint32_t w[2];
 #pragma unroll
-          for (int j = 0; j < C::BN; ++j)
-            tile[row * NOUT + wn * 64 + j * 32 + (lane & 31)] = f32_to_bf16(acc[i][j][r]);
+          for (int t2 = 0; t2 < 2; ++t2) {
+            float v[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+              const float gt = acc[i][0][4 * q + 2 * t2 + e];
+              const float up = acc[i][1][4 * q + 2 * t2 + e];
+              v[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+            }
+            w[t2] = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                    (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+          }
+          const int ch = wn * 4 + q;
+          *reinterpret_cast<uint2*>(trow + ((ch ^ sw) << 3)) = make_uint2(w[0], w[1]);
         }
+      } else {
+#pragma unroll
+        for (int j = 0; j < C::BN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f32x16_t& a = acc[i][j];
+            const uint32_t w0 = static_cast<uint32_t>(f32_to_bf16(a[4 * q])) |
+                                (static_cast<uint32_t>(f32_to_bf16(a[4 * q + 1])) << 16);
+            const uint32_t w1 = static_cast<uint32_t>(f32_to_bf16(a[4 * q + 2])) |
+                                (static_cast<uint32_t>(f32_to_bf16(a[4 * q + 3])) << 16);
+            const int ch = wn * 8 + j * 4 + q;
+            *reinterpret_cast<uint2*>(trow + ((ch ^ sw) << 3)) = make_uint2(w0, w1);
+          }
       }
     }
     __syncthreads();
     bf16_t* out = static_cast<bf16_t*>(routed ? p.out_routed : p.out_shared);
     const size_t orow0 = routed ? static_cast<size_t>(p.offsets[g]) + item.m0
                                 : static_cast<size_t>(g - p.E) * p.T + item.m0;
-    constexpr int CPR = NOUT / 8;  // 16-byte chunks per row
     const int col0 = item.n * NOUT;
     for (int c = tid; c < item.rows * CPR; c += C::THREADS) {
       const int row = c / CPR, ch = c % CPR;
       *reinterpret_cast<uint4*>(out + (orow0 + row) * p.ldo + col0 + ch * 8) =
-          *reinterpret_cast<const uint4*>(tile + row * NOUT + ch * 8);
+          *reinterpret_cast<const uint4*>(tile + row * NOUT + ((ch ^ (row & (CPR - 1))) << 3));
     }
   }
 }

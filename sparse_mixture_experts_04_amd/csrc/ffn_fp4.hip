@@ -99,7 +99,7 @@ struct Fp4Cfg {
   static constexpr int MT = 32;
   static constexpr int NB = 256;
   static constexpr int BK = 128;
-  static constexpr int NS = 4;
+  static constexpr int NS = 3;                        // ring stages (two workgroups per CU)
   static constexpr int A_BYTES = MT * BK * 2;        // 8 KiB
   static constexpr int C_BYTES = NB * BK / 2;        // 16 KiB
   static constexpr int S_BYTES = NB * BK / 32;       // 1 KiB
@@ -185,9 +185,13 @@ __device__ __forceinline__ void fp4_stage(const uint8_t* st, int wn, int lane,
 
 // Routed groups only (the shared experts' weights are bf16 and go through
 // the bf16 kernel).  Persistent workgroups over the items of groups
-// 0..E-1, cut into one contiguous chunk per XCD.
+// 0..E-1, cut into one contiguous chunk per XCD.  Two workgroups share each
+// CU (a 3-stage ring each, 77 KiB of LDS): every item starts by waiting a
+// full HBM latency for its first stage, and the other workgroup's stream
+// covers that wait (8% faster at T=64 than one workgroup with a 4-stage
+// ring; 5 or 6 stages in one workgroup gain nothing).
 template <bool GATED>
-__global__ __launch_bounds__(256, 1) void ffn_fp4_kernel(FfnArgs p) {
+__global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
   using C = Fp4Cfg;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NS * C::STAGE];
   __shared__ int ts[512];
@@ -317,7 +321,7 @@ hipError_t launch_fp4(const FfnArgs& a, bool gated, hipStream_t st) {
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
-  const int grid = (cus + 7) / 8 * 8;
+  const int grid = 2 * ((cus + 7) / 8 * 8);  // two resident workgroups per CU
   if (gated) ffn_fp4_kernel<true><<<grid, 256, 0, st>>>(a);
   else ffn_fp4_kernel<false><<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
