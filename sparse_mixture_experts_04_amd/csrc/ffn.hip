@@ -81,7 +81,10 @@ int ffn_row_tile(const Shape& s) {
 // swz(r) = (r & 7) ^ ((r >> 3) & 1): the MFMA fragment reads (one chunk of
 // 32 consecutive rows) then hit distinct 16-byte bank groups both within
 // every 8 lanes (128-byte window) and within every 16 lanes (256-byte
-// window).
+// window).  An A load covers 8 rows and is skipped when none of them holds
+// a row of the tile (a decode tile holds a row or two): those LDS rows only
+// feed accumulator rows that are never stored, and the wave's wait counts
+// follow its number of loads.
 // Matrix cores: v_mfma_f32_32x32x16_bf16, fp32 accumulation.
 template <int MT, bool GATED>
 struct Bf16Cfg {
@@ -109,12 +112,13 @@ struct TileCtx {
   const bf16_t* b_src1;             // GATED: first W_up load
   size_t b_step;                    // elements between consecutive B loads (8 rows)
   int bch[2];                       // this lane's chunk offset for even / odd loads
+  int na;                           // A loads this wave issues per stage (wave-uniform)
 
   // Loads of one stage (K columns k0..k0+63) into the LDS tiles sA, sB.
   __device__ __forceinline__ void issue(int k0, bf16_t* sA, bf16_t* sB, int wave) const {
 #pragma unroll
     for (int q = 0; q < C::A_LOADS; ++q)
-      dma16(a_src[q] + k0, sA + (wave * C::A_LOADS + q) * 512);
+      if (q < na) dma16(a_src[q] + k0, sA + (wave * C::A_LOADS + q) * 512);
 #pragma unroll
     for (int q = 0; q < C::B_LOADS; ++q) {
       const bf16_t* src;
@@ -206,7 +210,9 @@ __device__ __forceinline__ void ring_step(const TileCtx<MT, GATED>& t, int kt, i
                                                          [Bf16Cfg<MT, GATED>::BN]) {
   using C = Bf16Cfg<MT, GATED>;
   constexpr int NXT = (U + C::NS - 1) % C::NS;
-  wait_vm<(C::NS - 2) * C::LPW>();
+  static_assert(C::A_LOADS == 1, "wait cases");
+  if (t.na) wait_vm<(C::NS - 2) * C::LPW>();
+  else wait_vm<(C::NS - 2) * (C::LPW - 1)>();
   lds_barrier();
   const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
   t.issue(kn * C::BK, sA[NXT], sB[NXT], wave);
@@ -272,6 +278,11 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
                                    : kT + static_cast<size_t>(g - p.E) * p.T;
     TileCtx<MT, GATED> t;
+    {
+      const int left = item.rows - 8 * wave * C::A_LOADS;   // rows from this wave's first group
+      const int groups = left <= 0 ? 0 : (left + 7) / 8;
+      t.na = groups < C::A_LOADS ? groups : C::A_LOADS;
+    }
 #pragma unroll
     for (int q = 0; q < C::A_LOADS; ++q) {
       int r = (wave * C::A_LOADS + q) * 8 + lrow;

@@ -91,9 +91,12 @@ hipError_t launch_quantize_mxfp4(long long E, int N, int K, const void* w, uint8
 //   A      32 rows x 256 B (bf16), 16-byte chunk c of row r in slot c ^ (r & 15);
 //   codes  256 rows x 64 B, chunk c of row r in slot c ^ ((r >> 2) & 3);
 //   scales 4 K blocks x 256 rows (bytes);
-// all filled with direct global -> LDS loads: per wave 2 A loads and 4 code
-// loads of 1 KiB and one 256-byte scale load (the scales of K block 4kt +
-// wave).  B fragments are read as 4 code bytes + 1 scale byte per lane and
+// all filled with direct global -> LDS loads: per wave up to 2 A loads and
+// 4 code loads of 1 KiB and one 256-byte scale load (the scales of K block
+// 4kt + wave).  An A load covers 4 rows and is skipped when none of them
+// holds a row of the tile (decode tiles hold a row or two): the LDS rows it
+// would fill only feed accumulator rows that are never stored, and the
+// wave's wait counts follow its number of loads.  B fragments are read as 4 code bytes + 1 scale byte per lane and
 // converted to bf16 in registers.
 struct Fp4Cfg {
   static constexpr int MT = 32;
@@ -131,12 +134,13 @@ struct Fp4Ctx {
   const bf16_t* a_src[C::A_LOADS];   // per lane, chunk applied, K offset 0
   const uint8_t* c_src[C::C_LOADS];  // per lane, chunk applied, K offset 0
   const uint8_t* s_src;              // per lane: 4 scale bytes of K block `wave`
+  int na;                            // A loads this wave issues per stage (wave-uniform)
 
   // loads of stage kt into the ring slot at LDS byte address `slot`
   __device__ __forceinline__ void issue(int kt, uint32_t slot, int wave, int sstride) const {
 #pragma unroll
     for (int q = 0; q < C::A_LOADS; ++q)
-      dma16_lds(a_src[q] + kt * C::BK, slot + (wave * C::A_LOADS + q) * 1024);
+      if (q < na) dma16_lds(a_src[q] + kt * C::BK, slot + (wave * C::A_LOADS + q) * 1024);
 #pragma unroll
     for (int q = 0; q < C::C_LOADS; ++q)
       dma16_lds(c_src[q] + kt * (C::BK / 2), slot + C::A_BYTES + (wave * C::C_LOADS + q) * 1024);
@@ -227,6 +231,11 @@ __global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
     const int g = item.g;  // routed
     const size_t row_base = static_cast<size_t>(p.offsets[g]);
     Fp4Ctx t;
+    {
+      const int left = item.rows - 4 * wave * C::A_LOADS;   // rows from this wave's first group
+      const int groups = left <= 0 ? 0 : (left + 3) / 4;
+      t.na = groups < C::A_LOADS ? groups : C::A_LOADS;
+    }
 #pragma unroll
     for (int q = 0; q < C::A_LOADS; ++q) {
       const int j = wave * C::A_LOADS + q;
@@ -285,8 +294,11 @@ __global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
 #pragma unroll
     for (int s = 0; s < C::NS - 1; ++s)
       t.issue(s < nk ? s : nk - 1, ring_base + s * C::STAGE, wave, p.N);
+    static_assert(C::NS == 3 && C::A_LOADS == 2, "wait cases");
     for (int kt = 0; kt < nk; ++kt) {
-      wait_vm<(C::NS - 2) * C::LPW>();
+      if (t.na == 2) wait_vm<C::LPW>();
+      else if (t.na == 1) wait_vm<C::LPW - 1>();
+      else wait_vm<C::LPW - 2>();
       lds_barrier();
       const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
       t.issue(kn, ring_base + ((kt + C::NS - 1) % C::NS) * C::STAGE, wave, p.N);
