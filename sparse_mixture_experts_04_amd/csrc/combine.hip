@@ -43,38 +43,48 @@ template <> struct Vec<float> {
   }
 };
 
-// Block b handles token b / nchunk, columns (b % nchunk) * 256 * VEC + ...
+// Block b handles token b / nchunk, columns (b % nchunk) * CB * VEC + ...
+// Every contributor row is loaded before the sums start, so the loads of a
+// thread are in flight together; a dropped pair loads row 0 (a valid
+// address) and is left out of the sum, which keeps the fixed order.
+constexpr int CB = 128;  // threads per block
 template <typename T, int K, int S>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ yr,
-                                                      const T* __restrict__ ys,
-                                                      const float* __restrict__ gates,
-                                                      const int32_t* __restrict__ pair_pos,
-                                                      int Tn, int d, int nchunk,
-                                                      T* __restrict__ y) {
+__global__ __launch_bounds__(CB) void combine_kernel(const T* __restrict__ yr,
+                                                     const T* __restrict__ ys,
+                                                     const float* __restrict__ gates,
+                                                     const int32_t* __restrict__ pair_pos,
+                                                     int Tn, int d, int nchunk,
+                                                     T* __restrict__ y) {
   constexpr int V = Vec<T>::N;
   const int t = blockIdx.x / nchunk;
-  const int c0 = ((blockIdx.x % nchunk) * 256 + threadIdx.x) * V;
+  const int c0 = ((blockIdx.x % nchunk) * CB + threadIdx.x) * V;
   if (c0 >= d) return;
+  int pos[K];
+  float g[K + S];
+#pragma unroll
+  for (int j = 0; j < K; ++j) pos[j] = pair_pos[static_cast<size_t>(t) * K + j];
+#pragma unroll
+  for (int j = 0; j < K + S; ++j) g[j] = gates[static_cast<size_t>(t) * (K + S) + j];
+  float v[K + S][V];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    Vec<T>::load(yr + static_cast<size_t>(pos[j] < 0 ? 0 : pos[j]) * d + c0, v[j]);
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+    Vec<T>::load(ys + (static_cast<size_t>(s) * Tn + t) * d + c0, v[K + s]);
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.0f;
-  float v[V];
 #pragma unroll
   for (int j = 0; j < K; ++j) {
-    const float g = gates[static_cast<size_t>(t) * (K + S) + j];
-    const int pos = pair_pos[static_cast<size_t>(t) * K + j];
-    if (pos < 0) continue;  // dropped at the expert's capacity
-    Vec<T>::load(yr + static_cast<size_t>(pos) * d + c0, v);
+    if (pos[j] < 0) continue;  // dropped at the expert's capacity
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g[j], v[j][i], acc[i]);
   }
 #pragma unroll
-  for (int s = 0; s < S; ++s) {
-    const float g = gates[static_cast<size_t>(t) * (K + S) + K + s];
-    Vec<T>::load(ys + (static_cast<size_t>(s) * Tn + t) * d + c0, v);
+  for (int s = 0; s < S; ++s)
 #pragma unroll
-    for (int i = 0; i < V; ++i) acc[i] = fmaf(g, v[i], acc[i]);
-  }
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g[K + s], v[K + s][i], acc[i]);
   Vec<T>::store(y + static_cast<size_t>(t) * d + c0, acc);
 }
 
@@ -82,9 +92,9 @@ template <typename T, int S>
 static void run_combine(const Shape& s, const void* y_routed, const void* y_shared,
                         const float* gates, const int32_t* pair_pos, void* y, hipStream_t st) {
   constexpr int V = Vec<T>::N;
-  const int nchunk = (s.d + 256 * V - 1) / (256 * V);
+  const int nchunk = (s.d + CB * V - 1) / (CB * V);
   const long long blocks = static_cast<long long>(s.T) * nchunk;
-  combine_kernel<T, 6, S><<<static_cast<unsigned>(blocks), 256, 0, st>>>(
+  combine_kernel<T, 6, S><<<static_cast<unsigned>(blocks), CB, 0, st>>>(
       static_cast<const T*>(y_routed), static_cast<const T*>(y_shared), gates, pair_pos, s.T,
       s.d, nchunk, static_cast<T*>(y));
 }
