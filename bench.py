@@ -89,9 +89,25 @@ def setup(cfg, torch, L, synth):
     return inp, desc, w, y, counts, ws
 
 
-def time_forward(cfg, steps, warmup, torch, L, synth):
+def spread(ms):
+    """p10, median and p90 of per-step times."""
+    v = sorted(ms)
+    return [round(v[len(v) // 10], 4), round(v[len(v) // 2], 4), round(v[(9 * len(v)) // 10], 4)]
+
+
+def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5):
+    """Times `steps` back-to-back forwards after `warmup` untimed ones.  The
+    bias is updated by every step, so later steps route differently (at
+    T=64 they touch more experts).  With `replay`, the same sequence is then
+    run again from the initial bias (the path is deterministic, so it routes
+    step for step as the timed run did): once in groups of `group` timed
+    steps between event pairs, for the spread of the per-step time, and once
+    untimed with each step's expert loads copied out, so that per-step
+    figures (bytes streamed) refer to the very steps that were timed.  The
+    last step's loads stay in `counts` either way."""
     inp, desc, w, y, counts, ws = setup(cfg, torch, L, synth)
-    bias = inp["bias"].clone()
+    bias0 = inp["bias"].clone()
+    bias = bias0.clone()
     routing = {"counts": counts}
 
     def step():
@@ -109,6 +125,29 @@ def time_forward(cfg, steps, warmup, torch, L, synth):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_events = ev0.elapsed_time(ev1) / steps
+    if replay:
+        ngroups = max(1, steps // group)
+        bias.copy_(bias0)
+        for _ in range(warmup):
+            step()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(ngroups)]
+        for a, b in evs:
+            a.record()
+            for _ in range(group):
+                step()
+            b.record()
+        torch.cuda.synchronize()
+        inp["_spread"] = spread([a.elapsed_time(b) / group for a, b in evs])
+        bias.copy_(bias0)
+        for _ in range(warmup):
+            step()
+        loads = torch.empty((steps, cfg.E), dtype=counts.dtype, device=counts.device)
+        for i in range(steps):
+            step()
+            loads[i].copy_(counts)
+        torch.cuda.synchronize()
+        inp["_loads"] = loads.cpu()
     return inp, desc, w, ws, counts, wall * 1e3 / steps, ms_events
 
 
@@ -187,6 +226,21 @@ def traffic_for(kernel_file, profile):
     return rec.get("bytes_per_launch")
 
 
+def load_profile(counts, mean_load):
+    """Routed-load profile of one batch: the five largest loads and the
+    smallest over the mean, and the slope of log load against log rank over
+    ranks 1-64 (a Zipf profile of exponent a has slope -a)."""
+    import numpy as np
+    v = np.sort(np.asarray(counts, dtype=np.float64))[::-1]
+    r = np.arange(1, 65)
+    head = v[:64]
+    ok = head > 0
+    slope = float(np.polyfit(np.log(r[ok]), np.log(head[ok]), 1)[0]) if ok.sum() > 1 else None
+    return {"top5_over_mean": [round(float(x) / mean_load, 3) for x in v[:5]],
+            "min_over_mean": round(float(v[-1]) / mean_load, 3),
+            "loglog_slope_ranks_1_64": None if slope is None else round(slope, 3)}
+
+
 def time_skewed(cfg, steps, torch, L, synth):
     """Consecutive batches of the skewed workload: fresh tokens every batch
     (generated outside the timed region), the bias carried from batch to
@@ -202,6 +256,7 @@ def time_skewed(cfg, steps, torch, L, synth):
         import numpy as np
         cap = math.ceil(float(np.float32(cfg.capacity_factor)) * float(cfg.k * cfg.T) / cfg.E)
     ms, maxmean, dropped = [], [], []
+    profile = None
     for s in range(steps + 1):          # batch 0 also warms up
         x = synth.make_x(cfg, device="cuda", step=s)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -212,6 +267,8 @@ def time_skewed(cfg, steps, torch, L, synth):
         if s > 0:
             ms.append(e0.elapsed_time(e1))
         maxmean.append(counts.max().item() / mean_load)
+        if s == 0:
+            profile = load_profile(counts.cpu().numpy(), mean_load)
         if cap is not None:
             dropped.append((counts - cap).clamp(min=0).sum().item() / (cfg.k * cfg.T))
     f_gu, f_dn = expert_flops(cfg)
@@ -231,6 +288,7 @@ def time_skewed(cfg, steps, torch, L, synth):
                                    "middle": round(maxmean[len(maxmean) // 2], 3),
                                    "last": round(maxmean[-1], 3)},
             "bias_range": [round(bias.min().item(), 5), round(bias.max().item(), 5)],
+            "load_profile_first_batch": profile,
             **({"capacity_rows": cap,
                 "drop_rate": {"first": round(dropped[0], 4),
                               "middle": round(dropped[len(dropped) // 2], 4),
@@ -369,9 +427,19 @@ def cpu_baseline(cfg, inp, ntok, torch):
     out = O.moe_forward(x, wr, weights, bias, cfg.gamma, k=cfg.k)
     dt = time.perf_counter() - t0
     assert out["y"].shape == (ntok, cfg.d)
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    info = threadpool_info()
+    threads = max([i.get("num_threads", 1) for i in info] + [1])
+    blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
+                   if i.get("user_api") == "blas"})
+    cpu = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")),
+                       None)
+    except OSError:
+        pass
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2),
+            "seconds": round(dt, 2), "cpu": cpu, "blas": blas,
             "sample": (f"first {ntok} tokens of the T={cfg.T} batch: full oracle forward "
                        f"(fp64 router, dispatch, {len(need)} routed + {cfg.S} shared SwiGLU "
                        f"experts, combine, bias update)")}
@@ -392,21 +460,29 @@ def section(result, key, fn):
 def decode(dc, args, torch, L, synth):
     """A decode workload (bf16 or FP4 routed weights) against HBM bandwidth."""
     steps = max(args.steps, 20)
-    inp, desc, w, ws, counts, ms, _ = time_forward(dc, steps, args.warmup, torch, L, synth)
+    inp, desc, w, ws, counts, ms, _ = time_forward(dc, steps, args.warmup, torch, L, synth,
+                                                   replay=True)
     stages = None
     if not dc.fp4_weights:
         stages, _, _ = time_stages(dc, inp, desc, w, 10, torch, L, synth)
-    nbytes, n_active = decode_bytes(dc, counts.cpu())
+    # bytes of each timed step (its own active experts), averaged
+    per_step = [decode_bytes(dc, c) for c in inp.pop("_loads")]
+    nbytes = int(round(sum(b for b, _ in per_step) / len(per_step)))
+    actives = [n for _, n in per_step]
+    n_active = round(sum(actives) / len(actives), 1)
     gbs = nbytes / (ms / 1e3) / 1e9
     weights = ("routed experts' weights MXFP4 (E2M1, power-of-two scale per 32), shared "
                "experts bf16" if dc.fp4_weights else "bf16 weights")
     out = {"workload": f"decode MoE layer, {dc.describe()}, {weights}, fp32 router",
-           "tokens_s": round(dc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4)}
+           "tokens_s": round(dc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+           "ms_per_step_p10_p50_p90": inp.pop("_spread")}
     if stages is not None:
         out["stage_ms"] = {k: round(v, 4) for k, v in stages.items()}
     out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
                        "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
-                       "active_experts": n_active, "scope": "whole moe_forward step"}
+                       "active_experts": n_active,
+                       "active_experts_first_last": [actives[0], actives[-1]],
+                       "scope": "whole moe_forward step; bytes averaged over the timed steps"}
     del inp, ws
     torch.cuda.empty_cache()
     return out
@@ -444,7 +520,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     inp, desc, w, ws, counts, ms_wall, ms_ev = time_forward(cfg, args.steps, args.warmup,
-                                                            torch, L, synth)
+                                                            torch, L, synth, replay=True)
     stages, kernels, st_counts = time_stages(cfg, inp, desc, w, max(3, min(args.steps, 10)),
                                              torch, L, synth)
     f_gu, f_dn = expert_flops(cfg)
@@ -464,6 +540,7 @@ def main():
         "layer_tflops": round((f_gu + f_dn) / (ms / 1e3) / 1e12, 1),
         "layer_mfma_frac": round((f_gu + f_dn) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_events": round(ms_ev, 4),
+        "ms_per_step_p10_p50_p90": inp.pop("_spread"),   # over groups of 5 of the timed steps
         "stage_ms": {k: round(v, 4) for k, v in stages.items()},
         "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
         "roofline": {"kernel": "ffn_big_kernel<gate/up> (grouped gate/up GEMM + SwiGLU, "
