@@ -149,7 +149,11 @@ __device__ __forceinline__ void wait_vm() {
 // inline asm so that the compiler does not track these LDS writes (it would
 // otherwise fall back to waiting for every outstanding load before each LDS
 // read); the ring synchronises them explicitly with vmcnt waits and
-// barriers.  The asm has no output registers.
+// barriers.  The asm has no output registers.  It names m0 as clobbered;
+// the compiler reserves m0 and warns that it does not save it around asm,
+// which is harmless here: in the generated gfx950 code of these kernels
+// every write and read of m0 is one of these asm blocks (no register-array
+// indexing through m0, no messages, no compiler-issued LDS DMA).
 __device__ __forceinline__ void dma16(const bf16_t* src, bf16_t* dst) {
   const uint32_t lds = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(dst))));
