@@ -97,7 +97,7 @@ struct Bf16Cfg {
   static constexpr int BM = WM / 32;
   static constexpr int BN = WN / 32;
   static constexpr int NOUT = GATED ? NB / 2 : NB;
-  static constexpr int NS = MT >= 128 ? 3 : 4;          // LDS ring stages
+  static constexpr int NS = MT >= 64 ? 3 : 4;           // LDS ring stages
   static constexpr int A_LOADS = MT * 128 / 1024 / 4;   // KiB loads per wave per stage
   static constexpr int B_LOADS = NB * 128 / 1024 / 4;
   static constexpr int LPW = A_LOADS + B_LOADS;
@@ -210,9 +210,10 @@ __device__ __forceinline__ void ring_step(const TileCtx<MT, GATED>& t, int kt, i
                                                          [Bf16Cfg<MT, GATED>::BN]) {
   using C = Bf16Cfg<MT, GATED>;
   constexpr int NXT = (U + C::NS - 1) % C::NS;
-  static_assert(C::A_LOADS == 1, "wait cases");
-  if (t.na) wait_vm<(C::NS - 2) * C::LPW>();
-  else wait_vm<(C::NS - 2) * (C::LPW - 1)>();
+  static_assert(C::A_LOADS <= 2, "wait cases");
+  if (t.na == C::A_LOADS) wait_vm<(C::NS - 2) * C::LPW>();
+  else if (t.na == C::A_LOADS - 1) wait_vm<(C::NS - 2) * (C::LPW - 1)>();
+  else wait_vm<(C::NS - 2) * (C::LPW - 2)>();
   lds_barrier();
   const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
   t.issue(kn * C::BK, sA[NXT], sB[NXT], wave);
@@ -245,10 +246,15 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   __syncthreads();
 
   // items of groups g_lo..G-1, each tile cut into ksplit K slices (slice
-  // index innermost, so the slices of a tile run side by side)
+  // index innermost, so the slices of a tile run side by side).  The
+  // 64-row instantiation serves the shared experts alone: each has T rows,
+  // in ceil(T / 64) row tiles, and its items are numbered directly.
   const int ksplit = p.ksplit > 1 ? p.ksplit : 1;
-  const long long first = static_cast<long long>(ts[p.g_lo]) * p.n_tiles;
-  const long long total = (static_cast<long long>(ts[G]) * p.n_tiles - first) * ksplit;
+  const int srt = (p.T + MT - 1) / MT;   // row tiles of a shared expert (MT == 64)
+  const long long first = MT == 64 ? 0 : static_cast<long long>(ts[p.g_lo]) * p.n_tiles;
+  const long long total =
+      MT == 64 ? static_cast<long long>(p.S) * srt * p.n_tiles * ksplit
+               : (static_cast<long long>(ts[G]) * p.n_tiles - first) * ksplit;
   const int xcd = blockIdx.x & 7;
   __shared__ long long s_item;
 
@@ -269,7 +275,20 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
     const long long it = s_item;
     if (it < 0) break;
     const int ks = static_cast<int>(it % ksplit);
-    const Item item = decode_item(first + it / ksplit, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
+    Item item;
+    if constexpr (MT == 64) {
+      // shared expert, column tile outer, row tile inner
+      const long long t2 = it / ksplit;
+      const int per = srt * p.n_tiles;
+      const int local = static_cast<int>(t2 % per);
+      item.g = p.E + static_cast<int>(t2 / per);
+      item.n = local / srt;
+      item.m0 = (local % srt) * MT;
+      item.grows = p.T;
+      item.rows = p.T - item.m0 < MT ? p.T - item.m0 : MT;
+    } else {
+      item = decode_item(first + it / ksplit, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
+    }
     const int kb = ks * nk_all / ksplit;                 // this slice's K steps
     const int nk = (ks + 1) * nk_all / ksplit - kb;
     const size_t koff = static_cast<size_t>(kb) * C::BK;
@@ -524,15 +543,17 @@ __global__ __launch_bounds__(256) void shared_reduce_kernel(const float* __restr
 size_t shared_partial_floats(const Shape& s) {
   if (!s.w_fp4 || !s.bf16 || s.S == 0) return 0;
   const size_t rows = static_cast<size_t>(s.S) * s.T;
-  const int kg = shared_ksplit(s, s.F / 128, s.d / 64);
-  const int kd = shared_ksplit(s, s.d / 256, s.F / 64);
+  const int kg = shared_ksplit(s, s.F / 128, s.d / 64, kSharedRows);
+  const int kd = shared_ksplit(s, s.d / 256, s.F / 64, kSharedRows);
   const size_t g = kg > 1 ? kg * rows * 2 * s.F : 0;
   const size_t d = kd > 1 ? kd * rows * s.d : 0;
   return g > d ? g : d;
 }
 
-// The shared experts alone on the 32-row bf16 kernel (FP4 routed weights),
-// K-sliced when their tiles are too few to fill the chip.
+// The shared experts alone on the bf16 kernel with 64-row tiles (FP4 routed
+// weights), K-sliced when their tiles are too few to fill the chip.  At
+// decode sizes a shared expert's rows then sit in one row tile, so each of
+// its weight bytes passes through one CU rather than one per 32 rows.
 template <bool GATED>
 static hipError_t run_shared_bf16(FfnArgs a, const Shape& s, float* part, hipStream_t st);
 
@@ -553,10 +574,10 @@ template <bool GATED>
 static hipError_t run_shared_bf16(FfnArgs a, const Shape& s, float* part, hipStream_t st) {
   if (s.S == 0) return hipSuccess;
   a.g_lo = s.E;
-  a.ksplit = shared_ksplit(s, a.n_tiles, a.K / 64);
+  a.ksplit = shared_ksplit(s, a.n_tiles, a.K / 64, kSharedRows);
   a.part = a.ksplit > 1 ? part : nullptr;
   if (a.ksplit > 1 && !part) return hipErrorInvalidValue;
-  hipError_t e = run_bf16<32, GATED>(a, st);
+  hipError_t e = run_bf16<kSharedRows, GATED>(a, st);
   if (e != hipSuccess || !a.part) return e;
   const int rows = s.S * s.T;
   const int nout = GATED ? s.F : s.d;

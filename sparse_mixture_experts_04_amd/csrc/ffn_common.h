@@ -111,14 +111,18 @@ __device__ __forceinline__ long long claim_item(int32_t* counters, int xcd, long
   return -1;
 }
 
-// K slices of the shared experts' tiles when the 32-row bf16 kernel runs
-// them alone (FP4 routed weights): enough items to cover 256 workgroups,
-// at most 4 slices and never more than the K steps (nk) of a tile.
-inline int shared_ksplit(const Shape& s, int n_tiles, int nk) {
-  const long long items = static_cast<long long>(s.S) * ((s.T + 31) / 32) * n_tiles;
+// Row tile of the shared-expert GEMMs when the bf16 kernel runs them alone
+// (beside FP4 routed experts).
+constexpr int kSharedRows = 64;
+
+// K slices of those tiles (S * ceil(T / rows) * n_tiles of them): enough
+// items to cover 256 workgroups, at most 8 slices and never more than the
+// K steps (nk) of a tile.
+inline int shared_ksplit(const Shape& s, int n_tiles, int nk, int rows) {
+  const long long items = static_cast<long long>(s.S) * ((s.T + rows - 1) / rows) * n_tiles;
   if (items <= 0) return 1;
   long long k = (256 + items - 1) / items;
-  k = k > 4 ? 4 : k;
+  k = k > 8 ? 8 : k;
   k = k > nk ? nk : k;
   return static_cast<int>(k < 1 ? 1 : k);
 }
