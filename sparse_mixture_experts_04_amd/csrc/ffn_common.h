@@ -86,7 +86,7 @@ struct FfnArgs {
   int g_lo;               // first group the 32-row bf16 kernel processes
   int ksplit;             // 32-row bf16 kernel, shared groups only: K slices per tile
   float* part;            // ksplit > 1: fp32 partial tiles [ksplit][S*T][n_tiles*256]
-  int32_t* counters;      // 32-row kernels: kXcds work counters, zero at launch
+  int32_t* counters;      // ffn_bf16_kernel: kXcds work counters, zero at launch
 };
 
 // Work counters after the last entry of a tile plan (zeroed by the kernel
@@ -178,8 +178,8 @@ hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t*
 hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
                       hipEvent_t* marks, hipStream_t st);
 // Tile plan of the large-batch GEMM: [row tiles per group, exclusive
-// prefix (G+1) | work counters 2 GEMMs x kXcds].
-inline int big_plan_ints(int G) { return (G + 1) + 2 * kXcds; }
+// prefix (G+1) | work counters kCtrSets GEMMs x kXcds].
+inline int big_plan_ints(int G) { return (G + 1) + kCtrSets * kXcds; }
 
 // Decode-batch GEMMs over the routed groups with FP4 weights (ffn_fp4.hip).
 hipError_t launch_fp4(const FfnArgs& a, bool gated, hipStream_t st);
