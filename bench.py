@@ -331,11 +331,25 @@ def balance_lab(cfg, torch, gammas=(0.0, 0.01, 0.05)):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / len(xs)
+    # the same steps replayed from one HIP graph (the step is launch-bound)
+    graph = lab.capture(xs)
+    lab.reset()
+    graph.replay()
+    lab.reset()
+    torch.cuda.synchronize()
+    e0.record()
+    graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_graph = e0.elapsed_time(e1) / len(xs)
+    del graph
     return {"workload": f"Router Balance Lab, {cfg.describe()}, frozen router, "
                         f"Zipf-lumpy tokens (head/tail {cfg.lab_head_tail:g}), capacity "
                         f"{cfg.capacity_factor} x ideal, {cfg.steps} steps, routing only",
             "measures_mean_over_steps": runs,
-            "ms_per_step": round(ms, 4), "tokens_s": round(cfg.T / (ms / 1e3), 1)}
+            "ms_per_step": round(ms, 4), "tokens_s": round(cfg.T / (ms / 1e3), 1),
+            "ms_per_step_hip_graph": round(ms_graph, 4),
+            "tokens_s_hip_graph": round(cfg.T / (ms_graph / 1e3), 1)}
 
 
 def ep_share(cfg, inp, w, torch, L, synth, steps):

@@ -60,6 +60,29 @@ class BalanceLab:
                    self.pair_pos, ws=self.ws_dispatch)
         L.bias_update(self.desc, self.counts, self.gamma, self.bias)
 
+    def capture(self, xs):
+        """A HIP graph of the routing steps over the device batches ``xs``
+        (one step per batch, in order), for replay without per-launch host
+        cost.  The graph reads and updates ``self.bias`` in place, so a replay
+        continues from whatever bias the buffer holds.  The step's calls
+        launch kernels only (no memset, copy, allocation or sync), so they
+        capture as they run."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        saved = self.bias.clone()
+        with torch.cuda.stream(side):      # warm-up on a side stream before capture
+            for x in xs[:2]:
+                self.step(x)
+        torch.cuda.current_stream().wait_stream(side)
+        self.bias.copy_(saved)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for x in xs:
+                self.step(x)
+        torch.cuda.synchronize()
+        self.bias.copy_(saved)
+        return g
+
     def measures(self, x):
         """(max_vio, drop_rate, quality) of the last step on tokens x, as
         float64 device scalars (no host synchronisation)."""

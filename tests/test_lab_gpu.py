@@ -120,3 +120,34 @@ def test_routing_entry_points_narrow_d(name):
     err = np.abs(got - ref) - (ulp * np.abs(ref) + 1e-6 * mag)
     log(f"  routing {st}; dropped {int(T * k - dp['offsets'][-1])} pairs")
     assert np.all(err <= 0.0), float(err.max())
+
+
+def test_lab_graph_replays_match_eager():
+    """The lab's 100 routing steps captured in one HIP graph: three replays,
+    each from a zero bias with eager torch work and synchronisations between
+    them, and each leaves bit for bit the bias and routing tables of the
+    eager run of the same steps."""
+    cfg = configs.get("Lab")
+    log(f"[lab graph] {cfg.describe()}")
+    w = synth.make_lab_router(cfg).to(DEV)
+    xs = [synth.make_lab_x(cfg, i, device=DEV) for i in range(cfg.steps)]
+    lab = BalanceLab(cfg, w, cfg.gamma, DEV)
+    for x in xs:
+        lab.step(x)
+    torch.cuda.synchronize()
+    names = ("bias", "topk", "gates", "counts", "offsets", "sorted_pair", "pair_pos")
+    eager = {n: getattr(lab, n).clone() for n in names}
+    lab.reset()
+    graph = lab.capture(xs)
+    for rep in range(3):
+        lab.reset()
+        for n in names[1:]:
+            getattr(lab, n).fill_(-7)          # eager writes the graph must overwrite
+        junk = torch.randn(1 << 16, device=DEV).sum()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for n in names:
+            got, ref = getattr(lab, n), eager[n]
+            assert torch.equal(got, ref), f"replay {rep}: {n} differs"
+        assert torch.isfinite(junk)
