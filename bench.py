@@ -95,6 +95,18 @@ def spread(ms):
     return [round(v[len(v) // 10], 4), round(v[len(v) // 2], 4), round(v[(9 * len(v)) // 10], 4)]
 
 
+def capture_steps(step, n, torch):
+    """One HIP graph of `n` calls of `step` (a forward through the C ABI on
+    preallocated buffers: kernels only, no memset, copy or sync).  Every
+    kernel has run eagerly before, so nothing initialises during capture."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n):
+            step()
+    torch.cuda.synchronize()
+    return g
+
+
 def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5):
     """Times `steps` back-to-back forwards after `warmup` untimed ones.  The
     bias is updated by every step, so later steps route differently (at
@@ -148,6 +160,20 @@ def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5):
             loads[i].copy_(counts)
         torch.cuda.synchronize()
         inp["_loads"] = loads.cpu()
+        # the timed steps once more, replayed from one HIP graph
+        bias.copy_(bias0)
+        for _ in range(warmup):
+            step()
+        start = bias.clone()
+        graph = capture_steps(step, steps, torch)
+        bias.copy_(start)
+        torch.cuda.synchronize()
+        ev0.record()
+        graph.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        inp["_graph_ms"] = ev0.elapsed_time(ev1) / steps
+        del graph
     return inp, desc, w, ws, counts, wall * 1e3 / steps, ms_events
 
 
@@ -489,7 +515,8 @@ def decode(dc, args, torch, L, synth):
                "experts bf16" if dc.fp4_weights else "bf16 weights")
     out = {"workload": f"decode MoE layer, {dc.describe()}, {weights}, fp32 router",
            "tokens_s": round(dc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
-           "ms_per_step_p10_p50_p90": inp.pop("_spread")}
+           "ms_per_step_p10_p50_p90": inp.pop("_spread"),
+           "ms_per_step_hip_graph": round(inp.pop("_graph_ms"), 4)}
     if stages is not None:
         out["stage_ms"] = {k: round(v, 4) for k, v in stages.items()}
     out["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
@@ -555,6 +582,7 @@ def main():
         "layer_mfma_frac": round((f_gu + f_dn) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ms_per_step_events": round(ms_ev, 4),
         "ms_per_step_p10_p50_p90": inp.pop("_spread"),   # over groups of 5 of the timed steps
+        "ms_per_step_hip_graph": round(inp.pop("_graph_ms"), 4),
         "stage_ms": {k: round(v, 4) for k, v in stages.items()},
         "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
         "roofline": {"kernel": "ffn_big_kernel<gate/up> (grouped gate/up GEMM + SwiGLU, "
