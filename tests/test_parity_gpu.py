@@ -328,3 +328,47 @@ def test_expert_ffn_ep_share_sampled():
     assert worst <= 2e-2
     del inp, b
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("T", [1000, 4096])
+def test_identical_tokens_with_an_exact_tie(T):
+    """Every token the same, and the 6th choice's routing vector copied into
+    a lower-numbered expert, so the two keys are exactly equal for every
+    token: the lower id must win everywhere ("Inkling, Dissected", 02b,
+    with ties to the lower index), six experts then hold T rows each and the
+    other 250 none (T = 1000 runs the 32-row GEMM, T = 4096 the large one),
+    the bias moves down for the six and up for the rest, and the outputs
+    match the oracle's."""
+    cfg = MoEConfig(f"same_{T}", T=T, d=512, F=256, act="bf16", bias_range=0.0)
+    log(f"[identical tokens] {cfg.describe()}")
+    inp = synth.make_inputs(cfg, device="cpu")
+    inp["x"][:] = inp["x"][0]
+    x0 = inp["x"][0].double().numpy()
+    z = np64(inp["w_router"][: cfg.E]) @ x0
+    order = np.argsort(-z, kind="stable")
+    j6 = int(order[5])
+    i_low = int(min(e for e in range(cfg.E) if e not in set(order[:6].tolist())))
+    assert i_low < j6
+    inp["w_router"][i_low] = inp["w_router"][j6]
+    inp = to_dev(inp)
+    desc = desc_for(cfg)
+    b, bias_new = run_stages(desc, inp, cfg.gamma)
+
+    topk = npi(b.topk)
+    want = np.array(list(order[:5]) + [i_low])
+    assert np.array_equal(topk, np.broadcast_to(want, topk.shape)), topk[:2]
+    x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
+    r, g_ref, _ = check_routing(x64, wr64, b64, topk, np64(b.gates))
+    assert np.array_equal(r["topk_idx"], topk)        # the oracle breaks the tie the same way
+    dp = check_dispatch(topk, b, E=cfg.E)
+    assert sorted(np.nonzero(dp["counts"])[0].tolist()) == sorted(want.tolist())
+    assert set(dp["counts"][want].tolist()) == {T}
+    check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
+    hw = host_weights(inp)
+    yr_ref, ys_ref = O.expert_ffn(x64, hw, dp["offsets"], dp["sorted_pair"], cfg.k)
+    y_ref = O.combine(yr_ref, ys_ref, g_ref, dp["pair_pos"], cfg.k)
+    e_y = rel_l2(np64(b.y), y_ref)
+    log(f"  tie {i_low} over {j6}; rel L2 y {e_y:.2e}")
+    assert e_y <= out_tol(cfg)
+    y = np64(b.y)
+    assert np.array_equal(y, np.broadcast_to(y[0], y.shape))   # identical rows out
