@@ -107,7 +107,7 @@ def capture_steps(step, n, torch):
     return g
 
 
-def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5):
+def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5, marked=False):
     """Times `steps` back-to-back forwards after `warmup` untimed ones.  The
     bias is updated by every step, so later steps route differently (at
     T=64 they touch more experts).  With `replay`, the same sequence is then
@@ -116,25 +116,49 @@ def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5):
     steps between event pairs, for the spread of the per-step time, and once
     untimed with each step's expert loads copied out, so that per-step
     figures (bytes streamed) refer to the very steps that were timed.  The
-    last step's loads stay in `counts` either way."""
+    last step's loads stay in `counts` either way.  With `marked`, the timed
+    steps call moe_forward_marked, whose events between the stages give
+    every step's stage and GEMM-kernel times (averaged into
+    inp["_marks_ms"])."""
     inp, desc, w, y, counts, ws = setup(cfg, torch, L, synth)
     bias0 = inp["bias"].clone()
     bias = bias0.clone()
     routing = {"counts": counts}
 
-    def step():
-        L.forward(desc, inp["x"], w, bias, cfg.gamma, y, routing, ws=ws)
+    def step(events=None):
+        L.forward(desc, inp["x"], w, bias, cfg.gamma, y, routing, ws=ws, events=events)
 
+    marks = [None] * steps
+    if marked:
+        marks = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+        for m in marks:
+            for e in m:
+                e.record()          # the raw handles exist once an event was recorded
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
-    for _ in range(steps):
-        step()
+    for i in range(steps):
+        step(marks[i])
     ev1.record()
     torch.cuda.synchronize()
+    if marked:
+        # marks: router, dispatch, tile plan, gate/up GEMM, down GEMM, combine, bias
+        acc = {n: 0.0 for n in ("router", "dispatch", "gate_up", "down", "combine",
+                                "bias_update", "gate_up_gemm", "down_gemm")}
+        for i, m in enumerate(marks):
+            start = ev0 if i == 0 else marks[i - 1][6]
+            acc["router"] += start.elapsed_time(m[0])
+            acc["dispatch"] += m[0].elapsed_time(m[1])
+            acc["gate_up"] += m[1].elapsed_time(m[3])
+            acc["gate_up_gemm"] += m[2].elapsed_time(m[3])
+            acc["down"] += m[3].elapsed_time(m[4])
+            acc["down_gemm"] += m[3].elapsed_time(m[4])
+            acc["combine"] += m[4].elapsed_time(m[5])
+            acc["bias_update"] += m[5].elapsed_time(m[6])
+        inp["_marks_ms"] = {n: v / steps for n, v in acc.items()}
     wall = time.perf_counter() - t0
     ms_events = ev0.elapsed_time(ev1) / steps
     if replay:
@@ -561,9 +585,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     inp, desc, w, ws, counts, ms_wall, ms_ev = time_forward(cfg, args.steps, args.warmup,
-                                                            torch, L, synth, replay=True)
-    stages, kernels, st_counts = time_stages(cfg, inp, desc, w, max(3, min(args.steps, 10)),
-                                             torch, L, synth)
+                                                            torch, L, synth, replay=True,
+                                                            marked=True)
+    # stage and GEMM-kernel times of the timed steps themselves (events that
+    # moe_forward_marked records between its launches on the same stream)
+    mk = inp.pop("_marks_ms")
+    stages = {n: mk[n] for n in ("router", "dispatch", "gate_up", "down", "combine",
+                                 "bias_update")}
+    kernels = {"gate_up_gemm": mk["gate_up_gemm"], "down_gemm": mk["down_gemm"]}
     f_gu, f_dn = expert_flops(cfg)
     ms = ms_wall
     tokens_s = cfg.T / (ms / 1e3)

@@ -288,6 +288,19 @@ moe_status moe_forward(const moe_desc* desc, const void* x,
                        const moe_routing* routing_or_null, void* ws,
                        size_t ws_bytes, hipStream_t stream);
 
+/* Profiling variant of moe_forward, for timing its stages and GEMM kernels
+ * with events on the caller's stream inside a timed run of the layer.
+ * Same arguments, results and workspace; in addition marks[0..6] are
+ * recorded after the router, the dispatch, the GEMMs' tile plan, the
+ * gate/up GEMM, the down GEMM, the combine and the bias update (marks[6]
+ * also when gamma == 0).  marks[0..6] must be valid events (MOE_ERR_NULL
+ * otherwise). */
+moe_status moe_forward_marked(const moe_desc* desc, const void* x,
+                              const moe_weights* w, float* bias, float gamma,
+                              void* y, const moe_routing* routing_or_null,
+                              void* ws, size_t ws_bytes, hipEvent_t* marks,
+                              hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

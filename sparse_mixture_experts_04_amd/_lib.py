@@ -24,7 +24,7 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE"
 SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router",
            "moe_dispatch", "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn",
            "moe_combine", "moe_bias_update", "moe_forward", "moe_expert_gate_up_marked",
-           "moe_expert_down_marked", "moe_quantize_mxfp4")
+           "moe_expert_down_marked", "moe_quantize_mxfp4", "moe_forward_marked")
 
 
 class MoEError(RuntimeError):
@@ -75,6 +75,8 @@ def _load(path=LIB_PATH):
         "moe_combine": (I, [D, P, P, P, P, P, P]),
         "moe_bias_update": (I, [D, P, ctypes.c_float, P, P]),
         "moe_forward": (I, [D, P, W, P, ctypes.c_float, P, ctypes.POINTER(Routing), P, Z, P]),
+        "moe_forward_marked": (I, [D, P, W, P, ctypes.c_float, P, ctypes.POINTER(Routing), P, Z,
+                                   P, P]),
         "moe_quantize_mxfp4": (I, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, P, P, P, P]),
     }
     for name, (res, args) in sig.items():
@@ -255,10 +257,10 @@ def expert_down(desc, weights, offsets, h, y_routed, y_shared, ws=None):
     _check("moe_expert_down", st)
 
 
-def _marks(events):
-    if len(events) != 2:
-        raise ValueError("two events are needed")
-    arr = (ctypes.c_void_p * 2)(*[e.cuda_event for e in events])
+def _marks(events, n=2):
+    if len(events) != n:
+        raise ValueError(f"{n} events are needed")
+    arr = (ctypes.c_void_p * n)(*[e.cuda_event for e in events])
     return arr
 
 
@@ -319,9 +321,13 @@ def bias_update(desc, counts, gamma, bias):
     _check("moe_bias_update", st)
 
 
-def forward(desc, x, weights, bias, gamma, y, routing=None, ws=None):
+def forward(desc, x, weights, bias, gamma, y, routing=None, ws=None, events=None):
     """moe_forward.  ``routing`` is an optional dict of output tensors with
-    keys topk_idx, gates, margin, counts, offsets, sorted_pair, pair_pos."""
+    keys topk_idx, gates, margin, counts, offsets, sorted_pair, pair_pos.
+    With ``events`` (7 torch.cuda.Event, enable_timing=True, each recorded
+    once beforehand) it calls moe_forward_marked, which records them after
+    the router, dispatch, tile plan, gate/up GEMM, down GEMM, combine and
+    bias update."""
     ws = alloc_workspace(desc, CALL_FORWARD, bias.device) if ws is None else ws
     T, d, k, S, E = desc.T, desc.d, desc.k, desc.S, desc.E
     r = None
@@ -333,9 +339,13 @@ def forward(desc, x, weights, bias, gamma, y, routing=None, ws=None):
         r = Routing()
         for key, (shp, dt) in shapes.items():
             setattr(r, key, _ptr(routing.get(key), dt, shp, key))
-    st = lib.moe_forward(ctypes.byref(desc), _ptr(x, _act(desc), (T, d), "x"), ctypes.byref(weights),
-                         _ptr(bias, torch.float32, (E,), "bias"), ctypes.c_float(gamma),
-                         _ptr(y, _act(desc), (T, d), "y"),
-                         ctypes.byref(r) if r is not None else None,
-                         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(bias.device))
-    _check("moe_forward", st)
+    args = (ctypes.byref(desc), _ptr(x, _act(desc), (T, d), "x"), ctypes.byref(weights),
+            _ptr(bias, torch.float32, (E,), "bias"), ctypes.c_float(gamma),
+            _ptr(y, _act(desc), (T, d), "y"), ctypes.byref(r) if r is not None else None,
+            _ptr(ws, torch.uint8, None, "ws"), ws.numel())
+    if events is None:
+        st = lib.moe_forward(*args, _stream(bias.device))
+        _check("moe_forward", st)
+    else:
+        st = lib.moe_forward_marked(*args, _marks(events, 7), _stream(bias.device))
+        _check("moe_forward_marked", st)

@@ -366,15 +366,25 @@ moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w, ui
   return hip_status(launch_quantize_mxfp4(E, N, K, w, codes, scales, stream));
 }
 
-moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
-                       float gamma, void* y, const moe_routing* routing, void* ws,
-                       size_t ws_bytes, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// moe_forward's launches; marks (7 events, or NULL) are recorded after the
+// router, the dispatch, the tile plan, the gate/up GEMM, the down GEMM, the
+// combine and the bias update.
+moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
+                        float gamma, void* y, const moe_routing* routing, void* ws,
+                        size_t ws_bytes, hipEvent_t* marks, hipStream_t stream) {
   moe_status st = check_ffn_desc(desc);
   if (st != MOE_OK) return st;
   const Shape s = to_shape(desc);
   if (!weights_ok(w, s) || !w->w_router || !bias) return MOE_ERR_NULL;
   if (s.T > 0 && (!x || !y)) return MOE_ERR_NULL;
   if (!std::isfinite(gamma)) return MOE_ERR_SHAPE;
+  if (marks)
+    for (int i = 0; i < 7; ++i)
+      if (!marks[i]) return MOE_ERR_NULL;
   if ((st = check_ws(s, MOE_CALL_FORWARD, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   FwdWs f = carve_forward(c, s);
@@ -388,22 +398,48 @@ moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w
     if (routing->pair_pos) f.pair_pos = routing->pair_pos;
     margin = routing->margin;
   }
+  auto mark = [&](int i, hipError_t e) {
+    return (e == hipSuccess && marks) ? hipEventRecord(marks[i], stream) : e;
+  };
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_router(s, x, w->w_router, bias, f.topk, f.gates, margin,
                                f.router.planes, f.router.partial, stream);
+  e = mark(0, e);
   if (e == hipSuccess)
     e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg, stream);
+  e = mark(1, e);
   if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
+  e = mark(2, e);
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
-                       f.offsets, f.sorted_pair, f.plan, mt, f.h, f.part, nullptr, stream);
+                       f.offsets, f.sorted_pair, f.plan, mt, f.h, f.part,
+                       marks ? marks + 3 : nullptr, stream);
   if (e == hipSuccess)
     e = launch_down(s, w->w_down, w->ws_down, w->sc_down, f.offsets, f.plan, mt, f.h, f.y_routed,
-                    f.y_shared, f.part, nullptr, stream);
+                    f.y_shared, f.part, marks ? marks + 4 : nullptr, stream);
   if (e == hipSuccess)
     e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
+  e = mark(5, e);
   if (e == hipSuccess && gamma != 0.0f) e = launch_bias_update(s, f.counts, gamma, bias, stream);
+  e = mark(6, e);
   return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
+                       float gamma, void* y, const moe_routing* routing, void* ws,
+                       size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(desc, x, w, bias, gamma, y, routing, ws, ws_bytes, nullptr, stream);
+}
+
+moe_status moe_forward_marked(const moe_desc* desc, const void* x, const moe_weights* w,
+                              float* bias, float gamma, void* y, const moe_routing* routing,
+                              void* ws, size_t ws_bytes, hipEvent_t* marks, hipStream_t stream) {
+  if (!marks) return MOE_ERR_NULL;
+  return forward_impl(desc, x, w, bias, gamma, y, routing, ws, ws_bytes, marks, stream);
 }
 
 }  // extern "C"

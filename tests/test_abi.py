@@ -143,6 +143,12 @@ def test_calls_reject_bad_arguments_before_launch():
     wf2 = L.Weights(None, *([0x1000] * 6))
     assert lib.moe_forward(ctypes.byref(d), P, ctypes.byref(wf2), P, 1e-3, P, None, P,
                            need, None) == 1
+    # the marked forward needs all seven events
+    assert lib.moe_forward_marked(ctypes.byref(d), P, ctypes.byref(wf), P, 1e-3, P, None, P,
+                                  need, None, None) == 1
+    marks = (ctypes.c_void_p * 7)(*([0x1000] * 6 + [0]))
+    assert lib.moe_forward_marked(ctypes.byref(d), P, ctypes.byref(wf), P, 1e-3, P, None, P,
+                                  need, marks, None) == 1
 
 
 def test_binding_rejects_host_tensors():

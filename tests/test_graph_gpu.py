@@ -87,3 +87,43 @@ def test_forward_graph_replays_match_eager(cfg):
             assert torch.equal(got[n], ref), f"replay {rep}: {n} differs"
         assert torch.isfinite(junk)
     del keep
+
+
+@pytest.mark.parametrize("cfg", CASES[:3], ids=lambda c: c.name)
+def test_forward_marked_matches_forward(cfg):
+    """moe_forward_marked (the benchmark's timed entry point) gives bit for
+    bit what moe_forward gives, and its seven events come in launch order."""
+    log(f"[marked] {cfg.describe()} fp4={cfg.fp4_weights}")
+    inp = synth.make_inputs(cfg, device=DEV)
+    desc = L.make_desc(cfg.T, cfg.d, cfg.F, synth.act_dtype(cfg),
+                       fp4_weights=cfg.fp4_weights)
+    keep = None
+    if cfg.fp4_weights:
+        w, keep = L.fp4_weights(inp)
+    else:
+        w = L.weights_from(inp)
+    outs = []
+    for marked in (False, True):
+        y = torch.empty((cfg.T, cfg.d), dtype=synth.act_dtype(cfg), device=DEV)
+        routing = {"topk_idx": torch.empty((cfg.T, cfg.k), dtype=torch.int32, device=DEV),
+                   "counts": torch.empty(cfg.E, dtype=torch.int32, device=DEV)}
+        bias = inp["bias"].clone()
+        ev = None
+        if marked:
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+            for e in ev:
+                e.record()
+            torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        start.record()
+        L.forward(desc, inp["x"], w, bias, cfg.gamma, y, routing, events=ev)
+        torch.cuda.synchronize()
+        outs.append((y, bias, routing))
+        if marked:
+            spans = [start.elapsed_time(ev[0])] + [ev[i].elapsed_time(ev[i + 1]) for i in range(6)]
+            assert all(t >= 0.0 for t in spans), spans
+    (y0, b0, r0), (y1, b1, r1) = outs
+    assert torch.equal(y0, y1) and torch.equal(b0, b1)
+    for n in r0:
+        assert torch.equal(r0[n], r1[n]), n
+    del keep
