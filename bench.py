@@ -502,8 +502,11 @@ def cpu_baseline(cfg, inp, ntok, torch):
                        None)
     except OSError:
         pass
+    # the sample's arithmetic: router plus 8 SwiGLU experts per token (6 routed, 2 shared)
+    flop = ntok * (2.0 * cfg.d * (cfg.E + cfg.S) + (cfg.k + cfg.S) * 6.0 * cfg.d * cfg.F)
     return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2), "cpu": cpu, "blas": blas,
+            "seconds": round(dt, 2), "gflop_s": round(flop / dt / 1e9, 1), "cpu": cpu,
+            "blas": blas,
             "sample": (f"first {ntok} tokens of the T={cfg.T} batch: full oracle forward "
                        f"(fp64 router, dispatch, {len(need)} routed + {cfg.S} shared SwiGLU "
                        f"experts, combine, bias update)")}
