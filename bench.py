@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-skewed", action="store_true")
     ap.add_argument("--native-workload", default="I")
     ap.add_argument("--no-native", action="store_true")
+    ap.add_argument("--prefill-workload", default="B")
+    ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ep-share", action="store_true")
     ap.add_argument("--lab-workload", default="Lab")
     ap.add_argument("--no-lab", action="store_true")
@@ -556,6 +558,24 @@ def decode(dc, args, torch, L, synth):
     return out
 
 
+def prefill(pc, args, torch, L, synth):
+    """The prefill-chunk workload against both rooflines: with ~96 rows per
+    routed expert every expert's weights are streamed once per step (about
+    125 FLOP per byte, under the bf16 ridge, so HBM bounds it) while the
+    matrix cores run 96-row tiles."""
+    inp, _, _, ws, counts, ms, _ = time_forward(pc, max(5, min(args.steps, 20)), args.warmup,
+                                                torch, L, synth)
+    f_gu, f_dn = expert_flops(pc)
+    nbytes, n_active = decode_bytes(pc, counts.cpu())
+    del inp, ws
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill-chunk MoE layer, {pc.describe()}, fp32 router",
+            "tokens_s": round(pc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+            "mfma_frac": round((f_gu + f_dn) / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "hbm_frac": round(nbytes / (ms / 1e3) / 1e9 / PEAK_HBM_GBS, 4),
+            "bytes": nbytes, "active_experts": n_active}
+
+
 def native(nc, args, torch, L, synth):
     """The layer at the native shape with logsumexp gates."""
     inp, _, _, ws, _, ms, _ = time_forward(nc, max(5, min(args.steps, 10)), args.warmup,
@@ -638,6 +658,9 @@ def main():
                                                  torch, L, synth))
         section(result, "decode_fp4", lambda: decode(configs.get(args.fp4_decode_workload),
                                                      args, torch, L, synth))
+    if not args.no_prefill:
+        section(result, "prefill", lambda: prefill(configs.get(args.prefill_workload), args,
+                                                   torch, L, synth))
     if not args.no_native:
         section(result, "native", lambda: native(configs.get(args.native_workload), args,
                                                  torch, L, synth))
