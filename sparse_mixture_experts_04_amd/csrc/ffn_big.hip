@@ -1,17 +1,20 @@
-// Expert GEMMs for large batches: row tiles of up to 256 rows.
+// Expert GEMMs for large batches: row tiles of up to 256 rows (K step 32),
+// or of up to 128 rows (K step 64) when the experts hold fewer than ~160
+// rows each.
 //
 // Same computation as the 32-row kernel in ffn.hip ("Under The Hood:
 // Inkling", expert configuration: SwiGLU experts; "Inkling, Dissected", 02:
 // routed and shared experts), with a tile shaped for the matrix cores when
 // the routed experts hold hundreds of rows each:
 //
-// * Tile: up to 256 rows x 256 weight rows, K step 32, 512 threads.  Wave
-//   (wm, wn) = (wave / 4, wave % 4) owns weight rows 64wn..64wn+63 (two
-//   32-wide MFMA column blocks) and the 32-row blocks 2i + wm, i = 0..3.
+// * Tile: up to MT rows x 256 weight rows, 512 threads (BigShape: MT = 256
+//   with K step 32, or MT = 128 with K step 64).  Wave (wm, wn) =
+//   (wave / 4, wave % 4) owns weight rows 64wn..64wn+63 (two 32-wide MFMA
+//   column blocks) and the 32-row blocks 2i + wm, i < MT / 64.
 //   A tile that is only partly filled skips the MFMAs (and fragment reads)
 //   of its empty row blocks, so its cost follows its row count in steps of
 //   32 rows.
-// * Row tiles: a group of L rows is cut into t = ceil(L / 256) tiles of
+// * Row tiles: a group of L rows is cut into t = ceil(L / MT) tiles of
 //   nearly equal size (multiples of 32 rows but the last), all in one
 //   launch, so every weight tile of an expert is streamed while all of its
 //   rows use it.
@@ -19,9 +22,12 @@
 //   32wn..32wn+31 of the 128-column output tile followed by the same W_up
 //   columns; SwiGLU is applied to the accumulators in registers.
 // * Data path: direct global -> LDS loads into separate rings for the two
-//   operands (16 KiB per operand stage), 64-byte LDS rows with chunk c of
-//   row r in slot c ^ swz4(r), which keeps the fragment reads free of bank
-//   conflicts (see swz4).
+//   operands, LDS rows of one K step (64 or 128 bytes) with chunk c of row
+//   r in slot c ^ row_swz(r), which keeps the fragment reads free of bank
+//   conflicts (see row_swz).  The 128-row shape moves twice the bytes per
+//   K step, so its barriers and waits are spread over twice the loads:
+//   tiles with few rows carry few MFMAs per step, and the per-step cost
+//   dominates them.
 // * Scheduling: persistent workgroups; the item list is cut into one
 //   contiguous chunk per XCD and the workgroups of an XCD take the next item
 //   of their chunk from a counter, so consecutive items (sharing weight and
@@ -33,50 +39,87 @@
 
 namespace moe {
 
-struct BigCfg {
+// Tile shape: MT rows x 256 weight rows, K step BK (64-byte LDS rows for
+// BK = 32, 128-byte rows for BK = 64), NSA / NSB ring slots for the two
+// operands.
+template <int MT_, int BK_, int NSA_, int NSB_>
+struct BigShape {
   static constexpr int THREADS = 512;
   static constexpr int WAVES = THREADS / 64;
-  static constexpr int BK = 32;
-  static constexpr int MT = 256;
+  static constexpr int MT = MT_;
   static constexpr int NB = 256;
-  static constexpr int NSA = 3;                       // A (activation) ring slots
-  static constexpr int NSB = 6;                       // B (weight) ring slots
+  static constexpr int BK = BK_;
+  static constexpr int NSA = NSA_;                    // A (activation) ring slots
+  static constexpr int NSB = NSB_;                    // B (weight) ring slots
   static constexpr int BM = MT / 32 / 2;              // row blocks per wave
   static constexpr int BN = 2;                        // column blocks per wave
-  static constexpr int LPW = MT * 64 / 1024 / (WAVES / 2);  // KiB loads per loading wave
-  static constexpr int STAGE_ELEMS = MT * BK;         // bf16 elements of one operand stage
-  static_assert(MT == NB, "both operands use the same load shape");
-  static_assert((NSB - 2) * LPW < 64, "vmcnt range");
+  static constexpr int KK = BK / 16;                  // MFMA substeps per stage
+  static constexpr int CPR = BK / 8;                  // 16-byte chunks per LDS row
+  static constexpr int RPL = 64 / CPR;                // LDS rows per 1 KiB load
+  static constexpr int A_STAGE = MT * BK;             // bf16 elements of one A stage
+  static constexpr int B_STAGE = NB * BK;             // ... and of one B stage
+  static constexpr int LPW_A = A_STAGE * 2 / 1024 / (WAVES / 2);  // 1 KiB loads per loading wave
+  static constexpr int LPW_B = B_STAGE * 2 / 1024 / (WAVES / 2);
+  static constexpr int LPW_MAX = LPW_A > LPW_B ? LPW_A : LPW_B;
+  static constexpr int LDS_ELEMS = NSA * A_STAGE + NSB * B_STAGE;
+  static_assert((NSB - 2) * LPW_B < 64 && (NSA - 2) * LPW_A < 64, "vmcnt range");
+  static_assert(BK == 32 || BK == 64, "LDS row layouts");
+  static_assert(6 % NSA == 0 && 6 % NSB == 0, "the K loop is unrolled by 6");
 };
+// 256-row tiles with K step 32 (the most MFMA work per loaded byte), and
+// 128-row tiles with K step 64 for experts of up to ~200 rows: twice the
+// bytes per barrier, for groups whose K steps carry few MFMAs.
+using BigCfg = BigShape<256, 32, 3, 6>;
+using MidCfg = BigShape<128, 64, 3, 3>;
+static_assert(BigCfg::MT == BigCfgRows && MidCfg::MT == MidCfgRows, "row tiles");
+static_assert(BigCfg::LDS_ELEMS * 2 <= 147456 && MidCfg::LDS_ELEMS * 2 <= 147456, "LDS");
 
-// Slot of chunk c in LDS row r is c ^ swz4(r).  gfx950 serves a ds_read_b128
+// Slot of chunk c in LDS row r is c ^ row_swz(r).  gfx950 serves a ds_read_b128
 // 16 lanes per cycle over 64 banks of 4 bytes (one 256-byte bank row); the
 // 16 lanes of a cycle are 4 lane quads whose quad indices within the half
 // wave have equal parity (lanes 0-3, 12-15, 20-27 together).  A fragment
 // read (lane l: row l % 32, chunk 2kk + l / 32) then touches the 16 slots of
-// a bank row exactly once per cycle when swz4(r) = (r >> 2) & 3 (measured:
-// no bank-conflict cycles).
-__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+// a bank row exactly once per cycle when row_swz(r) = (r >> 2) & 3 for
+// 64-byte rows (measured: no bank-conflict cycles), and with
+// row_swz(r) = (r & 7) ^ ((r >> 3) & 1) for 128-byte rows (the layout of
+// the 32-row kernel, also measured conflict-free).  Rows of a 32-row block
+// differ only above bit 4, so the slot depends on the row inside its block.
+template <class C>
+__device__ __forceinline__ int row_swz(int row) {
+  if constexpr (C::BK == 32) return (row >> 2) & 3;
+  else return (row & 7) ^ ((row >> 3) & 1);
+}
+
+// Source chunk (in elements) that lane l fetches for load j of a stage: the
+// load fills LDS rows RPL*j.. and the lane lands in slot l % CPR of row
+// RPL*j + l / CPR, so it fetches chunk (l % CPR) ^ row_swz(that row).
+template <class C>
+__device__ __forceinline__ int src_chunk(int lane, int j) {
+  if constexpr (C::BK == 32) return ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  else return ((lane & 7) ^ (lane >> 3) ^ (j & 1)) * 8;
+}
 
 // Wave group 0 loads the weight (B) tiles, group 1 the activation (A)
-// tiles; each wave issues LPW 1 KiB loads per stage, load j = 4 * (wave % 4)
-// + q filling LDS rows 16j..16j+15 of its operand's slot.
+// tiles; each wave issues L 1 KiB loads per stage (LPW_B or LPW_A), load
+// j = L * (wave % 4) + q filling LDS rows RPL*j.. of its operand's slot.
+template <class C>
 struct BigCtx {
-  using C = BigCfg;
-  const bf16_t* src[C::LPW];  // per-lane source of each load (chunk applied)
+  const bf16_t* src[C::LPW_MAX];  // per-lane source of each load (chunk applied)
 
+  template <int L>
   __device__ __forceinline__ void issue(int k0, bf16_t* slot, int wig) const {
 #pragma unroll
-    for (int q = 0; q < C::LPW; ++q) dma16(src[q] + k0, slot + (wig * C::LPW + q) * 512);
+    for (int q = 0; q < L; ++q) dma16(src[q] + k0, slot + (wig * L + q) * 512);
   }
 };
 
-// Fragments of one stage for one wave: 2 MFMA substeps x (4 row blocks of
+// Fragments of one stage for one wave: KK MFMA substeps x (BM row blocks of
 // A, 2 column blocks of B).  Row block i of group grp is tile row block
 // 2i + grp (groups interleave so a partly filled tile stays balanced).
+template <class C>
 struct BigFrags {
-  bf16x8_t a[2][BigCfg::BM];
-  bf16x8_t b[2][BigCfg::BN];
+  bf16x8_t a[C::KK][C::BM];
+  bf16x8_t b[C::KK][C::BN];
 };
 
 // Fragment reads.  Rows of a 32-row block differ only above bit 4, so the
@@ -84,20 +127,21 @@ struct BigFrags {
 // offset per substep (`off[kk]`, in elements) plus a compile-time block
 // offset addresses every fragment.  `nv` (wave-uniform) is the number of
 // this wave's row blocks that hold rows of the tile.
+template <class C>
 __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* sB, int grp,
-                                               int wn, int nv, const int (&off)[2],
-                                               BigFrags& f) {
-  using C = BigCfg;
+                                               int wn, int nv, const int (&off)[C::KK],
+                                               BigFrags<C>& f) {
+  constexpr int BLK = 32 * C::BK;  // elements of a 32-row block
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk) {
+  for (int kk = 0; kk < C::KK; ++kk) {
 #pragma unroll
     for (int j = 0; j < C::BN; ++j)
       f.b[kk][j] =
-          *reinterpret_cast<const bf16x8_t*>(sB + (wn * 2 + j) * 1024 + off[kk]);
+          *reinterpret_cast<const bf16x8_t*>(sB + (wn * 2 + j) * BLK + off[kk]);
 #pragma unroll
     for (int i = 0; i < C::BM; ++i)
       if (i < nv)
-        f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + grp) * 1024 + off[kk]);
+        f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + grp) * BLK + off[kk]);
   }
 }
 
@@ -105,11 +149,11 @@ __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* s
 // is the transposed product (output columns down the lane's registers, tile
 // rows across lanes): a lane then holds 4 consecutive output columns of one
 // row, which the epilogue writes as one 8-byte word.
-__device__ __forceinline__ void big_mfma(const BigFrags& f, int nv,
-                                         f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
-  using C = BigCfg;
+template <class C>
+__device__ __forceinline__ void big_mfma(const BigFrags<C>& f, int nv,
+                                         f32x16_t (&acc)[C::BM][C::BN]) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+  for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
     for (int i = 0; i < C::BM; ++i)
       if (i < nv)
@@ -138,57 +182,60 @@ __device__ __forceinline__ void big_mfma(const BigFrags& f, int nv,
 // operand on its own waves lets the B loads run far ahead without the A
 // waits depending on them.  Past the last K step the loads repeat the last
 // step (L2 hits into slots never read), which keeps the counts uniform.
-template <int U, bool GATED>
-__device__ __forceinline__ void big_pp_step(const BigCtx& t, int kt, int nk,
-                                            bf16_t* const (&sA)[BigCfg::NSA],
-                                            bf16_t* const (&sB)[BigCfg::NSB], int grp, int wig,
-                                            int nv, const int (&off)[2],
-                                            f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
-  using C = BigCfg;
-  BigFrags f;
-  big_read_frags(sA[U % C::NSA], sB[U % C::NSB], grp, wig, nv, off, f);
-  {
-    const int ahead = grp == 0 ? C::NSB - 1 : C::NSA - 1;
-    const int ks = kt + ahead < nk ? kt + ahead : nk - 1;
-    bf16_t* slot = grp == 0 ? sB[(U + C::NSB - 1) % C::NSB] : sA[(U + C::NSA - 1) % C::NSA];
-    t.issue(ks * C::BK, slot, wig);
+template <class C, int U, bool GATED>
+__device__ __forceinline__ void big_pp_step(const BigCtx<C>& t, int kt, int nk,
+                                            bf16_t* const (&sA)[C::NSA],
+                                            bf16_t* const (&sB)[C::NSB], int grp, int wig,
+                                            int nv, const int (&off)[C::KK],
+                                            f32x16_t (&acc)[C::BM][C::BN]) {
+  BigFrags<C> f;
+  big_read_frags<C>(sA[U % C::NSA], sB[U % C::NSB], grp, wig, nv, off, f);
+  if (grp == 0) {
+    const int ks = kt + C::NSB - 1 < nk ? kt + C::NSB - 1 : nk - 1;
+    t.template issue<C::LPW_B>(ks * C::BK, sB[(U + C::NSB - 1) % C::NSB], wig);
+  } else {
+    const int ks = kt + C::NSA - 1 < nk ? kt + C::NSA - 1 : nk - 1;
+    t.template issue<C::LPW_A>(ks * C::BK, sA[(U + C::NSA - 1) % C::NSA], wig);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
-  if (grp == 1) wait_vm<(C::NSA - 2) * C::LPW>();
+  if (grp == 1) wait_vm<(C::NSA - 2) * C::LPW_A>();
   lds_barrier();
-  big_mfma(f, nv, acc);
-  if (grp == 0) wait_vm<(C::NSB - 2) * C::LPW>();
+  big_mfma<C>(f, nv, acc);
+  if (grp == 0) wait_vm<(C::NSB - 2) * C::LPW_B>();
   lds_barrier();
 }
 
-template <bool GATED>
-__device__ __forceinline__ void big_kloop(const BigCtx& t, int nk,
-                                          bf16_t* const (&sA)[BigCfg::NSA],
-                                          bf16_t* const (&sB)[BigCfg::NSB], int wave, int lane,
-                                          int nv, f32x16_t (&acc)[BigCfg::BM][BigCfg::BN]) {
-  using C = BigCfg;
+template <class C, bool GATED>
+__device__ __forceinline__ void big_kloop(const BigCtx<C>& t, int nk,
+                                          bf16_t* const (&sA)[C::NSA],
+                                          bf16_t* const (&sB)[C::NSB], int wave, int lane,
+                                          int nv, f32x16_t (&acc)[C::BM][C::BN]) {
   const int grp = wave >> 2, wig = wave & 3;
   const int r32 = lane & 31;
-  const int off[2] = {r32 * 32 + (((lane >> 5) ^ swz4(r32)) << 3),
-                      r32 * 32 + (((2 + (lane >> 5)) ^ swz4(r32)) << 3)};
+  int off[C::KK];
+#pragma unroll
+  for (int kk = 0; kk < C::KK; ++kk)
+    off[kk] = r32 * C::BK + (((2 * kk + (lane >> 5)) ^ row_swz<C>(r32)) << 3);
   if (grp == 0) {
 #pragma unroll
-    for (int s = 0; s < C::NSB - 1; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sB[s], wig);
-    wait_vm<(C::NSB - 2) * C::LPW>();
+    for (int s = 0; s < C::NSB - 1; ++s)
+      t.template issue<C::LPW_B>((s < nk ? s : nk - 1) * C::BK, sB[s], wig);
+    wait_vm<(C::NSB - 2) * C::LPW_B>();
   } else {
 #pragma unroll
-    for (int s = 0; s < C::NSA - 1; ++s) t.issue((s < nk ? s : nk - 1) * C::BK, sA[s], wig);
-    wait_vm<(C::NSA - 2) * C::LPW>();
+    for (int s = 0; s < C::NSA - 1; ++s)
+      t.template issue<C::LPW_A>((s < nk ? s : nk - 1) * C::BK, sA[s], wig);
+    wait_vm<(C::NSA - 2) * C::LPW_A>();
   }
   lds_barrier();                  // point 0: stage 0 complete
   if (grp == 1) lds_barrier();    // point 1 for group 1 (its phase 0 is idle)
   for (int kt = 0; kt < nk; kt += 6) {
-    big_pp_step<0, GATED>(t, kt, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 1 < nk) big_pp_step<1, GATED>(t, kt + 1, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 2 < nk) big_pp_step<2, GATED>(t, kt + 2, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 3 < nk) big_pp_step<3, GATED>(t, kt + 3, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 4 < nk) big_pp_step<4, GATED>(t, kt + 4, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 5 < nk) big_pp_step<5, GATED>(t, kt + 5, nk, sA, sB, grp, wig, nv, off, acc);
+    big_pp_step<C, 0, GATED>(t, kt, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 1 < nk) big_pp_step<C, 1, GATED>(t, kt + 1, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 2 < nk) big_pp_step<C, 2, GATED>(t, kt + 2, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 3 < nk) big_pp_step<C, 3, GATED>(t, kt + 3, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 4 < nk) big_pp_step<C, 4, GATED>(t, kt + 4, nk, sA, sB, grp, wig, nv, off, acc);
+    if (kt + 5 < nk) big_pp_step<C, 5, GATED>(t, kt + 5, nk, sA, sB, grp, wig, nv, off, acc);
   }
   if (grp == 0) lds_barrier();    // both groups pass the same number of points
 }
@@ -196,20 +243,21 @@ __device__ __forceinline__ void big_kloop(const BigCtx& t, int nk,
 // One launch covers every row tile of every group.  `plan` holds the row
 // tiles per group as an exclusive prefix (G+1 entries); `counters` the
 // per-XCD work counters, zero at launch.
-template <bool GATED>
+template <class C, bool GATED>
 __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_t* plan,
                                                          int32_t* counters) {
-  using C = BigCfg;
   // ring slots of the A and B tiles; after the K loop the same memory
   // stages the output tile for coalesced stores
-  __shared__ __attribute__((aligned(1024))) bf16_t lds[(C::NSA + C::NSB) * C::STAGE_ELEMS];
+  __shared__ __attribute__((aligned(1024))) bf16_t lds[C::LDS_ELEMS];
   __shared__ int ts[512];
   __shared__ long long s_item;
-  bf16_t* const sA[C::NSA] = {lds, lds + C::STAGE_ELEMS, lds + 2 * C::STAGE_ELEMS};
+  bf16_t* sA[C::NSA];
   bf16_t* sB[C::NSB];
 #pragma unroll
-  for (int i = 0; i < C::NSB; ++i) sB[i] = lds + (C::NSA + i) * C::STAGE_ELEMS;
-  static_assert(C::NSA == 3, "slot list");
+  for (int i = 0; i < C::NSA; ++i) sA[i] = lds + i * C::A_STAGE;
+#pragma unroll
+  for (int i = 0; i < C::NSB; ++i) sB[i] = lds + C::NSA * C::A_STAGE + i * C::B_STAGE;
+  static_assert(C::MT * (GATED ? C::NB / 2 : C::NB) <= C::LDS_ELEMS, "output tile");
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -226,11 +274,9 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
   const size_t kT = static_cast<size_t>(p.k) * p.T;
   const int nk = p.K / C::BK;
   const size_t wstride = static_cast<size_t>(p.N) * p.K;
-  // load j of a stage fills LDS rows 16j..16j+15; lane l lands in slot l%4
-  // of row 16j + l/4 and fetches chunk (l%4) ^ swz4(16j + l/4), which is
-  // (l%4) ^ ((l >> 4) & 3) for every j
-  const int lrow = lane >> 2;
-  const int lchunk = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  // load j of a stage fills LDS rows RPL*j..; lane l lands in row
+  // RPL*j + l / CPR (src_chunk gives the chunk it fetches)
+  const int lrow = lane / C::CPR;
 
   for (;;) {
     // the next item of this XCD's chunk, then of the others' (claim_item)
@@ -243,26 +289,26 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
                                    : kT + static_cast<size_t>(g - p.E) * p.T;
-    BigCtx t;
+    BigCtx<C> t;
     if (wm == 1) {
 #pragma unroll
-      for (int q = 0; q < C::LPW; ++q) {
-        const int j = wn * C::LPW + q;
-        int r = j * 16 + lrow;
+      for (int q = 0; q < C::LPW_A; ++q) {
+        const int j = wn * C::LPW_A + q;
+        int r = j * C::RPL + lrow;
         r = r < item.rows ? r : item.rows - 1;
         const int rr = item.m0 + r;
         size_t src_row;
         if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
                                     : static_cast<size_t>(rr);
         else src_row = row_base + rr;
-        t.src[q] = A + src_row * p.K + lchunk;
+        t.src[q] = A + src_row * p.K + src_chunk<C>(lane, j);
       }
     } else {
       const int ge = routed ? g : g - p.E;
 #pragma unroll
-      for (int q = 0; q < C::LPW; ++q) {
-        const int j = wn * C::LPW + q;
-        const int R = j * 16 + lrow;  // LDS B row
+      for (int q = 0; q < C::LPW_B; ++q) {
+        const int j = wn * C::LPW_B + q;
+        const int R = j * C::RPL + lrow;  // LDS B row
         const int cg = R >> 6, rl = R & 63;
         const bf16_t* base;
         int col;
@@ -275,7 +321,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
           base = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0);
           col = item.n * C::NB + R;
         }
-        t.src[q] = base + ge * wstride + static_cast<size_t>(col) * p.K + lchunk;
+        t.src[q] = base + ge * wstride + static_cast<size_t>(col) * p.K + src_chunk<C>(lane, j);
       }
     }
 
@@ -290,7 +336,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     // row blocks of this wave's group (2i + wm) that hold rows of the tile
     const int nblk = (item.rows + 31) >> 5;
     const int nv = min((nblk - wm + 1) >> 1, C::BM);
-    big_kloop<GATED>(t, nk, sA, sB, wave, lane, nv, acc);
+    big_kloop<C, GATED>(t, nk, sA, sB, wave, lane, nv, acc);
     // the last steps refill ring slots with copies of the final stage, and
     // those copies may still be landing: drain every wave's loads before the
     // ring memory is reused for the output tile
@@ -366,10 +412,10 @@ static int device_cus_big() {
 }
 
 // Tile plan of the large-batch GEMMs: group g (routed expert g, then the
-// shared experts) with L rows gets ceil(L / 256) row tiles.  Writes the
+// shared experts) with L rows gets ceil(L / mt) row tiles.  Writes the
 // exclusive prefix over groups and zeroes both GEMMs' work counters.
 __global__ __launch_bounds__(512) void tile_plan_big_kernel(const int32_t* __restrict__ offsets,
-                                                            int E, int S, int T,
+                                                            int E, int S, int T, int mt,
                                                             int32_t* __restrict__ plan) {
   __shared__ int sf[512];
   const int g = threadIdx.x;
@@ -377,7 +423,7 @@ __global__ __launch_bounds__(512) void tile_plan_big_kernel(const int32_t* __res
   int rows = 0;
   if (g < E) rows = offsets[g + 1] - offsets[g];
   else if (g < G) rows = T;
-  const int nt = (rows + BigCfg::MT - 1) / BigCfg::MT;
+  const int nt = (rows + mt - 1) / mt;
   sf[g] = nt;
   __syncthreads();
   for (int off = 1; off < 512; off <<= 1) {
@@ -391,19 +437,24 @@ __global__ __launch_bounds__(512) void tile_plan_big_kernel(const int32_t* __res
   if (g < kCtrSets * kXcds) plan[G + 1 + g] = 0;
 }
 
-hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,
+hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int mt, int32_t* plan,
                                 hipStream_t st) {
-  tile_plan_big_kernel<<<1, 512, 0, st>>>(offsets, s.E, s.S, s.T, plan);
+  tile_plan_big_kernel<<<1, 512, 0, st>>>(offsets, s.E, s.S, s.T, mt, plan);
   return hipGetLastError();
 }
 
-hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
+hipError_t launch_big(const FfnArgs& a, bool gated, int mt, const int32_t* plan, int which,
                       hipEvent_t* marks, hipStream_t st) {
   const int G = a.E + a.S;
   int32_t* ctr = const_cast<int32_t*>(plan) + (G + 1) + which * kXcds;
   const int grid = (device_cus_big() + kXcds - 1) / kXcds * kXcds;
-  if (gated) ffn_big_kernel<true><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
-  else ffn_big_kernel<false><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
+  if (mt == MidCfg::MT) {
+    if (gated) ffn_big_kernel<MidCfg, true><<<grid, MidCfg::THREADS, 0, st>>>(a, plan, ctr);
+    else ffn_big_kernel<MidCfg, false><<<grid, MidCfg::THREADS, 0, st>>>(a, plan, ctr);
+  } else {
+    if (gated) ffn_big_kernel<BigCfg, true><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
+    else ffn_big_kernel<BigCfg, false><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
+  }
   if (marks && hipEventRecord(marks[0], st) != hipSuccess) return hipErrorInvalidValue;
   return hipGetLastError();
 }

@@ -168,14 +168,17 @@ __device__ __forceinline__ void dma16(const bf16_t* src, bf16_t* dst) {
 }
 
 
-// Row tile of the large-batch GEMMs and their tile plan.
+// Row tiles of the large-batch GEMMs (256 rows with K step 32; 128 rows
+// with K step 64 for experts of a few hundred rows or fewer) and their plan.
 constexpr int BigCfgRows = 256;
-hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int32_t* plan,
+constexpr int MidCfgRows = 128;
+hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int mt, int32_t* plan,
                                 hipStream_t st);
-// Large-batch GEMMs: `plan` is the layout written by tile_plan_big_kernel;
+// Large-batch GEMMs with row tiles of mt (BigCfgRows or MidCfgRows) rows:
+// `plan` is the layout written by tile_plan_big_kernel for that mt;
 // `which` (0 = gate/up, 1 = down) picks the work counters; marks[0]
 // (optional) is recorded after the GEMM launch.
-hipError_t launch_big(const FfnArgs& a, bool gated, const int32_t* plan, int which,
+hipError_t launch_big(const FfnArgs& a, bool gated, int mt, const int32_t* plan, int which,
                       hipEvent_t* marks, hipStream_t st);
 // Tile plan of the large-batch GEMM: [row tiles per group, exclusive
 // prefix (G+1) | work counters kCtrSets GEMMs x kXcds].

@@ -29,8 +29,10 @@ SMALL = {
     "bf16_small": MoEConfig("bf16_small", T=300, d=512, F=256, act="bf16", bias_range=0.05),
     "bf16_tall": MoEConfig("bf16_tall", T=1500, d=256, F=128, act="bf16", bias_range=0.05),
     "bf16_one": MoEConfig("bf16_one", T=1, d=768, F=384, act="bf16", bias_range=0.05),
-    # >= 48 rows per routed expert on average: the 256-row tile path
+    # 48 to 160 rows per routed expert on average: the 128-row tiles
     "bf16_mt128": MoEConfig("bf16_mt128", T=2200, d=512, F=256, act="bf16", bias_range=0.05),
+    # 164 rows per routed expert: the 256-row tiles
+    "bf16_mt256": MoEConfig("bf16_mt256", T=7000, d=256, F=128, act="bf16", bias_range=0.05),
     # gates by logsumexp over log-sigmoids, scaled ("Under The Hood: Inkling")
     "bf16_lse": MoEConfig("bf16_lse", T=300, d=512, F=256, act="bf16", bias_range=0.05,
                           gate_norm="logsumexp", gate_scale=6.5),
@@ -242,14 +244,16 @@ def test_skewed_bias_trajectory_100_steps(cf):
         assert first_diff is None
 
 
-@pytest.mark.parametrize("T", [1200, 3000])
+@pytest.mark.parametrize("T", [1200, 3000, 7000])
 def test_expert_ffn_tile_boundaries(T):
     # Hand-picked per-expert row counts around every tile size the GEMMs use
-    # (32-row tiles, 256-row tiles with 128-row tails): 0, 1, 31..33, 63..65,
-    # 127..129, 255..257, 383, 384, 511..513, the rest spread over the other
-    # experts.  sorted_pair is a seeded permutation of the pair ids, so rows
-    # gather arbitrary tokens.
-    cfg = MoEConfig(f"tiles{T}", T=T, d=512, F=256, act="bf16")
+    # (32-row tiles at T=1200, 128-row tiles at T=3000, 256-row tiles at
+    # T=7000, each with its balanced tails): 0, 1, 31..33, 63..65, 127..129,
+    # 255..257, 383, 384, 511..513, the rest spread over the other experts.
+    # sorted_pair is a seeded permutation of the pair ids, so rows gather
+    # arbitrary tokens.
+    cfg = MoEConfig(f"tiles{T}", T=T, d=512 if T < 5000 else 256, F=256 if T < 5000 else 128,
+                    act="bf16")
     inp = to_dev(synth.make_inputs(cfg, device="cpu"))
     E, k = cfg.E, cfg.k
     special = [0, 1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 383, 384,
