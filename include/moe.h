@@ -64,6 +64,12 @@
  *                            in sorted order, row k*T + s*T + t shared s.
  * - y_routed  act   [T*k, d] expert outputs in sorted order;
  *   y_shared  act   [S, T, d] shared-expert outputs.
+ * These tables live in device memory and no call checks their contents:
+ * the expert calls and combine take them as moe_dispatch wrote them
+ * (offsets non-decreasing from 0 to at most T*k; sorted_pair entries below
+ * offsets[E] in [0, T*k); pair_pos entries -1 or below offsets[E]).  Other
+ * contents give undefined results and may make the kernels read or write
+ * outside the buffers.
  *
  * Capacity ("Inkling, Dissected" 02d: each expert takes a bounded number
  * of tokens per batch; pairs beyond it are dropped and the output is built

@@ -236,8 +236,9 @@ def dispatch(desc, topk_idx, counts, offsets, sorted_pair, pair_pos, ws=None):
 def expert_gate_up(desc, x, weights, offsets, sorted_pair, h, ws=None):
     ws = alloc_workspace(desc, CALL_GATE_UP, offsets.device) if ws is None else ws
     st = lib.moe_expert_gate_up(ctypes.byref(desc), _ptr(x, _act(desc), (desc.T, desc.d), "x"),
-                                ctypes.byref(weights), _ptr(offsets, torch.int32, None, "offsets"),
-                                _ptr(sorted_pair, torch.int32, None, "sorted_pair"),
+                                ctypes.byref(weights),
+                                _ptr(offsets, torch.int32, (desc.E + 1,), "offsets"),
+                                _ptr(sorted_pair, torch.int32, (desc.T * desc.k,), "sorted_pair"),
                                 _ptr(h, _act(desc), ((desc.k + desc.S) * desc.T, desc.F), "h"),
                                 _ptr(ws, torch.uint8, None, "ws"), ws.numel(),
                                 _stream(offsets.device))
@@ -248,7 +249,7 @@ def expert_down(desc, weights, offsets, h, y_routed, y_shared, ws=None):
     ws = alloc_workspace(desc, CALL_DOWN, offsets.device) if ws is None else ws
     T, d, k, S = desc.T, desc.d, desc.k, desc.S
     st = lib.moe_expert_down(ctypes.byref(desc), ctypes.byref(weights),
-                             _ptr(offsets, torch.int32, None, "offsets"),
+                             _ptr(offsets, torch.int32, (desc.E + 1,), "offsets"),
                              _ptr(h, _act(desc), ((k + S) * T, desc.F), "h"),
                              _ptr(y_routed, _act(desc), (T * k, d), "y_routed"),
                              _ptr(y_shared, _act(desc), (S, T, d), "y_shared"),
@@ -271,8 +272,8 @@ def expert_gate_up_marked(desc, x, weights, offsets, sorted_pair, h, events, ws=
     ws = alloc_workspace(desc, CALL_GATE_UP, offsets.device) if ws is None else ws
     st = lib.moe_expert_gate_up_marked(
         ctypes.byref(desc), _ptr(x, _act(desc), (desc.T, desc.d), "x"), ctypes.byref(weights),
-        _ptr(offsets, torch.int32, None, "offsets"),
-        _ptr(sorted_pair, torch.int32, None, "sorted_pair"),
+        _ptr(offsets, torch.int32, (desc.E + 1,), "offsets"),
+        _ptr(sorted_pair, torch.int32, (desc.T * desc.k,), "sorted_pair"),
         _ptr(h, _act(desc), ((desc.k + desc.S) * desc.T, desc.F), "h"),
         _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _marks(events), _stream(offsets.device))
     _check("moe_expert_gate_up_marked", st)
@@ -283,7 +284,8 @@ def expert_down_marked(desc, weights, offsets, h, y_routed, y_shared, events, ws
     ws = alloc_workspace(desc, CALL_DOWN, offsets.device) if ws is None else ws
     T, d, k, S = desc.T, desc.d, desc.k, desc.S
     st = lib.moe_expert_down_marked(
-        ctypes.byref(desc), ctypes.byref(weights), _ptr(offsets, torch.int32, None, "offsets"),
+        ctypes.byref(desc), ctypes.byref(weights),
+        _ptr(offsets, torch.int32, (desc.E + 1,), "offsets"),
         _ptr(h, _act(desc), ((k + S) * T, desc.F), "h"),
         _ptr(y_routed, _act(desc), (T * k, d), "y_routed"),
         _ptr(y_shared, _act(desc), (S, T, d), "y_shared"),
@@ -295,8 +297,8 @@ def expert_ffn(desc, x, weights, offsets, sorted_pair, y_routed, y_shared, ws=No
     ws = alloc_workspace(desc, CALL_EXPERT_FFN, offsets.device) if ws is None else ws
     T, d, k, S = desc.T, desc.d, desc.k, desc.S
     st = lib.moe_expert_ffn(ctypes.byref(desc), _ptr(x, _act(desc), (T, d), "x"), ctypes.byref(weights),
-                            _ptr(offsets, torch.int32, None, "offsets"),
-                            _ptr(sorted_pair, torch.int32, None, "sorted_pair"),
+                            _ptr(offsets, torch.int32, (desc.E + 1,), "offsets"),
+                            _ptr(sorted_pair, torch.int32, (desc.T * desc.k,), "sorted_pair"),
                             _ptr(y_routed, _act(desc), (T * k, d), "y_routed"),
                             _ptr(y_shared, _act(desc), (S, T, d), "y_shared"),
                             _ptr(ws, torch.uint8, None, "ws"), ws.numel(),

@@ -376,3 +376,24 @@ def test_identical_tokens_with_an_exact_tie(T):
     assert e_y <= out_tol(cfg)
     y = np64(b.y)
     assert np.array_equal(y, np.broadcast_to(y[0], y.shape))   # identical rows out
+
+
+def test_binding_rejects_short_routing_tables():
+    """The expert calls read offsets[0..E] and sorted_pair[0..T*k-1]; the
+    binding refuses tables of any other length before anything launches."""
+    from sparse_mixture_experts_04_amd import _lib as L
+    cfg = MoEConfig("short_tables", T=64, d=256, F=128, act="bf16")
+    inp = synth.make_inputs(cfg, device=DEV)
+    desc = desc_for(cfg)
+    b = Buffers(desc, DEV)
+    w = L.weights_from(inp)
+    short_off = b.offsets[:-1]
+    short_sp = b.sorted_pair[:-1]
+    with pytest.raises(ValueError, match="offsets"):
+        L.expert_gate_up(desc, inp["x"], w, short_off, b.sorted_pair, b.h)
+    with pytest.raises(ValueError, match="sorted_pair"):
+        L.expert_gate_up(desc, inp["x"], w, b.offsets, short_sp, b.h)
+    with pytest.raises(ValueError, match="offsets"):
+        L.expert_down(desc, w, short_off, b.h, b.y_routed, b.y_shared)
+    with pytest.raises(ValueError, match="sorted_pair"):
+        L.expert_ffn(desc, inp["x"], w, b.offsets, short_sp, b.y_routed, b.y_shared)
