@@ -592,7 +592,7 @@ def native(nc, args, torch, L, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build runs on a single MI355X and has no "
+        print(f"bench.py measures one GPU: the layer runs on a single MI355X and has no "
               f"multi-GPU path (asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
     import torch
