@@ -397,3 +397,34 @@ def test_binding_rejects_short_routing_tables():
         L.expert_down(desc, w, short_off, b.h, b.y_routed, b.y_shared)
     with pytest.raises(ValueError, match="sorted_pair"):
         L.expert_ffn(desc, inp["x"], w, b.offsets, short_sp, b.y_routed, b.y_shared)
+
+
+def test_layer_past_2_31_elements():
+    """T = 65536 at the layer's width (d = 7168, F = 2048): the expert-sorted
+    outputs Y [6T, d] hold 2.8e9 elements, so every sorted row from
+    2^31 / d on is addressed past 2^31 elements (and past 4 GiB).  Routing,
+    dispatch and the bias are checked in full; the output on the first and
+    last token and on the tokens that own sorted rows at and past that
+    boundary."""
+    cfg = MoEConfig("past_2_31", T=65536, d=7168, F=2048, act="bf16")
+    log(f"[past 2^31] {cfg.describe()}")
+    inp = synth.make_inputs(cfg, device=DEV)
+    desc = desc_for(cfg)
+    b, bias_new = run_forward(desc, inp, cfg.gamma)
+    x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
+    topk = npi(b.topk)
+    r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates))
+    log(f"  routing {st}")
+    dp = check_dispatch(topk, b)
+    check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
+    sp = dp["sorted_pair"]
+    edge = (1 << 31) // cfg.d  # first sorted row whose elements lie past 2^31
+    assert cfg.k * cfg.T > edge + 2
+    rows = [edge, edge + 1, (edge + len(sp)) // 2, len(sp) - 1]
+    toks = sorted({0, cfg.T - 1} | {int(sp[i]) // cfg.k for i in rows})
+    y_ref = O.output_rows(toks, x64, topk, g_ref, expert_getter(inp), pair_pos=dp["pair_pos"])
+    e = rel_l2(np64(b.y[toks]), y_ref)
+    log(f"  sampled {len(toks)} tokens: rel L2 {e:.2e}")
+    assert e <= 2e-2
+    del inp, b
+    torch.cuda.empty_cache()
