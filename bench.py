@@ -39,6 +39,11 @@ METRIC = "MoE-layer tokens/s + % bf16 MFMA peak (T=16384) / % HBM BW (T=64 decod
 PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 matrix peak
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 
+# Steps of the timed sequences re-run after the timing for a parity check
+# against the oracle (in the CPU-baseline leg): workload, the bias the step
+# routed with (host), and which batch of tokens (None: the workload's x).
+PROBES = []
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -97,38 +102,56 @@ def spread(ms):
     return [round(v[len(v) // 10], 4), round(v[len(v) // 2], 4), round(v[(9 * len(v)) // 10], 4)]
 
 
-def capture_steps(step, n, torch):
-    """One HIP graph of `n` calls of `step` (a forward through the C ABI on
-    preallocated buffers: kernels only, no memset, copy or sync).  Every
-    kernel has run eagerly before, so nothing initialises during capture."""
+def capture_steps(step, indices, torch):
+    """One HIP graph of the calls step(i) for i in `indices` (a forward
+    through the C ABI on preallocated buffers: kernels only, no memset, copy
+    or sync).  Every kernel has run eagerly before, so nothing initialises
+    during capture."""
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
-        for _ in range(n):
-            step()
+        for i in indices:
+            step(i)
     torch.cuda.synchronize()
     return g
 
 
-def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5, marked=False):
-    """Times `steps` back-to-back forwards after `warmup` untimed ones.  The
-    bias is updated by every step, so later steps route differently (at
-    T=64 they touch more experts).  With `replay`, the same sequence is then
-    run again from the initial bias (the path is deterministic, so it routes
-    step for step as the timed run did): once in groups of `group` timed
-    steps between event pairs, for the spread of the per-step time, and once
-    untimed with each step's expert loads copied out, so that per-step
-    figures (bytes streamed) refer to the very steps that were timed.  The
-    last step's loads stay in `counts` either way.  With `marked`, the timed
-    steps call moe_forward_marked, whose events between the stages give
-    every step's stage and GEMM-kernel times (averaged into
-    inp["_marks_ms"])."""
+def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5, marked=False,
+                 fresh_bias=False):
+    """Times `steps` back-to-back forwards after `warmup` untimed ones.  By
+    default the bias is updated in place by every step, so later steps route
+    differently (at T=64 they touch more experts).  With `fresh_bias`, every
+    step instead routes with the workload's own initial bias and updates a
+    copy of its own (one preallocated buffer per step), which times the
+    workload exactly as stated, bias update included.  With `replay`, the
+    same sequence is then run again from the initial bias (the path is
+    deterministic, so it routes step for step as the timed run did): once in
+    groups of `group` timed steps between event pairs, for the spread of the
+    per-step time, and once untimed with each step's expert loads copied
+    out, so that per-step figures (bytes streamed) refer to the very steps
+    that were timed.  The last step's loads stay in `counts` either way.
+    With `marked`, the timed steps call moe_forward_marked, whose events
+    between the stages give every step's stage and GEMM-kernel times
+    (averaged into inp["_marks_ms"]).  inp["_probe_bias"] is left holding
+    (on the host) the bias the last timed step routed with, so that step can
+    be re-run for a parity check."""
     inp, desc, w, y, counts, ws = setup(cfg, torch, L, synth)
     bias0 = inp["bias"].clone()
     bias = bias0.clone()
     routing = {"counts": counts}
+    n_all = warmup + steps
+    fresh = [bias0.clone() for _ in range(n_all)] if fresh_bias else None
 
-    def step(events=None):
-        L.forward(desc, inp["x"], w, bias, cfg.gamma, y, routing, ws=ws, events=events)
+    def step(events=None, i=0):
+        b = fresh[i] if fresh_bias else bias
+        L.forward(desc, inp["x"], w, b, cfg.gamma, y, routing, ws=ws, events=events)
+
+    def restart():
+        # back to the initial bias state before a replayed sequence
+        if fresh_bias:
+            for f in fresh:
+                f.copy_(bias0)
+        else:
+            bias.copy_(bias0)
 
     marks = [None] * steps
     if marked:
@@ -136,14 +159,14 @@ def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5, mar
         for m in marks:
             for e in m:
                 e.record()          # the raw handles exist once an event was recorded
-    for _ in range(warmup):
-        step()
+    for i in range(warmup):
+        step(i=i)
     torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     ev0.record()
     for i in range(steps):
-        step(marks[i])
+        step(marks[i], i=warmup + i)
     ev1.record()
     torch.cuda.synchronize()
     if marked:
@@ -163,36 +186,46 @@ def time_forward(cfg, steps, warmup, torch, L, synth, replay=False, group=5, mar
         inp["_marks_ms"] = {n: v / steps for n, v in acc.items()}
     wall = time.perf_counter() - t0
     ms_events = ev0.elapsed_time(ev1) / steps
+    # the bias the last timed step routed with (an untimed replay)
+    restart()
+    for i in range(n_all - 1):
+        step(i=i)
+    inp["_probe_bias"] = (fresh[n_all - 1] if fresh_bias else bias).cpu().numpy().copy()
+    torch.cuda.synchronize()
     if replay:
         ngroups = max(1, steps // group)
-        bias.copy_(bias0)
-        for _ in range(warmup):
-            step()
+        restart()
+        for i in range(warmup):
+            step(i=i)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(ngroups)]
-        for a, b in evs:
+        for gi, (a, b) in enumerate(evs):
             a.record()
-            for _ in range(group):
-                step()
+            for j in range(group):
+                step(i=min(n_all - 1, warmup + gi * group + j))
             b.record()
         torch.cuda.synchronize()
         inp["_spread"] = spread([a.elapsed_time(b) / group for a, b in evs])
-        bias.copy_(bias0)
-        for _ in range(warmup):
-            step()
+        restart()
+        for i in range(warmup):
+            step(i=i)
         loads = torch.empty((steps, cfg.E), dtype=counts.dtype, device=counts.device)
         for i in range(steps):
-            step()
+            step(i=warmup + i)
             loads[i].copy_(counts)
         torch.cuda.synchronize()
         inp["_loads"] = loads.cpu()
         # the timed steps once more, replayed from one HIP graph
-        bias.copy_(bias0)
-        for _ in range(warmup):
-            step()
-        start = bias.clone()
-        graph = capture_steps(step, steps, torch)
-        bias.copy_(start)
+        restart()
+        for i in range(warmup):
+            step(i=i)
+        start = [f.clone() for f in fresh] if fresh_bias else bias.clone()
+        graph = capture_steps(lambda i: step(i=i), range(warmup, n_all), torch)
+        if fresh_bias:
+            for f, s0 in zip(fresh, start):
+                f.copy_(s0)
+        else:
+            bias.copy_(start)
         torch.cuda.synchronize()
         ev0.record()
         graph.replay()
@@ -309,8 +342,11 @@ def time_skewed(cfg, steps, torch, L, synth):
         cap = math.ceil(float(np.float32(cfg.capacity_factor)) * float(cfg.k * cfg.T) / cfg.E)
     ms, maxmean, dropped = [], [], []
     profile = None
+    probe_bias = None
     for s in range(steps + 1):          # batch 0 also warms up
         x = synth.make_x(cfg, device="cuda", step=s)
+        if s == 1:
+            probe_bias = bias.cpu().numpy().copy()   # the first timed batch's bias
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         L.forward(desc, x, w, bias, cfg.gamma, y, routing, ws=ws)
@@ -341,12 +377,42 @@ def time_skewed(cfg, steps, torch, L, synth):
                                    "last": round(maxmean[-1], 3)},
             "bias_range": [round(bias.min().item(), 5), round(bias.max().item(), 5)],
             "load_profile_first_batch": profile,
+            "per_step": {"ms": [round(v, 4) for v in ms],
+                         "max_over_mean_load": [round(v, 3) for v in maxmean[1:]],
+                         "note": "timed batches 1..N (batch 0 warms up)"},
+            "_probe": {"bias": probe_bias, "x_step": 1},
             **({"capacity_rows": cap,
-                "drop_rate": {"first": round(dropped[0], 4),
+                "drop_rate_per_step": [round(v, 4) for v in dropped[1:]],
+              "drop_rate": {"first": round(dropped[0], 4),
                               "middle": round(dropped[len(dropped) // 2], 4),
                               "last": round(dropped[-1], 4),
                               "mean": round(sum(dropped) / len(dropped), 4)}}
                if cap is not None else {})}
+
+
+def lab_measures(lab, x, torch):
+    """The Router Balance Lab's measures ("Inkling, Dissected", 02g) of the
+    lab's last step on tokens x, as float64 device scalars (no host sync):
+
+    * MaxVio: the hottest expert's demand over the ideal load k*T/E, minus 1;
+    * drop rate: the fraction of the k*T expert slots dropped at capacity;
+    * layer quality: the gate-weighted affinity of the surviving pairs (the
+      router's own gates, a dropped pair adding nothing) over that of the
+      unbiased, uncapacitated top-k with its own gates, summed over the batch.
+
+    Bookkeeping around the step, taken by this harness from the step's
+    outputs; the affinities are recomputed here in float64."""
+    T, E, k = lab.cfg.T, lab.cfg.E, lab.cfg.k
+    slots = float(k * T)
+    max_vio = lab.counts.max().to(torch.float64) * (E / slots) - 1.0
+    kept = (lab.pair_pos >= 0).view(T, k)
+    drop_rate = 1.0 - kept.sum().to(torch.float64) / slots
+    s = torch.sigmoid(x.to(torch.float64) @ lab.w_router.to(torch.float64).T)
+    sel = torch.gather(s, 1, lab.topk.long())
+    captured = (lab.gates.to(torch.float64) * sel * kept).sum()
+    best = torch.topk(s, k, dim=1).values
+    unbiased = (best * best / best.sum(dim=1, keepdim=True)).sum()
+    return torch.stack([max_vio, drop_rate, captured / unbiased])
 
 
 def balance_lab(cfg, torch, gammas=(0.0, 0.01, 0.05)):
@@ -366,7 +432,7 @@ def balance_lab(cfg, torch, gammas=(0.0, 0.01, 0.05)):
         meas = []
         for x in xs:
             lab.step(x)
-            meas.append(lab.measures(x))
+            meas.append(lab_measures(lab, x, torch))
         meas = torch.stack(meas).cpu()
         mean, last = meas.mean(dim=0).tolist(), meas[-1].tolist()
         runs[f"gamma={g}"] = {"max_vio": round(mean[0], 4), "drop_rate": round(mean[1], 5),
@@ -460,9 +526,129 @@ def decode_bytes(cfg, counts):
     return int(n_active * routed + cfg.S * per_expert + router + xy), n_active
 
 
-def cpu_baseline(cfg, inp, ntok, torch):
-    """The oracle, as it stands, on the first ``ntok`` tokens of the batch.
-    Inputs are copied to the host before the clock starts."""
+class _Upcast:
+    """An expert stack on the device seen by the oracle as float64 host
+    matrices, converted on access; the conversion time is summed apart from
+    the oracle's arithmetic."""
+
+    def __init__(self, t):
+        self.t = t
+        self.seconds = 0.0
+        self.n = 0
+
+    def __len__(self):
+        return self.t.shape[0]
+
+    def __getitem__(self, e):
+        import numpy as np
+        t0 = time.perf_counter()
+        m = self.t[e].float().cpu().numpy().astype(np.float64)
+        self.seconds += time.perf_counter() - t0
+        self.n += 1
+        return m
+
+
+def _oracle_weights(inp):
+    return {n: _Upcast(inp[n]) for n in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up",
+                                         "ws_down")}
+
+
+def _sample_tokens(T, n, seed=0):
+    import numpy as np
+    if n >= T:
+        return list(range(T))
+    rng = np.random.default_rng(seed)
+    return sorted({0, T - 1} | set(rng.choice(T, size=n - 2, replace=False).tolist()))
+
+
+def probe_parity(probe, main_cfg, main_inp, torch, L, synth, configs, O, nsample):
+    """Re-runs one step of a timed sequence (same tokens, same bias, so the
+    same bits as the timed run) and checks it against the oracle: near-tie
+    tokens (oracle 6th/7th key margin below 1e-6) counted and how many of
+    them picked the other set, selection elsewhere, the gates' largest
+    relative error, and the output's relative L2 on sampled tokens."""
+    import numpy as np
+    cfg = configs.get(probe["workload"])
+    inp = main_inp if cfg.name == main_cfg.name else synth.make_inputs(cfg, device="cuda")
+    if probe["x_step"] is not None:
+        inp = dict(inp)
+        inp["x"] = synth.make_x(cfg, device="cuda", step=probe["x_step"])
+    desc = L.make_desc(cfg.T, cfg.d, cfg.F, synth.act_dtype(cfg), gate_norm=cfg.gate_norm,
+                       gate_scale=cfg.gate_scale, capacity_factor=cfg.capacity_factor,
+                       fp4_weights=cfg.fp4_weights)
+    keep = None
+    if cfg.fp4_weights:
+        w, keep = L.fp4_weights(inp)
+    else:
+        w = L.weights_from(inp)
+    T, k, S = cfg.T, cfg.k, cfg.S
+    i32 = torch.int32
+    topk = torch.empty((T, k), dtype=i32, device="cuda")
+    gates = torch.empty((T, k + S), dtype=torch.float32, device="cuda")
+    pair_pos = torch.empty(T * k, dtype=i32, device="cuda")
+    y = torch.empty((T, cfg.d), dtype=synth.act_dtype(cfg), device="cuda")
+    bias = torch.tensor(probe["bias"], device="cuda")
+    L.forward(desc, inp["x"], w, bias, cfg.gamma, y,
+              {"topk_idx": topk, "gates": gates, "pair_pos": pair_pos})
+    torch.cuda.synchronize()
+    del keep
+    x64 = inp["x"].float().cpu().numpy().astype(np.float64)
+    wr64 = inp["w_router"].cpu().numpy().astype(np.float64)
+    b64 = probe["bias"].astype(np.float64)
+    t0 = time.perf_counter()
+    r = O.route(x64, wr64, b64, n_routed=cfg.E, k=k, gate_norm=cfg.gate_norm,
+                gate_scale=cfg.gate_scale)
+    tg = topk.cpu().numpy().astype(np.int64)
+    exempt = r["margin"] < 1e-6
+    differ = np.any(tg != r["topk_idx"], axis=1)
+    shared = list(range(cfg.E, cfg.E + S))
+    if cfg.gate_norm == "ratio":
+        g_ref, _ = O.joint_gates(r["s"], tg, shared, cfg.gate_scale)
+    else:
+        g_ref, _ = O.joint_gates_logsumexp(r["z"], tg, shared, cfg.gate_scale)
+    g = gates.cpu().numpy().astype(np.float64)
+    gate_rel = float(np.max(np.abs(g - g_ref) / g_ref)) if g.size else 0.0
+    out = {"step": probe["what"], "tokens": T,
+           "near_ties": {"exempt": int(exempt.sum()), "exempt_differ": int((differ & exempt).sum())},
+           "selection_mismatch_outside_near_ties": int((differ & ~exempt).sum()),
+           "gate_max_rel_err": float(f"{gate_rel:.3e}")}
+    if nsample > 0:
+        out.update(_probe_output(cfg, inp, x64, tg, g_ref, pair_pos, y, nsample, O))
+    out["oracle_s"] = round(time.perf_counter() - t0, 1)
+    if cfg.name != main_cfg.name:
+        del inp
+    torch.cuda.empty_cache()
+    return out
+
+
+def _probe_output(cfg, inp, x64, tg, g_ref, pair_pos, y, nsample, O):
+    """Relative L2 of the GPU's y on sampled tokens against the oracle's
+    output rows for the GPU's selection."""
+    import numpy as np
+    k, S = cfg.k, cfg.S
+    toks = _sample_tokens(cfg.T, nsample)
+    W = _oracle_weights(inp)
+
+    def expert(e):
+        if e < cfg.E:
+            return W["w_gate"][e], W["w_up"][e], W["w_down"][e]
+        return W["ws_gate"][e - cfg.E], W["ws_up"][e - cfg.E], W["ws_down"][e - cfg.E]
+
+    y_ref = O.output_rows(toks, x64, tg, g_ref, expert, k=k, n_routed=cfg.E, n_shared=S,
+                          pair_pos=pair_pos.cpu().numpy().astype(np.int64))
+    got = y[toks].float().cpu().numpy().astype(np.float64)
+    rel = float(np.linalg.norm(got - y_ref) / np.linalg.norm(y_ref))
+    return {"output_rel_l2_sampled": float(f"{rel:.3e}"), "sampled_tokens": len(toks)}
+
+
+def cpu_baseline(cfg, inp, ntok, torch, L, synth, configs):
+    """The oracle, as it stands, on the first ``ntok`` tokens of the batch
+    (with the batch's initial bias), timed on the host cores.  The oracle
+    converts each expert's bf16 weights to float64 when it first uses them;
+    that conversion is timed apart from the arithmetic, and the full batch's
+    time is estimated from both (every expert is touched at T=16384).  In
+    the same leg, every timed workload's re-run step is checked against the
+    oracle (probe_parity)."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from oracle import moe_oracle as O
@@ -470,29 +656,16 @@ def cpu_baseline(cfg, inp, ntok, torch):
     x = inp["x"][:ntok].float().cpu().numpy()
     wr = inp["w_router"].cpu().numpy()
     bias = inp["bias"].cpu().numpy()
-    # the experts this sample needs, fetched before timing
-    r = O.route(x, wr, bias, n_routed=cfg.E, k=cfg.k)
-    need = sorted(set(r["topk_idx"].ravel().tolist()))
-
-    class Lazy:
-        def __init__(self, t, ids):
-            self.n = t.shape[0]
-            self.d = {e: t[e].float().cpu().numpy() for e in ids}
-
-        def __getitem__(self, e):
-            return self.d[e]
-
-        def __len__(self):
-            return self.n
-
-    weights = {"w_gate": Lazy(inp["w_gate"], need), "w_up": Lazy(inp["w_up"], need),
-               "w_down": Lazy(inp["w_down"], need)}
-    for n in ("ws_gate", "ws_up", "ws_down"):
-        weights[n] = [inp[n][s].float().cpu().numpy() for s in range(cfg.S)]
+    weights = _oracle_weights(inp)
     t0 = time.perf_counter()
     out = O.moe_forward(x, wr, weights, bias, cfg.gamma, k=cfg.k)
     dt = time.perf_counter() - t0
     assert out["y"].shape == (ntok, cfg.d)
+    up_s = sum(w.seconds for w in weights.values())
+    n_mats = sum(w.n for w in weights.values())
+    arith_s = dt - up_s
+    # full batch: all (E + S) experts' 3 matrices converted once, arithmetic x T/ntok
+    full_s = up_s / max(1, n_mats) * 3 * (cfg.E + cfg.S) + arith_s * cfg.T / ntok
     info = threadpool_info()
     threads = max([i.get("num_threads", 1) for i in info] + [1])
     blas = sorted({f"{i.get('internal_api')} {i.get('version')}" for i in info
@@ -506,12 +679,30 @@ def cpu_baseline(cfg, inp, ntok, torch):
         pass
     # the sample's arithmetic: router plus 8 SwiGLU experts per token (6 routed, 2 shared)
     flop = ntok * (2.0 * cfg.d * (cfg.E + cfg.S) + (cfg.k + cfg.S) * 6.0 * cfg.d * cfg.F)
-    return {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "seconds": round(dt, 2), "gflop_s": round(flop / dt / 1e9, 1), "cpu": cpu,
-            "blas": blas,
-            "sample": (f"first {ntok} tokens of the T={cfg.T} batch: full oracle forward "
-                       f"(fp64 router, dispatch, {len(need)} routed + {cfg.S} shared SwiGLU "
-                       f"experts, combine, bias update)")}
+    n_routed = len(set(out["router"]["topk_idx"].ravel().tolist()))
+    res = {"value": ntok / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "seconds": round(dt, 2), "cpu": cpu, "blas": blas,
+           "weight_upcast_s": round(up_s, 2), "arithmetic_s": round(arith_s, 2),
+           "arithmetic_tokens_s": round(ntok / arith_s, 1),
+           "arithmetic_gflop_s": round(flop / arith_s / 1e9, 1),
+           "full_batch_estimate": {"seconds": round(full_s, 1),
+                                   "tokens_s": round(cfg.T / full_s, 1),
+                                   "how": "weight conversion of all experts at the sample's "
+                                          "per-matrix rate + the sample's arithmetic x T/ntok"},
+           "sample": (f"first {ntok} tokens of the T={cfg.T} batch: full oracle forward "
+                      f"(fp64 router, dispatch, {n_routed} routed + {cfg.S} shared SwiGLU "
+                      f"experts, combine, bias update), the experts' bf16 weights converted "
+                      f"to fp64 as the oracle uses them")}
+    parity = {}
+    for pr in PROBES:
+        key = pr["key"]
+        try:
+            parity[key] = probe_parity(pr, cfg, inp, torch, L, synth, configs, O,
+                                       pr["nsample"])
+        except Exception as e:  # noqa: BLE001 - reported, not hidden
+            parity[key] = {"error": f"{type(e).__name__}: {e}"}
+    res["parity_vs_oracle"] = parity
+    return res
 
 
 def section(result, key, fn):
@@ -526,13 +717,13 @@ def section(result, key, fn):
         result[key] = {"error": f"{type(e).__name__}: {e}"}
 
 
-def decode(dc, args, torch, L, synth):
-    """A decode workload (bf16 or FP4 routed weights) against HBM bandwidth."""
+def decode_run(dc, args, torch, L, synth, fresh_bias):
+    """One timed decode sequence and its figures against HBM bandwidth."""
     steps = max(args.steps, 20)
     inp, desc, w, ws, counts, ms, _ = time_forward(dc, steps, args.warmup, torch, L, synth,
-                                                   replay=True)
+                                                   replay=True, fresh_bias=fresh_bias)
     stages = None
-    if not dc.fp4_weights:
+    if not dc.fp4_weights and fresh_bias:
         stages, _, _ = time_stages(dc, inp, desc, w, 10, torch, L, synth)
     # bytes of each timed step (its own active experts), averaged
     per_step = [decode_bytes(dc, c) for c in inp.pop("_loads")]
@@ -540,10 +731,7 @@ def decode(dc, args, torch, L, synth):
     actives = [n for _, n in per_step]
     n_active = round(sum(actives) / len(actives), 1)
     gbs = nbytes / (ms / 1e3) / 1e9
-    weights = ("routed experts' weights MXFP4 (E2M1, power-of-two scale per 32), shared "
-               "experts bf16" if dc.fp4_weights else "bf16 weights")
-    out = {"workload": f"decode MoE layer, {dc.describe()}, {weights}, fp32 router",
-           "tokens_s": round(dc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
+    out = {"tokens_s": round(dc.T / (ms / 1e3), 1), "ms_per_step": round(ms, 4),
            "ms_per_step_p10_p50_p90": inp.pop("_spread"),
            "ms_per_step_hip_graph": round(inp.pop("_graph_ms"), 4)}
     if stages is not None:
@@ -553,8 +741,33 @@ def decode(dc, args, torch, L, synth):
                        "active_experts": n_active,
                        "active_experts_first_last": [actives[0], actives[-1]],
                        "scope": "whole moe_forward step; bytes averaged over the timed steps"}
+    # output sampled on every token at the stated bias; FP4 layers are
+    # checked for routing here (their outputs in the GPU tests: the oracle's
+    # quantization takes ~1 s per matrix)
+    PROBES.append({"workload": dc.name, "bias": inp.pop("_probe_bias"), "x_step": None,
+                   "nsample": 0 if dc.fp4_weights else (dc.T if fresh_bias else 8),
+                   "key": dc.name + ("" if fresh_bias else " (bias drifting)"),
+                   "what": "the last timed step" + (", bias as stated" if fresh_bias
+                                                    else ", bias after the earlier steps")})
     del inp, ws
     torch.cuda.empty_cache()
+    return out
+
+
+def decode(dc, args, torch, L, synth):
+    """A decode workload (bf16 or FP4 routed weights) against HBM bandwidth:
+    timed as stated (every step routes with the workload's bias, here 0, and
+    applies its own bias update), and, beside it, as a sequence whose bias
+    drifts from step to step (at T=64 a drifting bias spreads the tokens
+    over more experts, so those steps stream more bytes)."""
+    weights = ("routed experts' weights MXFP4 (E2M1, power-of-two scale per 32), shared "
+               "experts bf16" if dc.fp4_weights else "bf16 weights")
+    out = {"workload": f"decode MoE layer, {dc.describe()}, {weights}, fp32 router, every "
+                       f"step from the stated bias"}
+    out.update(decode_run(dc, args, torch, L, synth, fresh_bias=True))
+    drift = decode_run(dc, args, torch, L, synth, fresh_bias=False)
+    out["bias_drifting"] = {"what": f"consecutive steps, the bias moving by {dc.gamma} per "
+                                    f"step from the stated one", **drift}
     return out
 
 
@@ -567,6 +780,8 @@ def prefill(pc, args, torch, L, synth):
                                                 torch, L, synth)
     f_gu, f_dn = expert_flops(pc)
     nbytes, n_active = decode_bytes(pc, counts.cpu())
+    PROBES.append({"workload": pc.name, "bias": inp.pop("_probe_bias"), "x_step": None,
+                   "nsample": 64, "key": pc.name, "what": "the last timed step"})
     del inp, ws
     torch.cuda.empty_cache()
     return {"workload": f"prefill-chunk MoE layer, {pc.describe()}, fp32 router",
@@ -581,6 +796,8 @@ def native(nc, args, torch, L, synth):
     inp, _, _, ws, _, ms, _ = time_forward(nc, max(5, min(args.steps, 10)), args.warmup,
                                            torch, L, synth)
     f_gu, f_dn = expert_flops(nc)
+    PROBES.append({"workload": nc.name, "bias": inp.pop("_probe_bias"), "x_step": None,
+                   "nsample": 8, "key": nc.name, "what": "the last timed step"})
     del inp, ws
     torch.cuda.empty_cache()
     return {"workload": f"MoE layer at the native shape, {nc.describe()}, gates "
@@ -648,6 +865,8 @@ def main():
     }
     max_load = counts.max().item()
     result["max_over_mean_load"] = round(max_load / (cfg.T * cfg.k / cfg.E), 3)
+    PROBES.insert(0, {"workload": cfg.name, "bias": inp.pop("_probe_bias"), "x_step": None,
+                      "nsample": 8, "key": cfg.name, "what": "the last timed step"})
     del ws
     torch.cuda.empty_cache()
     if not args.no_ep_share:
@@ -665,15 +884,20 @@ def main():
         section(result, "native", lambda: native(configs.get(args.native_workload), args,
                                                  torch, L, synth))
     if not args.no_skewed:
-        section(result, "skewed", lambda: time_skewed(configs.get(args.skewed_workload),
-                                                      args.skewed_steps, torch, L, synth))
-        section(result, "capacity", lambda: time_skewed(configs.get(args.capacity_workload),
-                                                        args.skewed_steps, torch, L, synth))
+        for key, name in (("skewed", args.skewed_workload), ("capacity", args.capacity_workload)):
+            section(result, key, lambda: time_skewed(configs.get(name), args.skewed_steps,
+                                                     torch, L, synth))
+            probe = result[key].pop("_probe", None)
+            if probe is not None:
+                PROBES.append({"workload": name, "bias": probe["bias"],
+                               "x_step": probe["x_step"], "nsample": 8, "key": name,
+                               "what": "the first timed batch"})
     if not args.no_lab:
         section(result, "balance_lab", lambda: balance_lab(configs.get(args.lab_workload), torch))
     if not args.no_cpu_baseline:
         section(result, "cpu_baseline",
-                lambda: cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch))
+                lambda: cpu_baseline(cfg, inp, args.cpu_sample_tokens, torch, L, synth,
+                                     configs))
     print(json.dumps(result), flush=True)
 
 

@@ -31,8 +31,10 @@
  *   (MOE_ERR_HIP).  Device faults surface at the caller's next sync.
  * - No C++ exception crosses this boundary.
  * - Floating-point inputs holding NaN or Inf give undefined results.
- *   Out-of-range expert ids handed to moe_dispatch are skipped (they never
- *   cause out-of-bounds writes) and leave the outputs undefined.
+ *   A pair whose expert id handed to moe_dispatch lies outside [0, E) is
+ *   counted in no load, enters no expert's rows and gets pair_pos = -1, so
+ *   moe_combine leaves it out as it does a pair dropped at capacity (and
+ *   the bias update sees only the valid pairs).
  * - Supported shapes: E in {64, 128, 256}, S in {0, 1, 2}, k = 6;
  *   act == weight, either MOE_F32 or MOE_BF16, or act MOE_BF16 with weight
  *   MOE_MXFP4 for decode batches (T * k < 48 * E, the batches whose experts
@@ -226,8 +228,12 @@ moe_status moe_expert_gate_up(const moe_desc* desc, const void* x,
                               const int32_t* sorted_pair, void* h, void* ws,
                               size_t ws_bytes, hipStream_t stream);
 
-/* Down half of every expert: y = h W_down^T.  Reads h [(k+S)*T, F];
- * writes y_routed [T*k, d] and y_shared [S, T, d]. */
+/* Down half of every expert ("Under The Hood", expert configuration: the
+ * SwiGLU FFN's output projection; "Inkling, Dissected", 02: an expert's
+ * second matrix product after the nonlinearity): y = h W_down^T per expert,
+ * matrix cores, fp32 accumulation, rounded to act.  Reads h [(k+S)*T, F]
+ * (routed rows in expert-sorted order, then each shared expert's T rows);
+ * writes y_routed [T*k, d] (sorted order) and y_shared [S, T, d]. */
 moe_status moe_expert_down(const moe_desc* desc, const moe_weights* w,
                            const int32_t* offsets, const void* h,
                            void* y_routed, void* y_shared, void* ws,
@@ -249,8 +255,12 @@ moe_status moe_expert_down_marked(const moe_desc* desc, const moe_weights* w,
                                   size_t ws_bytes, hipEvent_t* marks,
                                   hipStream_t stream);
 
-/* Both halves: moe_expert_gate_up then moe_expert_down, h in the
- * workspace. */
+/* Every expert's whole FFN ("Under The Hood", expert configuration:
+ * y_e = W_down (silu(W_gate x) * W_up x) for each routed expert on the
+ * tokens dispatched to it and each shared expert on every token;
+ * "Inkling, Dissected", 02: each token visits its 6 routed experts and the
+ * 2 shared ones): moe_expert_gate_up then moe_expert_down, h in the
+ * workspace.  Same inputs and outputs as the two calls. */
 moe_status moe_expert_ffn(const moe_desc* desc, const void* x,
                           const moe_weights* w, const int32_t* offsets,
                           const int32_t* sorted_pair, void* y_routed,
@@ -285,10 +295,13 @@ moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts,
 moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
-/* The whole layer: router (with the incoming bias), dispatch, expert FFN,
- * combine, then the bias update in place (the next batch routes with the
- * new bias; gamma == 0 leaves it unchanged).  Writes y [T, d] and, when
- * `routing` is non-NULL, its non-NULL members. */
+/* The whole layer ("Inkling, Dissected", 02b: the per-token sketch of
+ * router, top-6, joint gates and the weighted sum of the 8 experts' outputs;
+ * 02e: the bias moves once the batch is done): router (with the incoming
+ * bias), dispatch, expert FFN, combine, then the bias update in place (the
+ * next batch routes with the new bias; gamma == 0 leaves it unchanged).
+ * Writes y [T, d] and, when `routing` is non-NULL, its non-NULL members
+ * (the tensors a caller wants to keep; the others live in the workspace). */
 moe_status moe_forward(const moe_desc* desc, const void* x,
                        const moe_weights* w, float* bias, float gamma, void* y,
                        const moe_routing* routing_or_null, void* ws,

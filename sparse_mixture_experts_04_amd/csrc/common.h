@@ -66,10 +66,11 @@ inline int dispatch_segments(const Shape& s) {
 int ffn_row_tile(const Shape& s);
 
 // ---- launchers (return hipSuccess or the launch error) -------------------
+// refine: T + 1 ints of workspace (the tokens the exact pass redoes).
 hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
                          const float* bias, int32_t* topk_idx, float* gates,
                          float* margin, bf16_t* wplanes, double* partial,
-                         hipStream_t st);
+                         int32_t* refine, hipStream_t st);
 
 hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,

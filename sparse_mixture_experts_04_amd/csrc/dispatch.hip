@@ -19,7 +19,9 @@
 //                       expert.
 // Within an expert the pairs therefore come out in ascending pair number,
 // i.e. ascending token.  Capacity ("Inkling, Dissected" 02d): a pair whose
-// rank reaches the expert's capacity is dropped (pair_pos = -1).
+// rank reaches the expert's capacity is dropped (pair_pos = -1).  A pair
+// whose expert id lies outside [0, E) is counted nowhere and also gets
+// pair_pos = -1.
 #include "common.h"
 
 namespace moe {
@@ -108,9 +110,12 @@ __global__ __launch_bounds__(64) void dispatch_scatter(const int32_t* __restrict
   const long long base = static_cast<long long>(blockIdx.x) * kDispatchSeg;
   for (int c = 0; c < kDispatchSeg; c += 64) {
     const long long p = base + c + lane;
-    bool valid = p < npairs;
-    const int e = valid ? topk[p] : 0;
-    valid = valid && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    const bool in_range = p < npairs;
+    const int e = in_range ? topk[p] : 0;
+    const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    // a pair whose id is outside [0, E) joins no expert: it is marked
+    // dropped, so that combine leaves it out like a pair over capacity
+    if (in_range && !valid) pair_pos[p] = -1;
     unsigned long long peers = __ballot(valid);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {

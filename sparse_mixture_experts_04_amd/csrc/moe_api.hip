@@ -81,12 +81,13 @@ struct Carver {
   }
 };
 
-struct RouterWs { bf16_t* planes; double* partial; };
+struct RouterWs { bf16_t* planes; double* partial; int32_t* refine; };
 RouterWs carve_router(Carver& c, const Shape& s) {
   RouterWs r;
   const size_t npad = router_cols_padded(s);
   r.planes = c.take<bf16_t>(3 * npad * s.d);
   r.partial = c.take<double>(static_cast<size_t>(router_ksplits(s)) * s.T * npad);
+  r.refine = c.take<int32_t>(static_cast<size_t>(s.T) + 1);
   return r;
 }
 int32_t* carve_dispatch(Carver& c, const Shape& s) {
@@ -207,7 +208,7 @@ moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router
   Carver c{static_cast<char*>(ws)};
   const RouterWs r = carve_router(c, s);
   return hip_status(launch_router(s, x, w_router, bias, topk_idx, gates, margin_or_null,
-                                  r.planes, r.partial, stream));
+                                  r.planes, r.partial, r.refine, stream));
 }
 
 moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts,
@@ -403,7 +404,7 @@ moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* 
   };
   const int mt = ffn_row_tile(s);
   hipError_t e = launch_router(s, x, w->w_router, bias, f.topk, f.gates, margin,
-                               f.router.planes, f.router.partial, stream);
+                               f.router.planes, f.router.partial, f.router.refine, stream);
   e = mark(0, e);
   if (e == hipSuccess)
     e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg, stream);

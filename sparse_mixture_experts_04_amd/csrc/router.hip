@@ -21,10 +21,21 @@
 
 namespace moe {
 
+// Gap between adjacent keys (s + b) among a token's k + 1 best under which
+// its selection is redone from exact logits (router_refine): far above the
+// keys' error from the matrix-core logits (those keys are within ~1e-7 of
+// exact; see router_select), so every token whose picks or their order
+// could differ from exact arithmetic is redone, and few enough tokens that
+// the refinement is cheap.
+constexpr double kRefineGap = 2e-5;
+
 // ---------------------------------------------------------------- planes
 
+// Also empties the refinement list of this router call (refine[0] = 0).
 __global__ __launch_bounds__(256) void router_split_planes(
-    const float* __restrict__ w, int rows, int d, int rows_pad, bf16_t* __restrict__ planes) {
+    const float* __restrict__ w, int rows, int d, int rows_pad, bf16_t* __restrict__ planes,
+    int32_t* __restrict__ refine) {
+  if (blockIdx.x == 0 && threadIdx.x == 0) refine[0] = 0;
   const size_t n = static_cast<size_t>(rows_pad) * d;
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -366,92 +377,87 @@ __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
-// One wave per token.  E = 64 * EPL: lane l owns routed experts l, l+64,
-// ...; lanes 0..S-1 also own the shared experts E+lane.  K routed picks in
-// rank order (descending key, exact ties to the lower id), then one more
-// round for the first expert left out (the margin).
-template <int K, int S, int EPL>
-__global__ __launch_bounds__(256) void router_select(
-    const double* __restrict__ partial, int nks, int T, int npad, int E,
-    const float* __restrict__ bias, int32_t* __restrict__ topk, float* __restrict__ gates,
-    float* __restrict__ margin, bool logsumexp_norm, double gate_scale) {
-  const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave leaves together; no block barrier below
-
-  double sv[EPL], zv[EPL], key[EPL];
-  bool taken[EPL];
-  const size_t kstride = static_cast<size_t>(T) * npad;
+// K + 1 rounds of a wave-wide argmax over the candidates the lanes hold:
+// lane l holds Q of them (expert ids id[q], -1 for none; keys, affinities
+// s and logits z).  Rank order is descending key, exact ties to the lower
+// id.  Fills, on every lane, the ids, s and z of the K picks and the keys of
+// the K + 1 best (the last one for the margin).
+template <int K, int Q>
+__device__ __forceinline__ void rank_rounds(int lane, const int (&id)[Q], const double (&key)[Q],
+                                            const double (&sv)[Q], const double (&zv)[Q],
+                                            int (&i_sel)[K], double (&s_sel)[K],
+                                            double (&z_sel)[K], double (&k_sel)[K + 1]) {
+  bool taken[Q];
 #pragma unroll
-  for (int q = 0; q < EPL; ++q) {
-    const int c = lane + 64 * q;
-    zv[q] = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + c);
-    const double s = 1.0 / (1.0 + exp(-zv[q]));
-    sv[q] = s;
-    key[q] = s + static_cast<double>(bias[c]);
-    taken[q] = false;
-  }
-  double s_shared = 0.0, z_shared = 0.0;
-  if (lane < S) {
-    const double z = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + E + lane);
-    s_shared = 1.0 / (1.0 + exp(-z));
-    z_shared = z;
-  }
-
-  double s_sel[K + S], z_sel[K + S];
-  int i_sel[K];
-  double k_last = 0.0, k_next = 0.0;
+  for (int q = 0; q < Q; ++q) taken[q] = id[q] < 0;
 #pragma unroll
   for (int r = 0; r <= K; ++r) {
     double bk = -INFINITY;
-    int bi = 0x7fffffff;
+    int bi = 0x7fffffff, bq = -1;
 #pragma unroll
-    for (int q = 0; q < EPL; ++q) {
-      const int c = lane + 64 * q;
-      if (!taken[q] && better(key[q], c, bk, bi)) {
+    for (int q = 0; q < Q; ++q)
+      if (!taken[q] && better(key[q], id[q], bk, bi)) {
         bk = key[q];
-        bi = c;
+        bi = id[q];
+        bq = q;
       }
-    }
+    int bl = lane;
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const double ok = __shfl_xor(bk, off);
       const int oi = __shfl_xor(bi, off);
+      const int ol = __shfl_xor(bl, off);
+      const int oq = __shfl_xor(bq, off);
       if (better(ok, oi, bk, bi)) {
         bk = ok;
         bi = oi;
+        bl = ol;
+        bq = oq;
       }
     }
-    if (r == K) {
-      k_next = bk;
-    } else {
-      const int q = bi >> 6;
-      const int owner = bi & 63;
+    k_sel[r] = bk;
+    if (r < K) {
       double my = sv[0], mz = zv[0];
 #pragma unroll
-      for (int qq = 1; qq < EPL; ++qq) {
-        my = q == qq ? sv[qq] : my;
-        mz = q == qq ? zv[qq] : mz;
+      for (int qq = 1; qq < Q; ++qq) {
+        my = bq == qq ? sv[qq] : my;
+        mz = bq == qq ? zv[qq] : mz;
       }
-      s_sel[r] = __shfl(my, owner);
-      z_sel[r] = __shfl(mz, owner);
-      if (lane == owner) {
+      s_sel[r] = __shfl(my, bl);
+      z_sel[r] = __shfl(mz, bl);
+      if (lane == bl) {
 #pragma unroll
-        for (int qq = 0; qq < EPL; ++qq) taken[qq] = taken[qq] || q == qq;
+        for (int qq = 0; qq < Q; ++qq) taken[qq] = taken[qq] || bq == qq;
       }
       i_sel[r] = bi;
-      k_last = bk;
     }
+  }
+}
+
+// Gates of the K picks and the S shared experts (s_sh, z_sh: shared expert
+// j's affinity and logit on lane j), then the outputs of token t: topk in
+// rank order, gates in slot order, margin = key_K - key_(K+1).  Gates:
+// s_j / sum s, or exp(logsigmoid(z_j) - logsumexp logsigmoid(z)), over the
+// K + S contributors in slot order, times gate_scale.
+template <int K, int S>
+__device__ __forceinline__ void write_token(int t, int lane, const int (&i_sel)[K],
+                                            const double (&s_pick)[K], const double (&z_pick)[K],
+                                            double s_sh, double z_sh,
+                                            const double (&k_sel)[K + 1],
+                                            int32_t* __restrict__ topk, float* __restrict__ gates,
+                                            float* __restrict__ margin, bool logsumexp_norm,
+                                            double gate_scale) {
+  double s_sel[K + S], z_sel[K + S];
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    s_sel[j] = s_pick[j];
+    z_sel[j] = z_pick[j];
   }
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    s_sel[K + j] = __shfl(s_shared, j);
-    z_sel[K + j] = __shfl(z_shared, j);
+    s_sel[K + j] = __shfl(s_sh, j);
+    z_sel[K + j] = __shfl(z_sh, j);
   }
-
-  // gates: s_j / sum s, or exp(logsigmoid(z_j) - logsumexp logsigmoid(z)),
-  // both over the k kept and S shared contributors in slot order, then
-  // times gate_scale.  Written as g_j = num_j / denom.
   double denom = 0.0;
   if (logsumexp_norm) {
 #pragma unroll
@@ -485,7 +491,185 @@ __global__ __launch_bounds__(256) void router_select(
     for (int j = 1; j < K + S; ++j) sj = lane == j ? s_sel[j] : sj;
     gates[static_cast<size_t>(t) * (K + S) + lane] = static_cast<float>(sj / denom);
   }
-  if (margin && lane == 0) margin[t] = static_cast<float>(k_last - k_next);
+  if (margin && lane == 0) margin[t] = static_cast<float>(k_sel[K - 1] - k_sel[K]);
+}
+
+__device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+// Keys of token t from the matrix-core logits (sum of the K-split partials):
+// lane l holds routed experts l + 64q.
+template <int EPL>
+__device__ __forceinline__ void token_keys(const double* __restrict__ partial, int nks, int T,
+                                           int npad, int t, int lane,
+                                           const float* __restrict__ bias, int (&id)[EPL],
+                                           double (&zv)[EPL], double (&sv)[EPL],
+                                           double (&key)[EPL]) {
+  const size_t kstride = static_cast<size_t>(T) * npad;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    id[q] = lane + 64 * q;
+    zv[q] = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + id[q]);
+    sv[q] = sigmoid64(zv[q]);
+    key[q] = sv[q] + static_cast<double>(bias[id[q]]);
+  }
+}
+
+// One wave per token, from the matrix-core logits.  Their error (the
+// matrix cores round each 32-term partial sum, by up to a few 1e-7 measured
+// on gfx950) can reorder keys that lie closer than ~1e-6.  A token with
+// two adjacent keys among its K + 1 best closer than kRefineGap is
+// therefore appended to `refine` (count at refine[0], tokens from refine[1];
+// the list's order does not matter), and router_refine redoes it from
+// exact logits; the outputs written here stand for every other token.
+template <int K, int S, int EPL>
+__global__ __launch_bounds__(256) void router_select(
+    const double* __restrict__ partial, int nks, int T, int npad, int E,
+    const float* __restrict__ bias, int32_t* __restrict__ topk, float* __restrict__ gates,
+    float* __restrict__ margin, bool logsumexp_norm, double gate_scale,
+    int32_t* __restrict__ refine) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;  // whole wave leaves together; no block barrier below
+
+  int id[EPL];
+  double zv[EPL], sv[EPL], key[EPL];
+  token_keys<EPL>(partial, nks, T, npad, t, lane, bias, id, zv, sv, key);
+  double z_sh = 0.0;
+  if (lane < S)
+    z_sh = sum_partials(partial, static_cast<size_t>(T) * npad, nks,
+                        static_cast<size_t>(t) * npad + E + lane);
+  int i_sel[K];
+  double s_pick[K], z_pick[K], k_sel[K + 1];
+  rank_rounds<K, EPL>(lane, id, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
+  write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk, gates,
+                    margin, logsumexp_norm, gate_scale);
+  double gap = INFINITY;
+#pragma unroll
+  for (int r = 0; r < K; ++r) gap = fmin(gap, k_sel[r] - k_sel[r + 1]);
+  if (lane == 0 && gap < kRefineGap) refine[1 + atomicAdd(refine, 1)] = t;
+}
+
+// Exact logits of the tokens router_select listed, for the experts that can
+// rank among their K + 1 best: every routed expert whose matrix-core key is
+// within kRefineGap of the (K + 1)-th best (a key's error is far below
+// kRefineGap / 2, so no other expert can rank there), and the shared
+// experts for the gates.  z = sum_c x[t,c] * w[e,c] in fp64: the products of
+// bf16 (or fp32) x and fp32 w are exact in fp64, so z is the dot product to
+// fp64 rounding and the picks are those of exact arithmetic unless two keys
+// agree to ~1e-15.  One workgroup per listed token (a fixed grid walks the
+// list): wave 0 lists the candidates; all 256 threads take 4 consecutive
+// elements of K per 1024, 4 candidates at a time, and the lane and wave sums
+// are added in a fixed order; wave 0 then ranks the candidates and writes
+// the token's outputs.
+template <int K, int S, int EPL>
+__global__ __launch_bounds__(256) void router_refine(
+    const double* __restrict__ partial, int nks, int T, int npad, int E, int d,
+    const void* __restrict__ xv, bool x_bf16, const float* __restrict__ w,
+    const int32_t* __restrict__ refine, const float* __restrict__ bias,
+    int32_t* __restrict__ topk, float* __restrict__ gates, float* __restrict__ margin,
+    bool logsumexp_norm, double gate_scale) {
+  constexpr int NB = 4;                   // candidates per pass over K
+  __shared__ int cand[64 * EPL + S];      // routed candidates, then the shared experts
+  __shared__ double zc[64 * EPL + S];     // their exact logits
+  __shared__ double wsum[4][NB];
+  __shared__ int s_nc;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int n = refine[0];
+  for (int i = blockIdx.x; i < n; i += gridDim.x) {
+    const int t = refine[1 + i];
+    if (wave == 0) {
+      int id[EPL];
+      double zv[EPL], sv[EPL], key[EPL];
+      token_keys<EPL>(partial, nks, T, npad, t, lane, bias, id, zv, sv, key);
+      int i_sel[K];
+      double s_pick[K], z_pick[K], k_sel[K + 1];
+      rank_rounds<K, EPL>(lane, id, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
+      const double thresh = k_sel[K] - kRefineGap;
+      int base = 0;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const bool c = key[q] >= thresh;
+        const unsigned long long m = __ballot(c);
+        if (c) cand[base + __popcll(m & ((1ull << lane) - 1ull))] = id[q];
+        base += __popcll(m);
+      }
+      if (lane < S) cand[base + lane] = E + lane;
+      if (lane == 0) s_nc = base;
+    }
+    __syncthreads();
+    const int nc = s_nc;
+    const int ntot = nc + S;
+    for (int b0 = 0; b0 < ntot; b0 += NB) {
+      double acc[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) acc[j] = 0.0;
+      for (int c = tid * 4; c < d; c += 1024) {
+        double xs[4];
+        if (x_bf16) {
+          const bf16_t* x = static_cast<const bf16_t*>(xv) + static_cast<size_t>(t) * d + c;
+          const uint2 v = *reinterpret_cast<const uint2*>(x);
+          xs[0] = bf16_to_f32(static_cast<bf16_t>(v.x & 0xffff));
+          xs[1] = bf16_to_f32(static_cast<bf16_t>(v.x >> 16));
+          xs[2] = bf16_to_f32(static_cast<bf16_t>(v.y & 0xffff));
+          xs[3] = bf16_to_f32(static_cast<bf16_t>(v.y >> 16));
+        } else {
+          const float4 v = *reinterpret_cast<const float4*>(
+              static_cast<const float*>(xv) + static_cast<size_t>(t) * d + c);
+          xs[0] = v.x;
+          xs[1] = v.y;
+          xs[2] = v.z;
+          xs[3] = v.w;
+        }
+        float4 wv[NB];
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (b0 + j < ntot)
+            wv[j] = *reinterpret_cast<const float4*>(w + static_cast<size_t>(cand[b0 + j]) * d + c);
+#pragma unroll
+        for (int j = 0; j < NB; ++j)
+          if (b0 + j < ntot) {
+            acc[j] = fma(xs[0], static_cast<double>(wv[j].x), acc[j]);
+            acc[j] = fma(xs[1], static_cast<double>(wv[j].y), acc[j]);
+            acc[j] = fma(xs[2], static_cast<double>(wv[j].z), acc[j]);
+            acc[j] = fma(xs[3], static_cast<double>(wv[j].w), acc[j]);
+          }
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc[j] += __shfl_xor(acc[j], off);
+      }
+      if (lane == 0) {
+#pragma unroll
+        for (int j = 0; j < NB; ++j) wsum[wave][j] = acc[j];
+      }
+      __syncthreads();
+      if (tid < NB && b0 + tid < ntot)
+        zc[b0 + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
+      __syncthreads();
+    }
+    if (wave == 0) {
+      // candidate q of lane l is cand[l + 64q] (routed ones only)
+      int id[EPL];
+      double zv[EPL], sv[EPL], key[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        const int j = lane + 64 * q;
+        id[q] = j < nc ? cand[j] : -1;
+        zv[q] = j < nc ? zc[j] : 0.0;
+        sv[q] = sigmoid64(zv[q]);
+        key[q] = j < nc ? sv[q] + static_cast<double>(bias[id[q]]) : -INFINITY;
+      }
+      const double z_sh = lane < S ? zc[nc + lane] : 0.0;
+      int i_sel[K];
+      double s_pick[K], z_pick[K], k_sel[K + 1];
+      rank_rounds<K, EPL>(lane, id, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
+      write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk,
+                        gates, margin, logsumexp_norm, gate_scale);
+    }
+    __syncthreads();
+  }
 }
 
 // ------------------------------------------------------------------ host
@@ -500,33 +684,49 @@ int router_ksplits(const Shape& s) {
   return want < nch ? want : nch;
 }
 
+struct SelectArgs {
+  const void* x;
+  const float* w_router;
+  const double* partial;
+  int nks, npad;
+  const float* bias;
+  int32_t* topk_idx;
+  float* gates;
+  float* margin;
+  int32_t* refine;
+};
+
+// Workgroups of router_refine: the listed tokens are few (an adjacent pair
+// of their best keys lies within kRefineGap), so a fixed grid walks the list.
+constexpr int kRefineGrid = 256;
+
 template <int S, int EPL>
-static void launch_select(const Shape& s, const double* partial, int nks, int npad,
-                          const float* bias, int32_t* topk_idx, float* gates, float* margin,
-                          hipStream_t st) {
-  router_select<6, S, EPL><<<(s.T + 3) / 4, 256, 0, st>>>(partial, nks, s.T, npad, s.E, bias,
-                                                          topk_idx, gates, margin,
-                                                          s.gate_logsumexp, s.gate_scale);
+static void launch_select(const Shape& s, const SelectArgs& a, hipStream_t st) {
+  router_select<6, S, EPL><<<(s.T + 3) / 4, 256, 0, st>>>(
+      a.partial, a.nks, s.T, a.npad, s.E, a.bias, a.topk_idx, a.gates, a.margin,
+      s.gate_logsumexp, s.gate_scale, a.refine);
+  router_refine<6, S, EPL><<<kRefineGrid, 256, 0, st>>>(
+      a.partial, a.nks, s.T, a.npad, s.E, s.d, a.x, s.bf16, a.w_router, a.refine, a.bias,
+      a.topk_idx, a.gates, a.margin, s.gate_logsumexp, s.gate_scale);
 }
 
 template <int S>
-static void launch_select_e(const Shape& s, const double* partial, int nks, int npad,
-                            const float* bias, int32_t* topk_idx, float* gates, float* margin,
-                            hipStream_t st) {
-  if (s.E == 64) launch_select<S, 1>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
-  else if (s.E == 128) launch_select<S, 2>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
-  else launch_select<S, 4>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
+static void launch_select_e(const Shape& s, const SelectArgs& a, hipStream_t st) {
+  if (s.E == 64) launch_select<S, 1>(s, a, st);
+  else if (s.E == 128) launch_select<S, 2>(s, a, st);
+  else launch_select<S, 4>(s, a, st);
 }
 
 hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
                          const float* bias, int32_t* topk_idx, float* gates, float* margin,
-                         bf16_t* wplanes, double* partial, hipStream_t st) {
+                         bf16_t* wplanes, double* partial, int32_t* refine, hipStream_t st) {
   if (s.T == 0) return hipSuccess;
   const int npad = router_cols_padded(s);
   const size_t n = static_cast<size_t>(npad) * s.d;
   int blocks = static_cast<int>((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  router_split_planes<<<blocks, 256, 0, st>>>(w_router, s.E + s.S, s.d, npad, wplanes);
+  router_split_planes<<<blocks, 256, 0, st>>>(w_router, s.E + s.S, s.d, npad, wplanes,
+                                              refine);
   const int nks = router_ksplits(s);
   const int chunk = router_chunk(s);
   dim3 grid((s.T + 127) / 128, npad / kRouterColTile, nks);
@@ -535,9 +735,10 @@ hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
                                               npad, nks, chunk, partial);
   else
     router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, chunk, partial);
-  if (s.S == 0) launch_select_e<0>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
-  else if (s.S == 1) launch_select_e<1>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
-  else launch_select_e<2>(s, partial, nks, npad, bias, topk_idx, gates, margin, st);
+  const SelectArgs a{x, w_router, partial, nks, npad, bias, topk_idx, gates, margin, refine};
+  if (s.S == 0) launch_select_e<0>(s, a, st);
+  else if (s.S == 1) launch_select_e<1>(s, a, st);
+  else launch_select_e<2>(s, a, st);
   return hipGetLastError();
 }
 

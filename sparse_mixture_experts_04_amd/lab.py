@@ -3,17 +3,9 @@
 A frozen router, one fresh batch per step, a hard capacity per expert and
 the selection-only bias of 02e: each step is moe_router -> moe_dispatch
 (capacity-limited) -> moe_bias_update through the C ABI, on buffers
-allocated once.  The lab's measures are taken on the step's outputs:
-
-* MaxVio: the hottest expert's demand over the ideal load k*T/E, minus 1;
-* drop rate: the fraction of the k*T expert slots dropped at capacity;
-* layer quality: the gate-weighted affinity of the surviving pairs
-  (g_j = s_j over the sum of s over the token's picks, a dropped pair
-  contributing nothing) over that of the unbiased, uncapacitated top-k,
-  summed over the batch.
-
-The measures read the affinities s = sigmoid(x . w_i) in float64 with torch
-on the device; they are bookkeeping around the step, never part of it.
+allocated once.  The step's outputs (loads, kept pairs, picks, gates) stay
+in the buffers below, where a harness reads them to take the lab's
+measures; this module computes none of them.
 """
 import torch
 
@@ -43,7 +35,6 @@ class BalanceLab:
         self.pair_pos = torch.empty(T * k, dtype=i32, device=device)
         self.ws_router = L.alloc_workspace(self.desc, L.CALL_ROUTER, device)
         self.ws_dispatch = L.alloc_workspace(self.desc, L.CALL_DISPATCH, device)
-        self.w64 = w_router.to(torch.float64)
 
     def reset(self, bias=None):
         if bias is None:
@@ -82,18 +73,3 @@ class BalanceLab:
         torch.cuda.synchronize()
         self.bias.copy_(saved)
         return g
-
-    def measures(self, x):
-        """(max_vio, drop_rate, quality) of the last step on tokens x, as
-        float64 device scalars (no host synchronisation)."""
-        T, E, k = self.cfg.T, self.cfg.E, self.cfg.k
-        slots = float(k * T)
-        max_vio = self.counts.max().to(torch.float64) * (E / slots) - 1.0
-        kept = (self.pair_pos >= 0).view(T, k)
-        drop_rate = 1.0 - kept.sum().to(torch.float64) / slots
-        s = torch.sigmoid(x.to(torch.float64) @ self.w64.T)
-        sel = torch.gather(s, 1, self.topk.long())
-        captured = (self.gates.to(torch.float64) * sel * kept).sum()   # the router's own gates
-        best = torch.topk(s, k, dim=1).values
-        oracle = (best * best / best.sum(dim=1, keepdim=True)).sum()
-        return torch.stack([max_vio, drop_rate, captured / oracle])

@@ -99,6 +99,14 @@ def check_routing(x64, wr64, b64, topk_gpu, gates_gpu, k=6, gate_norm="ratio", g
     exempt = r["margin"] < TIE_MARGIN
     mism = np.any(topk_gpu != r["topk_idx"], axis=1)
     bad = mism & ~exempt
+    if bad.any():
+        for t in np.nonzero(bad)[0][:3]:
+            o = np.argsort(-r["key"][t], kind="stable")[:8]
+            keys = [(int(e), round(float(r["key"][t][e]), 9)) for e in o]
+            logits = [round(float(r["z"][t][e]), 6) for e in o]
+            log(f"  token {t}: oracle picks {r['topk_idx'][t].tolist()} margin "
+                f"{r['margin'][t]:.3e}; GPU picks {topk_gpu[t].tolist()}; oracle top-8 "
+                f"(id, key) {keys}; their logits {logits}")
     assert not bad.any(), f"{bad.sum()} tokens differ in selection with margin >= {TIE_MARGIN}: " \
                           f"first {np.nonzero(bad)[0][:5]}"
     # GPU picks are always a valid top-k set: distinct routed ids
@@ -155,3 +163,43 @@ def expert_getter(inp, E=256):
 def host_weights(inp):
     return {k: inp[k].to(torch.float32).cpu().numpy()
             for k in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+
+
+class DeviceExperts:
+    """One expert stack ([n, out, in] on the device) seen by the oracle as a
+    sequence of float64 host matrices, converted one expert at a time on
+    access (the whole stack in float64 would not fit in host memory at the
+    large workloads).  ``upcast_s`` accumulates the time spent converting."""
+
+    def __init__(self, t):
+        self.t = t
+        self.upcast_s = 0.0
+
+    def __len__(self):
+        return self.t.shape[0]
+
+    def __getitem__(self, e):
+        t0 = time.perf_counter()
+        m = np64(self.t[e])
+        self.upcast_s += time.perf_counter() - t0
+        return m
+
+
+def device_weights(inp):
+    """The oracle's ``weights`` mapping over the device expert stacks."""
+    return {k: DeviceExperts(inp[k])
+            for k in ("w_gate", "w_up", "w_down", "ws_gate", "ws_up", "ws_down")}
+
+
+def per_expert_rel_l2(got, ref, offsets):
+    """Largest relative L2 error over the row blocks offsets[e]:offsets[e+1]
+    of expert-sorted outputs, and the expert it occurs at."""
+    worst, at = 0.0, -1
+    for e in range(len(offsets) - 1):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi > lo:
+            err = rel_l2(got[lo:hi], ref[lo:hi])
+            if err > worst:
+                worst, at = err, e
+    return worst, at
+
