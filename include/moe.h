@@ -24,8 +24,9 @@
  * - Every tensor pointer is a DEVICE pointer owned by the caller; tensors
  *   are dense row-major, 16-byte aligned (256 recommended).  The library
  *   never allocates, frees or synchronises; it keeps no mutable global
- *   state.  Workspace is caller-provided device memory of at least
- *   moe_workspace_size() bytes for that call.
+ *   state apart from the scratch array of moe_dispatch_noalloc (one per
+ *   GPU, described there).  Workspace is caller-provided device memory of
+ *   at least moe_workspace_size() bytes for that call.
  * - Calls are asynchronous on `stream`.  The returned status covers host-side
  *   validation (nothing is launched when it is not MOE_OK) plus launch errors
  *   (MOE_ERR_HIP).  Device faults surface at the caller's next sync.
@@ -217,6 +218,23 @@ moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_pair,
                         int32_t* pair_pos, void* ws, size_t ws_bytes,
                         hipStream_t stream);
+
+/* Dispatch without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments (minus the workspace), results and
+ * errors as moe_dispatch; its scratch (the per-segment expert counts,
+ * ceil(T*k / 512) * E + 1 ints) lives in a 1 MiB device array the library
+ * holds on each GPU it runs on until the process ends, so T * k may be at
+ * most 523776 pairs at E = 256 (1048064 at E = 128, 2096640 at E = 64);
+ * larger batches return MOE_ERR_UNSUPPORTED before anything launches.  The
+ * first call on a device looks the array up there (MOE_ERR_HIP if that
+ * fails).  The call allocates and frees nothing.  Every call on one GPU
+ * shares that GPU's array: calls that overlap on one GPU (on different
+ * streams, or from different host threads without ordering) race. */
+moe_status moe_dispatch_noalloc(const moe_desc* desc, const int32_t* topk_idx,
+                                int32_t* counts, int32_t* offsets,
+                                int32_t* sorted_pair, int32_t* pair_pos,
+                                hipStream_t stream);
 
 /* Gate/up half of every expert ("Under The Hood", expert configuration:
  * SwiGLU experts): h = silu(X W_gate^T) * (X W_up^T), X the rows of x

@@ -24,7 +24,8 @@ STATUS = {0: "MOE_OK", 1: "MOE_ERR_NULL", 2: "MOE_ERR_SHAPE", 3: "MOE_ERR_DTYPE"
 SYMBOLS = ("moe_abi_version", "moe_status_string", "moe_workspace_size", "moe_router",
            "moe_dispatch", "moe_expert_gate_up", "moe_expert_down", "moe_expert_ffn",
            "moe_combine", "moe_bias_update", "moe_forward", "moe_expert_gate_up_marked",
-           "moe_expert_down_marked", "moe_quantize_mxfp4", "moe_forward_marked")
+           "moe_expert_down_marked", "moe_quantize_mxfp4", "moe_forward_marked",
+           "moe_dispatch_noalloc")
 
 
 class MoEError(RuntimeError):
@@ -67,6 +68,7 @@ def _load(path=LIB_PATH):
         "moe_workspace_size": (I, [D, I, ctypes.POINTER(Z)]),
         "moe_router": (I, [D, P, P, P, P, P, P, P, Z, P]),
         "moe_dispatch": (I, [D, P, P, P, P, P, P, Z, P]),
+        "moe_dispatch_noalloc": (I, [D, P, P, P, P, P, P]),
         "moe_expert_gate_up": (I, [D, P, W, P, P, P, P, Z, P]),
         "moe_expert_down": (I, [D, W, P, P, P, P, P, Z, P]),
         "moe_expert_gate_up_marked": (I, [D, P, W, P, P, P, P, Z, P, P]),
@@ -231,6 +233,20 @@ def dispatch(desc, topk_idx, counts, offsets, sorted_pair, pair_pos, ws=None):
                           _ptr(pair_pos, torch.int32, (T * k,), "pair_pos"),
                           _ptr(ws, torch.uint8, None, "ws"), ws.numel(), _stream(counts.device))
     _check("moe_dispatch", st)
+
+
+def dispatch_noalloc(desc, topk_idx, counts, offsets, sorted_pair, pair_pos):
+    """moe_dispatch_noalloc: the dispatch with its scratch in the library's
+    own device array (no workspace, nothing allocated)."""
+    T, E, k = desc.T, desc.E, desc.k
+    st = lib.moe_dispatch_noalloc(ctypes.byref(desc),
+                                  _ptr(topk_idx, torch.int32, (T, k), "topk_idx"),
+                                  _ptr(counts, torch.int32, (E,), "counts"),
+                                  _ptr(offsets, torch.int32, (E + 1,), "offsets"),
+                                  _ptr(sorted_pair, torch.int32, (T * k,), "sorted_pair"),
+                                  _ptr(pair_pos, torch.int32, (T * k,), "pair_pos"),
+                                  _stream(counts.device))
+    _check("moe_dispatch_noalloc", st)
 
 
 def expert_gate_up(desc, x, weights, offsets, sorted_pair, h, ws=None):

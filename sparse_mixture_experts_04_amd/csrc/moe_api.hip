@@ -2,6 +2,7 @@
 // of kernel launches.  Declarations and the meaning of every argument are
 // in include/moe.h.
 #include <cmath>
+#include <mutex>
 
 #include "../../include/moe.h"
 #include "ffn_common.h"
@@ -444,3 +445,52 @@ moe_status moe_forward_marked(const moe_desc* desc, const void* x, const moe_wei
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------- no-alloc
+
+// Scratch of moe_dispatch_noalloc: the dispatch's per-segment expert counts
+// (dispatch_segments(s) * E + 1 ints), in an array the library owns instead
+// of a caller workspace.  Each GPU holds its own copy for the life of the
+// process.  Host code never passes this name to a kernel: it takes the
+// device address from hipGetSymbolAddress once per device (scratch_on).
+constexpr size_t kNoAllocScratchInts = size_t(1) << 18;  // 1 MiB
+static __device__ __align__(256) int32_t scratch[kNoAllocScratchInts];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+int32_t* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current and kept; nullptr on a HIP error.
+int32_t* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch_ptr[dev] = static_cast<int32_t*>(p);
+  }
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" moe_status moe_dispatch_noalloc(const moe_desc* desc, const int32_t* topk_idx,
+                                           int32_t* counts, int32_t* offsets,
+                                           int32_t* sorted_pair, int32_t* pair_pos,
+                                           hipStream_t stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  if (!counts || !offsets) return MOE_ERR_NULL;
+  if (s.T > 0 && (!topk_idx || !sorted_pair || !pair_pos)) return MOE_ERR_NULL;
+  const size_t need = static_cast<size_t>(dispatch_segments(s)) * s.E + 1;
+  if (need > kNoAllocScratchInts) return MOE_ERR_UNSUPPORTED;
+  int32_t* seg = scratch_on_current_device();
+  if (!seg) return MOE_ERR_HIP;
+  return hip_status(
+      launch_dispatch(s, topk_idx, counts, offsets, sorted_pair, pair_pos, seg, stream));
+}

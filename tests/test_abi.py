@@ -170,3 +170,18 @@ def test_quantize_argument_checks():
     assert lib.moe_quantize_mxfp4(2, 8, 64, None, P, P, None) == 1
     assert lib.moe_quantize_mxfp4(2, 8, 64, ctypes.c_void_p(0x1004), P, P, None) == 5
     assert lib.moe_quantize_mxfp4(0, 8, 64, None, None, None, None) == 0  # nothing to do
+
+
+def test_dispatch_noalloc_validates_before_launch():
+    """moe_dispatch_noalloc checks its arguments, then that the batch fits its
+    1 MiB scratch (523776 pairs at E=256), before it touches a device."""
+    P = FAKE
+    d = desc(T=1023 * 512 // 6 + 1)                      # 1024 segments of 512 pairs
+    assert lib.moe_dispatch_noalloc(ctypes.byref(d), P, P, P, P, P, None) == 5
+    d64 = desc(T=4095 * 512 // 6 + 1, E=64, S=0)         # 4096 segments at E=64
+    assert lib.moe_dispatch_noalloc(ctypes.byref(d64), P, P, P, P, P, None) == 5
+    ok = desc(T=1000)
+    assert lib.moe_dispatch_noalloc(ctypes.byref(ok), P, None, P, P, P, None) == 1
+    assert lib.moe_dispatch_noalloc(ctypes.byref(ok), None, P, P, P, P, None) == 1
+    assert lib.moe_dispatch_noalloc(None, P, P, P, P, P, None) == 1
+    assert lib.moe_dispatch_noalloc(ctypes.byref(desc(k=8)), P, P, P, P, P, None) == 5
