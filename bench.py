@@ -854,8 +854,8 @@ def main():
         "ms_per_step_hip_graph": round(inp.pop("_graph_ms"), 4),
         "stage_ms": {k: round(v, 4) for k, v in stages.items()},
         "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
-        "roofline": {"kernel": "ffn_big_kernel<gate/up> (grouped gate/up GEMM + SwiGLU, "
-                               "row tiles of up to 256 rows)",
+        "roofline": {"kernel": "ffn_big_kernel<gate/up> (grouped gate/up GEMM + SwiGLU over "
+                               "every routed and shared row)",
                      "bound": "mfma", "achieved": round(gu_tflops, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gu_tflops / PEAK_BF16_TFLOPS, 4),

@@ -27,7 +27,7 @@ namespace moe {
 // exact; see router_select), so every token whose picks or their order
 // could differ from exact arithmetic is redone, and few enough tokens that
 // the refinement is cheap.
-constexpr double kRefineGap = 2e-5;
+constexpr double kRefineGap = 1e-5;
 
 // ---------------------------------------------------------------- planes
 
@@ -378,58 +378,58 @@ __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
 }
 
 // K + 1 rounds of a wave-wide argmax over the candidates the lanes hold:
-// lane l holds Q of them (expert ids id[q], -1 for none; keys, affinities
-// s and logits z).  Rank order is descending key, exact ties to the lower
-// id.  Fills, on every lane, the ids, s and z of the K picks and the keys of
-// the K + 1 best (the last one for the margin).
+// candidate j = lane + 64q sits on lane j % 64 (valid[q]; keys, affinities
+// s and logits z).  The candidates are numbered in ascending expert id, so
+// rank order is descending key with exact ties to the lower number.  Fills,
+// on every lane, the numbers, s and z of the K picks and the keys of the
+// K + 1 best (the last one for the margin).
 template <int K, int Q>
-__device__ __forceinline__ void rank_rounds(int lane, const int (&id)[Q], const double (&key)[Q],
-                                            const double (&sv)[Q], const double (&zv)[Q],
-                                            int (&i_sel)[K], double (&s_sel)[K],
-                                            double (&z_sel)[K], double (&k_sel)[K + 1]) {
+__device__ __forceinline__ void rank_rounds(int lane, const bool (&valid)[Q],
+                                            const double (&key)[Q], const double (&sv)[Q],
+                                            const double (&zv)[Q], int (&j_sel)[K],
+                                            double (&s_sel)[K], double (&z_sel)[K],
+                                            double (&k_sel)[K + 1]) {
   bool taken[Q];
 #pragma unroll
-  for (int q = 0; q < Q; ++q) taken[q] = id[q] < 0;
+  for (int q = 0; q < Q; ++q) taken[q] = !valid[q];
 #pragma unroll
   for (int r = 0; r <= K; ++r) {
     double bk = -INFINITY;
-    int bi = 0x7fffffff, bq = -1;
+    int bj = 0x7fffffff;
 #pragma unroll
-    for (int q = 0; q < Q; ++q)
-      if (!taken[q] && better(key[q], id[q], bk, bi)) {
+    for (int q = 0; q < Q; ++q) {
+      const int j = lane + 64 * q;
+      if (!taken[q] && better(key[q], j, bk, bj)) {
         bk = key[q];
-        bi = id[q];
-        bq = q;
+        bj = j;
       }
-    int bl = lane;
+    }
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) {
       const double ok = __shfl_xor(bk, off);
-      const int oi = __shfl_xor(bi, off);
-      const int ol = __shfl_xor(bl, off);
-      const int oq = __shfl_xor(bq, off);
-      if (better(ok, oi, bk, bi)) {
+      const int oj = __shfl_xor(bj, off);
+      if (better(ok, oj, bk, bj)) {
         bk = ok;
-        bi = oi;
-        bl = ol;
-        bq = oq;
+        bj = oj;
       }
     }
     k_sel[r] = bk;
     if (r < K) {
+      const int q = bj >> 6;
+      const int owner = bj & 63;
       double my = sv[0], mz = zv[0];
 #pragma unroll
       for (int qq = 1; qq < Q; ++qq) {
-        my = bq == qq ? sv[qq] : my;
-        mz = bq == qq ? zv[qq] : mz;
+        my = q == qq ? sv[qq] : my;
+        mz = q == qq ? zv[qq] : mz;
       }
-      s_sel[r] = __shfl(my, bl);
-      z_sel[r] = __shfl(mz, bl);
-      if (lane == bl) {
+      s_sel[r] = __shfl(my, owner);
+      z_sel[r] = __shfl(mz, owner);
+      if (lane == owner) {
 #pragma unroll
-        for (int qq = 0; qq < Q; ++qq) taken[qq] = taken[qq] || bq == qq;
+        for (int qq = 0; qq < Q; ++qq) taken[qq] = taken[qq] || q == qq;
       }
-      i_sel[r] = bi;
+      j_sel[r] = bj;
     }
   }
 }
@@ -501,16 +501,15 @@ __device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(
 template <int EPL>
 __device__ __forceinline__ void token_keys(const double* __restrict__ partial, int nks, int T,
                                            int npad, int t, int lane,
-                                           const float* __restrict__ bias, int (&id)[EPL],
-                                           double (&zv)[EPL], double (&sv)[EPL],
-                                           double (&key)[EPL]) {
+                                           const float* __restrict__ bias, double (&zv)[EPL],
+                                           double (&sv)[EPL], double (&key)[EPL]) {
   const size_t kstride = static_cast<size_t>(T) * npad;
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
-    id[q] = lane + 64 * q;
-    zv[q] = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + id[q]);
+    const int e = lane + 64 * q;
+    zv[q] = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + e);
     sv[q] = sigmoid64(zv[q]);
-    key[q] = sv[q] + static_cast<double>(bias[id[q]]);
+    key[q] = sv[q] + static_cast<double>(bias[e]);
   }
 }
 
@@ -531,16 +530,18 @@ __global__ __launch_bounds__(256) void router_select(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together; no block barrier below
 
-  int id[EPL];
   double zv[EPL], sv[EPL], key[EPL];
-  token_keys<EPL>(partial, nks, T, npad, t, lane, bias, id, zv, sv, key);
+  token_keys<EPL>(partial, nks, T, npad, t, lane, bias, zv, sv, key);
   double z_sh = 0.0;
   if (lane < S)
     z_sh = sum_partials(partial, static_cast<size_t>(T) * npad, nks,
                         static_cast<size_t>(t) * npad + E + lane);
-  int i_sel[K];
+  bool valid[EPL];
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) valid[q] = true;
+  int i_sel[K];     // candidate j is expert j here
   double s_pick[K], z_pick[K], k_sel[K + 1];
-  rank_rounds<K, EPL>(lane, id, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
+  rank_rounds<K, EPL>(lane, valid, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
   write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk, gates,
                     margin, logsumexp_norm, gate_scale);
   double gap = INFINITY;
@@ -557,21 +558,23 @@ __global__ __launch_bounds__(256) void router_select(
 // bf16 (or fp32) x and fp32 w are exact in fp64, so z is the dot product to
 // fp64 rounding and the picks are those of exact arithmetic unless two keys
 // agree to ~1e-15.  One workgroup per listed token (a fixed grid walks the
-// list): wave 0 lists the candidates; all 256 threads take 4 consecutive
-// elements of K per 1024, 4 candidates at a time, and the lane and wave sums
-// are added in a fixed order; wave 0 then ranks the candidates and writes
-// the token's outputs.
+// list): wave 0 lists the candidates; all 512 threads take 4 consecutive
+// elements of K per 2048, and the lane, wave and span sums are added in a
+// fixed order; wave 0 then ranks the candidates and writes the token's
+// outputs.
 template <int K, int S, int EPL>
-__global__ __launch_bounds__(256) void router_refine(
+__global__ __launch_bounds__(512) void router_refine(
     const double* __restrict__ partial, int nks, int T, int npad, int E, int d,
     const void* __restrict__ xv, bool x_bf16, const float* __restrict__ w,
     const int32_t* __restrict__ refine, const float* __restrict__ bias,
     int32_t* __restrict__ topk, float* __restrict__ gates, float* __restrict__ margin,
     bool logsumexp_norm, double gate_scale) {
-  constexpr int NB = 4;                   // candidates per pass over K
+  constexpr int NW = 8;                   // waves of the workgroup
+  constexpr int NB = 9;                   // candidates per group of loads (7 + shared, usually)
+  constexpr int CH = 2;                   // 2048-element chunks of K per span
   __shared__ int cand[64 * EPL + S];      // routed candidates, then the shared experts
   __shared__ double zc[64 * EPL + S];     // their exact logits
-  __shared__ double wsum[4][NB];
+  __shared__ double wsum[NW][NB];
   __shared__ int s_nc;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -579,19 +582,22 @@ __global__ __launch_bounds__(256) void router_refine(
   for (int i = blockIdx.x; i < n; i += gridDim.x) {
     const int t = refine[1 + i];
     if (wave == 0) {
-      int id[EPL];
       double zv[EPL], sv[EPL], key[EPL];
-      token_keys<EPL>(partial, nks, T, npad, t, lane, bias, id, zv, sv, key);
+      token_keys<EPL>(partial, nks, T, npad, t, lane, bias, zv, sv, key);
+      bool valid[EPL];
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) valid[q] = true;
       int i_sel[K];
       double s_pick[K], z_pick[K], k_sel[K + 1];
-      rank_rounds<K, EPL>(lane, id, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
+      rank_rounds<K, EPL>(lane, valid, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
       const double thresh = k_sel[K] - kRefineGap;
+      // candidates listed in ascending expert id (q outer, lane inner)
       int base = 0;
 #pragma unroll
       for (int q = 0; q < EPL; ++q) {
         const bool c = key[q] >= thresh;
         const unsigned long long m = __ballot(c);
-        if (c) cand[base + __popcll(m & ((1ull << lane) - 1ull))] = id[q];
+        if (c) cand[base + __popcll(m & ((1ull << lane) - 1ull))] = lane + 64 * q;
         base += __popcll(m);
       }
       if (lane < S) cand[base + lane] = E + lane;
@@ -600,71 +606,90 @@ __global__ __launch_bounds__(256) void router_refine(
     __syncthreads();
     const int nc = s_nc;
     const int ntot = nc + S;
-    for (int b0 = 0; b0 < ntot; b0 += NB) {
-      double acc[NB];
+    // K in spans of 512 threads x 4 elements x CH chunks; each group of NB
+    // candidates issues all of its loads for the span before any addition,
+    // so a token costs about one round trip per span and group
+    for (int span = 0; span < d; span += 2048 * CH) {
+      double xs[CH][4];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) acc[j] = 0.0;
-      for (int c = tid * 4; c < d; c += 1024) {
-        double xs[4];
-        if (x_bf16) {
-          const bf16_t* x = static_cast<const bf16_t*>(xv) + static_cast<size_t>(t) * d + c;
-          const uint2 v = *reinterpret_cast<const uint2*>(x);
-          xs[0] = bf16_to_f32(static_cast<bf16_t>(v.x & 0xffff));
-          xs[1] = bf16_to_f32(static_cast<bf16_t>(v.x >> 16));
-          xs[2] = bf16_to_f32(static_cast<bf16_t>(v.y & 0xffff));
-          xs[3] = bf16_to_f32(static_cast<bf16_t>(v.y >> 16));
-        } else {
-          const float4 v = *reinterpret_cast<const float4*>(
-              static_cast<const float*>(xv) + static_cast<size_t>(t) * d + c);
-          xs[0] = v.x;
-          xs[1] = v.y;
-          xs[2] = v.z;
-          xs[3] = v.w;
-        }
-        float4 wv[NB];
+      for (int h = 0; h < CH; ++h) {
+        const int c = span + h * 2048 + tid * 4;
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
-          if (b0 + j < ntot)
-            wv[j] = *reinterpret_cast<const float4*>(w + static_cast<size_t>(cand[b0 + j]) * d + c);
-#pragma unroll
-        for (int j = 0; j < NB; ++j)
-          if (b0 + j < ntot) {
-            acc[j] = fma(xs[0], static_cast<double>(wv[j].x), acc[j]);
-            acc[j] = fma(xs[1], static_cast<double>(wv[j].y), acc[j]);
-            acc[j] = fma(xs[2], static_cast<double>(wv[j].z), acc[j]);
-            acc[j] = fma(xs[3], static_cast<double>(wv[j].w), acc[j]);
+        for (int e = 0; e < 4; ++e) xs[h][e] = 0.0;
+        if (c < d) {
+          if (x_bf16) {
+            const uint2 v = *reinterpret_cast<const uint2*>(static_cast<const bf16_t*>(xv) +
+                                                            static_cast<size_t>(t) * d + c);
+            xs[h][0] = bf16_to_f32(static_cast<bf16_t>(v.x & 0xffff));
+            xs[h][1] = bf16_to_f32(static_cast<bf16_t>(v.x >> 16));
+            xs[h][2] = bf16_to_f32(static_cast<bf16_t>(v.y & 0xffff));
+            xs[h][3] = bf16_to_f32(static_cast<bf16_t>(v.y >> 16));
+          } else {
+            const float4 v = *reinterpret_cast<const float4*>(
+                static_cast<const float*>(xv) + static_cast<size_t>(t) * d + c);
+            xs[h][0] = v.x;
+            xs[h][1] = v.y;
+            xs[h][2] = v.z;
+            xs[h][3] = v.w;
           }
+        }
       }
+      for (int b0 = 0; b0 < ntot; b0 += NB) {
+        float4 wv[NB][CH];
 #pragma unroll
-      for (int j = 0; j < NB; ++j) {
+        for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc[j] += __shfl_xor(acc[j], off);
+          for (int h = 0; h < CH; ++h) {
+            const int c = span + h * 2048 + tid * 4;
+            wv[j][h] = (b0 + j < ntot && c < d)
+                           ? *reinterpret_cast<const float4*>(
+                                 w + static_cast<size_t>(cand[b0 + j]) * d + c)
+                           : make_float4(0.f, 0.f, 0.f, 0.f);
+          }
+#pragma unroll
+        for (int j = 0; j < NB; ++j) {
+          double acc = 0.0;
+#pragma unroll
+          for (int h = 0; h < CH; ++h) {
+            acc = fma(xs[h][0], static_cast<double>(wv[j][h].x), acc);
+            acc = fma(xs[h][1], static_cast<double>(wv[j][h].y), acc);
+            acc = fma(xs[h][2], static_cast<double>(wv[j][h].z), acc);
+            acc = fma(xs[h][3], static_cast<double>(wv[j][h].w), acc);
+          }
+#pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+          if (lane == 0) wsum[wave][j] = acc;
+        }
+        __syncthreads();
+        // the group's sums in a fixed order: waves 0..NW-1, then onto the
+        // running logit (spans in order)
+        if (tid < NB && b0 + tid < ntot) {
+          double v = wsum[0][tid];
+#pragma unroll
+          for (int q = 1; q < NW; ++q) v += wsum[q][tid];
+          zc[b0 + tid] = span == 0 ? v : zc[b0 + tid] + v;
+        }
+        __syncthreads();
       }
-      if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < NB; ++j) wsum[wave][j] = acc[j];
-      }
-      __syncthreads();
-      if (tid < NB && b0 + tid < ntot)
-        zc[b0 + tid] = ((wsum[0][tid] + wsum[1][tid]) + wsum[2][tid]) + wsum[3][tid];
-      __syncthreads();
     }
     if (wave == 0) {
-      // candidate q of lane l is cand[l + 64q] (routed ones only)
-      int id[EPL];
+      // candidate j = lane + 64q is cand[j] (routed ones only, ascending id)
+      bool valid[EPL];
       double zv[EPL], sv[EPL], key[EPL];
 #pragma unroll
       for (int q = 0; q < EPL; ++q) {
         const int j = lane + 64 * q;
-        id[q] = j < nc ? cand[j] : -1;
-        zv[q] = j < nc ? zc[j] : 0.0;
+        valid[q] = j < nc;
+        zv[q] = valid[q] ? zc[j] : 0.0;
         sv[q] = sigmoid64(zv[q]);
-        key[q] = j < nc ? sv[q] + static_cast<double>(bias[id[q]]) : -INFINITY;
+        key[q] = valid[q] ? sv[q] + static_cast<double>(bias[cand[j]]) : -INFINITY;
       }
       const double z_sh = lane < S ? zc[nc + lane] : 0.0;
-      int i_sel[K];
+      int j_sel[K], i_sel[K];
       double s_pick[K], z_pick[K], k_sel[K + 1];
-      rank_rounds<K, EPL>(lane, id, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
+      rank_rounds<K, EPL>(lane, valid, key, sv, zv, j_sel, s_pick, z_pick, k_sel);
+#pragma unroll
+      for (int r = 0; r < K; ++r) i_sel[r] = cand[j_sel[r]];
       write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk,
                         gates, margin, logsumexp_norm, gate_scale);
     }
@@ -705,7 +730,7 @@ static void launch_select(const Shape& s, const SelectArgs& a, hipStream_t st) {
   router_select<6, S, EPL><<<(s.T + 3) / 4, 256, 0, st>>>(
       a.partial, a.nks, s.T, a.npad, s.E, a.bias, a.topk_idx, a.gates, a.margin,
       s.gate_logsumexp, s.gate_scale, a.refine);
-  router_refine<6, S, EPL><<<kRefineGrid, 256, 0, st>>>(
+  router_refine<6, S, EPL><<<s.T < kRefineGrid ? s.T : kRefineGrid, 512, 0, st>>>(
       a.partial, a.nks, s.T, a.npad, s.E, s.d, a.x, s.bf16, a.w_router, a.refine, a.bias,
       a.topk_idx, a.gates, a.margin, s.gate_logsumexp, s.gate_scale);
 }
