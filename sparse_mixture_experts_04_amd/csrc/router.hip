@@ -355,24 +355,6 @@ __global__ __launch_bounds__(256) void router_logits_bf16(
 
 // ------------------------------------------------------------- selection
 
-// z = sum of the K-split partial logits in split order.  The loads of a
-// group of 8 splits are issued together (small batches split K up to 28
-// ways); the additions stay in split order.
-__device__ __forceinline__ double sum_partials(const double* __restrict__ partial, size_t kstride,
-                                               int nks, size_t off) {
-  double z = 0.0;
-  int ks = 0;
-  for (; ks + 8 <= nks; ks += 8) {
-    double v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) v[j] = partial[(ks + j) * kstride + off];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) z += v[j];
-  }
-  for (; ks < nks; ++ks) z += partial[ks * kstride + off];
-  return z;
-}
-
 __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
@@ -498,16 +480,45 @@ __device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(
 
 // Keys of token t from the matrix-core logits (sum of the K-split partials):
 // lane l holds routed experts l + 64q.
-template <int EPL>
+// z_sh: shared expert E + lane's logit on lanes < S (0 elsewhere).  The
+// partials of a group of 4 splits are loaded for all of the lane's experts
+// before any is added (at T=64 K is split 28 ways, and a load at a time
+// per expert would cost a round trip each); each logit still adds its
+// splits in split order.
+template <int EPL, int S>
 __device__ __forceinline__ void token_keys(const double* __restrict__ partial, int nks, int T,
-                                           int npad, int t, int lane,
+                                           int npad, int E, int t, int lane,
                                            const float* __restrict__ bias, double (&zv)[EPL],
-                                           double (&sv)[EPL], double (&key)[EPL]) {
+                                           double (&sv)[EPL], double (&key)[EPL],
+                                           double& z_sh) {
   const size_t kstride = static_cast<size_t>(T) * npad;
+  const double* row = partial + static_cast<size_t>(t) * npad;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) zv[q] = 0.0;
+  z_sh = 0.0;
+  for (int ks = 0; ks < nks; ks += 4) {
+    double v[4][EPL], vs[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ks + j < nks) {
+        const double* r = row + static_cast<size_t>(ks + j) * kstride;
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) v[j][q] = r[lane + 64 * q];
+        vs[j] = lane < S ? r[E + lane] : 0.0;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (ks + j < nks) {
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) zv[q] += v[j][q];
+        z_sh += vs[j];
+      }
+    }
+  }
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     const int e = lane + 64 * q;
-    zv[q] = sum_partials(partial, kstride, nks, static_cast<size_t>(t) * npad + e);
     sv[q] = sigmoid64(zv[q]);
     key[q] = sv[q] + static_cast<double>(bias[e]);
   }
@@ -530,12 +541,8 @@ __global__ __launch_bounds__(256) void router_select(
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;  // whole wave leaves together; no block barrier below
 
-  double zv[EPL], sv[EPL], key[EPL];
-  token_keys<EPL>(partial, nks, T, npad, t, lane, bias, zv, sv, key);
-  double z_sh = 0.0;
-  if (lane < S)
-    z_sh = sum_partials(partial, static_cast<size_t>(T) * npad, nks,
-                        static_cast<size_t>(t) * npad + E + lane);
+  double zv[EPL], sv[EPL], key[EPL], z_sh;
+  token_keys<EPL, S>(partial, nks, T, npad, E, t, lane, bias, zv, sv, key, z_sh);
   bool valid[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) valid[q] = true;
@@ -582,8 +589,8 @@ __global__ __launch_bounds__(512) void router_refine(
   for (int i = blockIdx.x; i < n; i += gridDim.x) {
     const int t = refine[1 + i];
     if (wave == 0) {
-      double zv[EPL], sv[EPL], key[EPL];
-      token_keys<EPL>(partial, nks, T, npad, t, lane, bias, zv, sv, key);
+      double zv[EPL], sv[EPL], key[EPL], z_unused;
+      token_keys<EPL, S>(partial, nks, T, npad, E, t, lane, bias, zv, sv, key, z_unused);
       bool valid[EPL];
 #pragma unroll
       for (int q = 0; q < EPL; ++q) valid[q] = true;
