@@ -359,6 +359,86 @@ __device__ __forceinline__ bool better(double ka, int ia, double kb, int ib) {
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// Lane exchanges of the wave reductions: step STEP returns the value of
+// lane l's partner.  Within a row of 16 lanes by DPP (xor 1, xor 2, then
+// each 4-lane group against the other half of its 8 lanes, each 8-lane
+// group against the other half of its row: lane i <-> 7 - i and 15 - i);
+// across rows by the gfx950 permlane swaps (l <-> l ^ 16, l <-> l ^ 32).
+// Every pairing is an involution, so after the six steps every lane holds
+// the reduction of all 64 (an associative and commutative one, or a sum
+// whose order is the same on every lane).  No exchange goes through LDS.
+template <int STEP>
+__device__ __forceinline__ int lane_xchg(int v, int lane) {
+  if constexpr (STEP == 0) {
+    return __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  } else if constexpr (STEP == 1) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  } else if constexpr (STEP == 2) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  } else if constexpr (STEP == 3) {
+    return __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false);  // row_mirror
+  } else if constexpr (STEP == 4) {
+    // odd rows of the first result hold the even rows' values, and the
+    // even rows of the second the odd rows'
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? static_cast<int>(r[0]) : static_cast<int>(r[1]);
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? static_cast<int>(r[0]) : static_cast<int>(r[1]);
+  }
+}
+
+template <int STEP>
+__device__ __forceinline__ double lane_xchg64(double v, int lane) {
+  const long long u = __double_as_longlong(v);
+  const int lo = lane_xchg<STEP>(static_cast<int>(u), lane);
+  const int hi = lane_xchg<STEP>(static_cast<int>(u >> 32), lane);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
+template <int STEP>
+__device__ __forceinline__ void argmax_step(double& bk, int& bj, int lane) {
+  const double ok = lane_xchg64<STEP>(bk, lane);
+  const int oj = lane_xchg<STEP>(bj, lane);
+  if (better(ok, oj, bk, bj)) {
+    bk = ok;
+    bj = oj;
+  }
+}
+
+// (bk, bj) := the best pair over the wave (descending key, lower number on
+// an exact tie: a total order, so the result does not depend on the order
+// of the steps), on every lane.
+__device__ __forceinline__ void wave_argmax(double& bk, int& bj, int lane) {
+  argmax_step<0>(bk, bj, lane);
+  argmax_step<1>(bk, bj, lane);
+  argmax_step<2>(bk, bj, lane);
+  argmax_step<3>(bk, bj, lane);
+  argmax_step<4>(bk, bj, lane);
+  argmax_step<5>(bk, bj, lane);
+}
+
+// Sum over the wave in a fixed order (the same on every lane).
+__device__ __forceinline__ double wave_sum(double v, int lane) {
+  v += lane_xchg64<0>(v, lane);
+  v += lane_xchg64<1>(v, lane);
+  v += lane_xchg64<2>(v, lane);
+  v += lane_xchg64<3>(v, lane);
+  v += lane_xchg64<4>(v, lane);
+  v += lane_xchg64<5>(v, lane);
+  return v;
+}
+
+// Value of a double on a wave-uniform lane.
+__device__ __forceinline__ double read_lane64(double v, int src) {
+  const long long u = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane(static_cast<int>(u), src);
+  const int hi = __builtin_amdgcn_readlane(static_cast<int>(u >> 32), src);
+  return __longlong_as_double((static_cast<long long>(hi) << 32) |
+                              static_cast<unsigned int>(lo));
+}
+
 // K + 1 rounds of a wave-wide argmax over the candidates the lanes hold:
 // candidate j = lane + 64q sits on lane j % 64 (valid[q]; keys, affinities
 // s and logits z).  The candidates are numbered in ascending expert id, so
@@ -386,15 +466,8 @@ __device__ __forceinline__ void rank_rounds(int lane, const bool (&valid)[Q],
         bj = j;
       }
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ok = __shfl_xor(bk, off);
-      const int oj = __shfl_xor(bj, off);
-      if (better(ok, oj, bk, bj)) {
-        bk = ok;
-        bj = oj;
-      }
-    }
+    wave_argmax(bk, bj, lane);
+    bj = __builtin_amdgcn_readfirstlane(bj);  // the same on every lane
     k_sel[r] = bk;
     if (r < K) {
       const int q = bj >> 6;
@@ -405,8 +478,8 @@ __device__ __forceinline__ void rank_rounds(int lane, const bool (&valid)[Q],
         my = q == qq ? sv[qq] : my;
         mz = q == qq ? zv[qq] : mz;
       }
-      s_sel[r] = __shfl(my, owner);
-      z_sel[r] = __shfl(mz, owner);
+      s_sel[r] = read_lane64(my, owner);
+      z_sel[r] = read_lane64(mz, owner);
       if (lane == owner) {
 #pragma unroll
         for (int qq = 0; qq < Q; ++qq) taken[qq] = taken[qq] || q == qq;
@@ -437,8 +510,8 @@ __device__ __forceinline__ void write_token(int t, int lane, const int (&i_sel)[
   }
 #pragma unroll
   for (int j = 0; j < S; ++j) {
-    s_sel[K + j] = __shfl(s_sh, j);
-    z_sel[K + j] = __shfl(z_sh, j);
+    s_sel[K + j] = read_lane64(s_sh, j);
+    z_sel[K + j] = read_lane64(z_sh, j);
   }
   double denom = 0.0;
   if (logsumexp_norm) {
@@ -663,8 +736,7 @@ __global__ __launch_bounds__(512) void router_refine(
             acc = fma(xs[h][2], static_cast<double>(wv[j][h].z), acc);
             acc = fma(xs[h][3], static_cast<double>(wv[j][h].w), acc);
           }
-#pragma unroll
-          for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+          acc = wave_sum(acc, lane);
           if (lane == 0) wsum[wave][j] = acc;
         }
         __syncthreads();
