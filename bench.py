@@ -89,6 +89,10 @@ def setup(cfg, torch, L, synth):
         inp.update({"fp4_" + k: v for k, v in q.items()})   # keep them alive
     else:
         w = L.weights_from(inp)
+    # the router's bf16 planes of w_router, prepared once per weights like
+    # the quantization (moe_router_prepare), outside the timed region
+    inp["_router_planes"] = L.router_planes(desc, inp["w_router"])
+    w = L.with_router_planes(w, inp["_router_planes"])
     y = torch.empty((cfg.T, cfg.d), dtype=synth.act_dtype(cfg), device="cuda")
     counts = torch.empty(cfg.E, dtype=torch.int32, device="cuda")
     ws = L.alloc_workspace(desc, L.CALL_FORWARD, "cuda")

@@ -94,7 +94,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -158,7 +158,11 @@ typedef struct {
  * With weight == MOE_MXFP4 the routed matrices are the outputs of
  * moe_quantize_mxfp4: w_gate, w_up [E, F, d/2] and w_down [E, d, F/2]
  * bytes of packed FP4 codes, and sc_gate, sc_up [E, d/32, F], sc_down
- * [E, F/32, d] their scale bytes (NULL otherwise). */
+ * [E, F/32, d] their scale bytes (NULL otherwise).
+ * w_router_planes (optional, may be NULL): the output of moe_router_prepare
+ * for this w_router; moe_forward then routes with it instead of splitting
+ * w_router again on every call.  It must be refreshed whenever w_router
+ * changes. */
 typedef struct {
   const float* w_router;
   const void* w_gate;
@@ -170,6 +174,7 @@ typedef struct {
   const uint8_t* sc_gate;
   const uint8_t* sc_up;
   const uint8_t* sc_down;
+  const uint16_t* w_router_planes;
 } moe_weights;
 
 /* Optional routing outputs of moe_forward: each pointer may be NULL, in
@@ -207,6 +212,21 @@ moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router
                       const float* bias, int32_t* topk_idx, float* gates,
                       float* margin_or_null, void* ws, size_t ws_bytes,
                       hipStream_t stream);
+
+/* The router's split of w_router into bf16 planes, once per weights
+ * ("Inkling, Dissected" 02b: the router scores every token against each
+ * expert's vector; the vectors change only when the weights do).
+ *   planes [3, P, d] bf16 bits, P = E+S rounded up to a multiple of 64:
+ *   plane 0 = bf16(w), plane 1 = bf16(w - plane 0), plane 2 = bf16(w -
+ *   plane 0 - plane 1), rounding to nearest even: the exact split that
+ *   moe_router makes on every call; rows E+S.. are zero.
+ * moe_router_planes_size gives the bytes of planes for a shape (the same
+ * validation errors as moe_router; T may be 0).  moe_router_prepare writes
+ * them on `stream` from w_router [E+S, d] fp32; the caller owns planes and
+ * passes it as moe_weights.w_router_planes.  It needs no workspace. */
+moe_status moe_router_planes_size(const moe_desc* desc, size_t* bytes);
+moe_status moe_router_prepare(const moe_desc* desc, const float* w_router, uint16_t* planes,
+                              hipStream_t stream);
 
 /* Dispatch: group the T*k (token, slot) pairs by expert ("Inkling,
  * Dissected" 02: each token visits its 6 chosen experts; 02e: L_e is the

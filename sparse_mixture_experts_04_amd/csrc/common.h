@@ -66,10 +66,16 @@ inline int dispatch_segments(const Shape& s) {
 int ffn_row_tile(const Shape& s);
 
 // ---- launchers (return hipSuccess or the launch error) -------------------
-// refine: T + 1 ints of workspace (the tokens the exact pass redoes).
+// The three bf16 planes of w_router ([3, router_cols_padded(s), d]).
+hipError_t launch_router_planes(const Shape& s, const float* w_router, bf16_t* planes,
+                                hipStream_t st);
+
+// prepared: planes from launch_router_planes, or null to split w_router
+// into wplanes (workspace) first.  refine: T + 1 ints of workspace (the
+// tokens the exact pass redoes).
 hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
-                         const float* bias, int32_t* topk_idx, float* gates,
-                         float* margin, bf16_t* wplanes, double* partial,
+                         const bf16_t* prepared, const float* bias, int32_t* topk_idx,
+                         float* gates, float* margin, bf16_t* wplanes, double* partial,
                          int32_t* refine, hipStream_t st);
 
 hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* counts,

@@ -208,8 +208,25 @@ moe_status moe_router(const moe_desc* desc, const void* x, const float* w_router
   if ((st = check_ws(s, MOE_CALL_ROUTER, ws, ws_bytes)) != MOE_OK) return st;
   Carver c{static_cast<char*>(ws)};
   const RouterWs r = carve_router(c, s);
-  return hip_status(launch_router(s, x, w_router, bias, topk_idx, gates, margin_or_null,
-                                  r.planes, r.partial, r.refine, stream));
+  return hip_status(launch_router(s, x, w_router, nullptr, bias, topk_idx, gates,
+                                  margin_or_null, r.planes, r.partial, r.refine, stream));
+}
+
+moe_status moe_router_planes_size(const moe_desc* desc, size_t* bytes) {
+  if (!bytes) return MOE_ERR_NULL;
+  const moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  const Shape s = to_shape(desc);
+  *bytes = 3 * static_cast<size_t>(router_cols_padded(s)) * s.d * sizeof(bf16_t);
+  return MOE_OK;
+}
+
+moe_status moe_router_prepare(const moe_desc* desc, const float* w_router, uint16_t* planes,
+                              hipStream_t stream) {
+  const moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (!w_router || !planes) return MOE_ERR_NULL;
+  return hip_status(launch_router_planes(to_shape(desc), w_router, planes, stream));
 }
 
 moe_status moe_dispatch(const moe_desc* desc, const int32_t* topk_idx, int32_t* counts,
@@ -404,8 +421,9 @@ moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* 
     return (e == hipSuccess && marks) ? hipEventRecord(marks[i], stream) : e;
   };
   const int mt = ffn_row_tile(s);
-  hipError_t e = launch_router(s, x, w->w_router, bias, f.topk, f.gates, margin,
-                               f.router.planes, f.router.partial, f.router.refine, stream);
+  hipError_t e = launch_router(s, x, w->w_router, w->w_router_planes, bias, f.topk, f.gates,
+                               margin, f.router.planes, f.router.partial, f.router.refine,
+                               stream);
   e = mark(0, e);
   if (e == hipSuccess)
     e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg, stream);

@@ -31,11 +31,8 @@ constexpr double kRefineGap = 1e-5;
 
 // ---------------------------------------------------------------- planes
 
-// Also empties the refinement list of this router call (refine[0] = 0).
 __global__ __launch_bounds__(256) void router_split_planes(
-    const float* __restrict__ w, int rows, int d, int rows_pad, bf16_t* __restrict__ planes,
-    int32_t* __restrict__ refine) {
-  if (blockIdx.x == 0 && threadIdx.x == 0) refine[0] = 0;
+    const float* __restrict__ w, int rows, int d, int rows_pad, bf16_t* __restrict__ planes) {
   const size_t n = static_cast<size_t>(rows_pad) * d;
   const size_t stride = static_cast<size_t>(gridDim.x) * blockDim.x;
   for (size_t i = static_cast<size_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n; i += stride) {
@@ -101,7 +98,8 @@ __device__ __forceinline__ void router_load_x(const void* __restrict__ xv, const
 template <int NXP>
 __global__ __launch_bounds__(256) void router_logits(
     const void* __restrict__ xv, const bf16_t* __restrict__ planes, int T, int d, int npad,
-    int nks, int chunk, double* __restrict__ partial) {
+    int nks, int chunk, double* __restrict__ partial, int32_t* __restrict__ refine) {
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) refine[0] = 0;
   constexpr int KS = 32;
   constexpr int LDSW = KS + 8;
   const int steps_per_chunk = chunk / KS;
@@ -233,7 +231,8 @@ constexpr int kRouterStageElems = (128 + 3 * 64) * 32;  // x rows, then 3 planes
 
 __global__ __launch_bounds__(256) void router_logits_bf16(
     const bf16_t* __restrict__ x, const bf16_t* __restrict__ planes, int T, int d, int npad,
-    int nks, int chunk, double* __restrict__ partial) {
+    int nks, int chunk, double* __restrict__ partial, int32_t* __restrict__ refine) {
+  if ((blockIdx.x | blockIdx.y | blockIdx.z | threadIdx.x) == 0) refine[0] = 0;
   constexpr int KS = 32;
   constexpr int RS = kRouterRing;
   constexpr int SE = kRouterStageElems;
@@ -821,24 +820,37 @@ static void launch_select_e(const Shape& s, const SelectArgs& a, hipStream_t st)
   else launch_select<S, 4>(s, a, st);
 }
 
-hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
-                         const float* bias, int32_t* topk_idx, float* gates, float* margin,
-                         bf16_t* wplanes, double* partial, int32_t* refine, hipStream_t st) {
-  if (s.T == 0) return hipSuccess;
+hipError_t launch_router_planes(const Shape& s, const float* w_router, bf16_t* planes,
+                                hipStream_t st) {
   const int npad = router_cols_padded(s);
   const size_t n = static_cast<size_t>(npad) * s.d;
   int blocks = static_cast<int>((n + 255) / 256);
   if (blocks > 4096) blocks = 4096;
-  router_split_planes<<<blocks, 256, 0, st>>>(w_router, s.E + s.S, s.d, npad, wplanes,
-                                              refine);
+  router_split_planes<<<blocks, 256, 0, st>>>(w_router, s.E + s.S, s.d, npad, planes);
+  return hipGetLastError();
+}
+
+hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
+                         const bf16_t* prepared, const float* bias, int32_t* topk_idx,
+                         float* gates, float* margin, bf16_t* wplanes, double* partial,
+                         int32_t* refine, hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  const int npad = router_cols_padded(s);
+  if (prepared) {
+    wplanes = const_cast<bf16_t*>(prepared);  // only read from here on
+  } else {
+    const hipError_t e = launch_router_planes(s, w_router, wplanes, st);
+    if (e != hipSuccess) return e;
+  }
   const int nks = router_ksplits(s);
   const int chunk = router_chunk(s);
   dim3 grid((s.T + 127) / 128, npad / kRouterColTile, nks);
   if (s.bf16)
     router_logits_bf16<<<grid, 256, 0, st>>>(static_cast<const bf16_t*>(x), wplanes, s.T, s.d,
-                                              npad, nks, chunk, partial);
+                                              npad, nks, chunk, partial, refine);
   else
-    router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, chunk, partial);
+    router_logits<3><<<grid, 256, 0, st>>>(x, wplanes, s.T, s.d, npad, nks, chunk, partial,
+                                           refine);
   const SelectArgs a{x, w_router, partial, nks, npad, bias, topk_idx, gates, margin, refine};
   if (s.S == 0) launch_select_e<0>(s, a, st);
   else if (s.S == 1) launch_select_e<1>(s, a, st);

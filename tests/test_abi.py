@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lib.moe_abi_version() == 2
+    assert lib.moe_abi_version() == L.ABI_VERSION == 3
     for code in range(7):
         s = lib.moe_status_string(code)
         assert s and isinstance(s, bytes)
@@ -185,3 +185,24 @@ def test_dispatch_noalloc_validates_before_launch():
     assert lib.moe_dispatch_noalloc(ctypes.byref(ok), None, P, P, P, P, None) == 1
     assert lib.moe_dispatch_noalloc(None, P, P, P, P, P, None) == 1
     assert lib.moe_dispatch_noalloc(ctypes.byref(desc(k=8)), P, P, P, P, P, None) == 5
+
+
+def test_router_prepare_validates_before_launch():
+    d = desc(d=7168, F=2048, act=L.BF16, weight=L.BF16)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_router_planes_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    # three bf16 planes of the 258 router rows padded to 320
+    assert n.value == 3 * 320 * 7168 * 2
+    assert lib.moe_router_planes_size(ctypes.byref(d), None) == 1
+    assert lib.moe_router_planes_size(None, ctypes.byref(n)) == 1
+    e64 = desc(E=64, S=0)
+    assert lib.moe_router_planes_size(ctypes.byref(e64), ctypes.byref(n)) == 0
+    assert n.value == 3 * 64 * 512 * 4 // 2
+    P = FAKE
+    assert lib.moe_router_prepare(ctypes.byref(d), None, P, None) == 1
+    assert lib.moe_router_prepare(ctypes.byref(d), P, None, None) == 1
+    assert lib.moe_router_prepare(ctypes.byref(desc(E=100)), P, P, None) == 5
+    assert lib.moe_router_prepare(ctypes.byref(desc(d=-1)), P, P, None) == 2
+    # the binding's Weights carries the prepared planes as its last field
+    assert L.Weights._fields_[-1][0] == "w_router_planes"
+    assert ctypes.sizeof(L.Weights) == 11 * ctypes.sizeof(ctypes.c_void_p)
