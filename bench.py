@@ -63,6 +63,7 @@ def parse():
     ap.add_argument("--prefill-workload", default="B")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-ep-share", action="store_true")
+    ap.add_argument("--no-library-gemm", action="store_true")
     ap.add_argument("--lab-workload", default="Lab")
     ap.add_argument("--no-lab", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -520,6 +521,51 @@ def ep_share(cfg, inp, w, torch, L, synth, steps):
             "mfma_frac": round(flops / (ms / 1e3) / 1e12 / PEAK_BF16_TFLOPS, 4)}
 
 
+def library_gemm(cfg, torch, reps=5):
+    """Reference point for the gate/up GEMM's roofline fraction: the vendor
+    library (hipBLASLt through torch.matmul / torch.bmm, bf16) on plain GEMMs
+    of the same FLOPs on this GPU, random operands, not part of the layer.
+    dense: all T*(k+S) rows against one [d, 2F] weight; batched: the routed
+    rows split evenly over the E experts (T*k/E each, no gather, every tile
+    full) against each expert's own [d, 2F] weight."""
+    def timed(fn):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    bf = torch.bfloat16
+    out = {"what": "hipBLASLt (torch.matmul / torch.bmm) bf16 GEMMs of the gate/up GEMM's "
+                   "shape, random operands; context for the roofline fraction"}
+    M, N, K = cfg.T * (cfg.k + cfg.S), 2 * cfg.F, cfg.d
+    a = torch.randn((M, K), generator=g, device="cuda").to(bf)
+    b = torch.randn((K, N), generator=g, device="cuda").to(bf)
+    ms = timed(lambda: torch.matmul(a, b))
+    tf = 2.0 * M * N * K / (ms / 1e3) / 1e12
+    out["dense"] = {"shape": [M, N, K], "ms": round(ms, 4), "tflops": round(tf, 1),
+                    "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del a, b
+    rows = cfg.T * cfg.k // cfg.E
+    a = torch.randn((cfg.E, rows, K), generator=g, device="cuda").to(bf)
+    w = torch.randn((cfg.E, K, N), generator=g, device="cuda").to(bf)   # contiguous operand
+    ms = timed(lambda: torch.bmm(a, w))
+    tf = 2.0 * cfg.E * rows * N * K / (ms / 1e3) / 1e12
+    out["batched_uniform"] = {"experts": cfg.E, "rows_each": rows, "shape": [rows, N, K],
+                              "ms": round(ms, 4), "tflops": round(tf, 1),
+                              "mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+    del a, w
+    torch.cuda.empty_cache()
+    return out
+
+
 def decode_bytes(cfg, counts):
     n_active = int((counts > 0).sum())
     esz = 2 if cfg.act == "bf16" else 4
@@ -876,6 +922,8 @@ def main():
     if not args.no_ep_share:
         section(result, "ep_share",
                 lambda: ep_share(cfg, inp, w, torch, L, synth, max(3, min(args.steps, 10))))
+    if not args.no_library_gemm:
+        section(result, "library_gemm", lambda: library_gemm(cfg, torch))
     if not args.no_decode:
         section(result, "decode", lambda: decode(configs.get(args.decode_workload), args,
                                                  torch, L, synth))

@@ -90,17 +90,33 @@ hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile
 // scg, scu, scd: scales of the routed weights when they are FP4 (s.w_fp4),
 // else unused.
 // part: shared_partial_floats(s) floats of workspace (null when 0).
+// fold_gates (large-batch tiles only, else null): gates [T, k+S]; each
+// shared expert's row of h is scaled by its token's gate for that expert,
+// for launch_shared_combine.
 hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const void* wu,
                           const void* wsg, const void* wsu, const uint8_t* scg,
                           const uint8_t* scu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start,
                           int row_tile, void* h, float* part, hipEvent_t* marks,
-                          hipStream_t st);
+                          hipStream_t st, const float* fold_gates = nullptr);
 
+// routed_only (large-batch tiles only): the routed experts' tiles alone; the
+// shared experts' down GEMM is left to launch_shared_combine.
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
                        const void* h, void* y_routed, void* y_shared, float* part,
-                       hipEvent_t* marks, hipStream_t st);
+                       hipEvent_t* marks, hipStream_t st, bool routed_only = false);
+
+// The shared experts' down GEMM over their gate-scaled rows of h (from
+// launch_gate_up with fold_gates), fused with the combine: writes
+// y = sum of the routed contributions (y_routed through pair_pos, in slot
+// order) plus the shared experts' gate-weighted outputs.  Large-batch tiles
+// (row_tile 128 or 256) and S > 0 only; tile_start is the tile plan whose
+// fused-combine work counters it uses.
+hipError_t launch_shared_combine(const Shape& s, const void* wsd, const int32_t* tile_start,
+                                 int row_tile, const void* h, const void* y_routed,
+                                 const float* gates, const int32_t* pair_pos, void* y,
+                                 hipStream_t st);
 
 // fp32 floats of the K-slice partials the shared experts need with FP4
 // routed weights (0 otherwise); the gate/up and down launches share them.

@@ -603,9 +603,11 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
                           const void* wsg, const void* wsu, const uint8_t* scg,
                           const uint8_t* scu, const int32_t* offsets,
                           const int32_t* sorted_pair, const int32_t* tile_start, int row_tile,
-                          void* h, float* part, hipEvent_t* marks, hipStream_t st) {
+                          void* h, float* part, hipEvent_t* marks, hipStream_t st,
+                          const float* fold_gates) {
   if (s.T == 0) return record_marks(marks, st);
   FfnArgs a{};
+  a.gates = fold_gates;
   a.sc0 = scg;
   a.sc1 = scu;
   a.a = x;
@@ -629,6 +631,7 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
   if (s.bf16) {
     a.n_tiles = s.F / 128;
     if (row_tile != 32) return launch_big(a, true, row_tile, tile_start, kCtrGateUp, marks, st);
+    if (fold_gates) return hipErrorInvalidValue;  // the fused combine is large-batch only
     int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1;
     a.counters = ctr + kCtrGateUp * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {  // routed experts in FP4, then the bf16 shared experts
@@ -647,7 +650,7 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
                        const void* h, void* y_routed, void* y_shared, float* part,
-                       hipEvent_t* marks, hipStream_t st) {
+                       hipEvent_t* marks, hipStream_t st, bool routed_only) {
   if (s.T == 0) return record_marks(marks, st);
   FfnArgs a{};
   a.sc0 = scd;
@@ -667,7 +670,9 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const ui
   a.ldo = s.d;
   if (s.bf16) {
     a.n_tiles = s.d / 256;
+    a.g_hi = routed_only ? s.E : 0;
     if (row_tile != 32) return launch_big(a, false, row_tile, tile_start, kCtrDown, marks, st);
+    if (routed_only) return hipErrorInvalidValue;  // the fused combine is large-batch only
     int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1;
     a.counters = ctr + kCtrDown * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {
@@ -681,6 +686,33 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const ui
   a.n_tiles = s.d / 64;
   hipError_t e = run_f32<false>(a, st);
   return e == hipSuccess ? record_marks(marks, st) : e;
+}
+
+hipError_t launch_shared_combine(const Shape& s, const void* wsd, const int32_t* tile_start,
+                                 int row_tile, const void* h, const void* y_routed,
+                                 const float* gates, const int32_t* pair_pos, void* y,
+                                 hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (!s.bf16 || s.S == 0 || (row_tile != BigCfgRows && row_tile != MidCfgRows))
+    return hipErrorInvalidValue;
+  FfnArgs a{};
+  a.a = h;
+  a.ws0 = wsd;
+  a.T = s.T;
+  a.E = 0;          // one group: the T token rows of the shared experts
+  a.S = 1;
+  a.k = s.k;
+  a.K = s.S * s.F;  // the shared experts one after the other
+  a.kcat = s.F;
+  a.N = s.d;
+  a.ldo = s.d;
+  a.n_tiles = s.d / 256;
+  a.gates = gates;
+  a.pair_pos = pair_pos;
+  a.y_routed = y_routed;
+  a.y = y;
+  int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1 + kCtrCombine * kXcds;
+  return launch_big_combine(a, row_tile, ctr, st);
 }
 
 }  // namespace moe

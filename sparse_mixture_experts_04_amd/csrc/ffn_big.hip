@@ -102,14 +102,21 @@ __device__ __forceinline__ int src_chunk(int lane, int j) {
 // Wave group 0 loads the weight (B) tiles, group 1 the activation (A)
 // tiles; each wave issues L 1 KiB loads per stage (LPW_B or LPW_A), load
 // j = L * (wave % 4) + q filling LDS rows RPL*j.. of its operand's slot.
-template <class C>
+// KCAT (the fused shared-expert down + combine): K runs over the S shared
+// experts one after the other, and from K offset kcat on a load's source
+// moves on by `jump` elements (to the next expert's h rows or W_down rows).
+template <class C, bool KCAT = false>
 struct BigCtx {
   const bf16_t* src[C::LPW_MAX];  // per-lane source of each load (chunk applied)
+  long long jump = 0;             // wave-uniform (KCAT only)
+  int kcat = 0x7fffffff;
 
   template <int L>
   __device__ __forceinline__ void issue(int k0, bf16_t* slot, int wig) const {
+    long long off = k0;
+    if constexpr (KCAT) off += k0 >= kcat ? jump : 0;
 #pragma unroll
-    for (int q = 0; q < L; ++q) dma16(src[q] + k0, slot + (wig * L + q) * 512);
+    for (int q = 0; q < L; ++q) dma16(src[q] + off, slot + (wig * L + q) * 512);
   }
 };
 
@@ -182,8 +189,8 @@ __device__ __forceinline__ void big_mfma(const BigFrags<C>& f, int nv,
 // operand on its own waves lets the B loads run far ahead without the A
 // waits depending on them.  Past the last K step the loads repeat the last
 // step (L2 hits into slots never read), which keeps the counts uniform.
-template <class C, int U, bool GATED>
-__device__ __forceinline__ void big_pp_step(const BigCtx<C>& t, int kt, int nk,
+template <class C, int U, bool GATED, class Ctx>
+__device__ __forceinline__ void big_pp_step(const Ctx& t, int kt, int nk,
                                             bf16_t* const (&sA)[C::NSA],
                                             bf16_t* const (&sB)[C::NSB], int grp, int wig,
                                             int nv, const int (&off)[C::KK],
@@ -205,8 +212,8 @@ __device__ __forceinline__ void big_pp_step(const BigCtx<C>& t, int kt, int nk,
   lds_barrier();
 }
 
-template <class C, bool GATED>
-__device__ __forceinline__ void big_kloop(const BigCtx<C>& t, int nk,
+template <class C, bool GATED, class Ctx>
+__device__ __forceinline__ void big_kloop(const Ctx& t, int nk,
                                           bf16_t* const (&sA)[C::NSA],
                                           bf16_t* const (&sB)[C::NSB], int wave, int lane,
                                           int nv, f32x16_t (&acc)[C::BM][C::BN]) {
@@ -240,10 +247,95 @@ __device__ __forceinline__ void big_kloop(const BigCtx<C>& t, int nk,
   if (grp == 0) lds_barrier();    // both groups pass the same number of points
 }
 
-// One launch covers every row tile of every group.  `plan` holds the row
-// tiles per group as an exclusive prefix (G+1 entries); `counters` the
-// per-XCD work counters, zero at launch.
-template <class C, bool GATED>
+// Epilogue of the fused shared-expert down + combine ("Inkling, Dissected",
+// 02b: the layer output is the gate-weighted sum of the token's 6 routed
+// and the shared experts' outputs).  The LDS tile holds, for the tile's
+// tokens and 256 output columns, the shared experts' down products of their
+// gate-scaled h rows (their gate-weighted sum, rounded to bf16).  Each thread
+// takes 16-byte chunks (8 columns of one token) and sums in fp32, in a fixed
+// order: the routed slots in rank order by fma of gate and y_routed row (a
+// pair dropped at its expert's capacity, pair_pos < 0, left out), then the
+// shared value; one rounding to bf16 into y.  The loads of kCombineBatch
+// chunks are issued before any sum, so they are in flight together.
+constexpr int kTopK = 6;          // routed experts per token (the descriptor enforces it)
+constexpr int kCombineBatch = 4;  // chunks per thread in flight
+template <class C, int CPR>
+__device__ __forceinline__ void combine_epilogue(const FfnArgs& p, const Item& item,
+                                                 const bf16_t* tile, int col0, int tid) {
+  const bf16_t* yr = static_cast<const bf16_t*>(p.y_routed);
+  bf16_t* yo = static_cast<bf16_t*>(p.y);
+  const int ns = p.K / p.kcat;       // shared experts
+  const int gstride = kTopK + ns;    // gates per token
+  const int n = item.rows * CPR;
+  for (int c0 = tid; c0 < n; c0 += kCombineBatch * C::THREADS) {
+    int pos[kCombineBatch][kTopK];
+    float gw[kCombineBatch][kTopK];
+    uint4 v[kCombineBatch][kTopK];
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int c = c0 + b * C::THREADS;
+      const int t = item.m0 + (c < n ? c / CPR : 0);
+#pragma unroll
+      for (int j = 0; j < kTopK; ++j) {
+        pos[b][j] = c < n ? p.pair_pos[static_cast<size_t>(t) * kTopK + j] : -1;
+        gw[b][j] = p.gates[static_cast<size_t>(t) * gstride + j];
+      }
+    }
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int ch = (c0 + b * C::THREADS) % CPR;
+#pragma unroll
+      for (int j = 0; j < kTopK; ++j)
+        v[b][j] = pos[b][j] >= 0
+                      ? *reinterpret_cast<const uint4*>(
+                            yr + static_cast<size_t>(pos[b][j]) * p.ldo + col0 + ch * 8)
+                      : make_uint4(0u, 0u, 0u, 0u);
+    }
+#pragma unroll
+    for (int b = 0; b < kCombineBatch; ++b) {
+      const int c = c0 + b * C::THREADS;
+      if (c >= n) continue;
+      const int row = c / CPR, ch = c % CPR;
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+#pragma unroll
+      for (int j = 0; j < kTopK; ++j) {
+        if (pos[b][j] < 0) continue;
+        const uint32_t w[4] = {v[b][j].x, v[b][j].y, v[b][j].z, v[b][j].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          acc[2 * e] = fmaf(gw[b][j], __uint_as_float(w[e] << 16), acc[2 * e]);
+          acc[2 * e + 1] = fmaf(gw[b][j], __uint_as_float(w[e] & 0xffff0000u), acc[2 * e + 1]);
+        }
+      }
+      const uint4 sv = *reinterpret_cast<const uint4*>(
+          tile + row * (CPR * 8) + ((ch ^ (row & (CPR - 1))) << 3));
+      const uint32_t sw[4] = {sv.x, sv.y, sv.z, sv.w};
+      uint32_t o[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = acc[2 * e] + __uint_as_float(sw[e] << 16);
+        const float hi = acc[2 * e + 1] + __uint_as_float(sw[e] & 0xffff0000u);
+        o[e] = static_cast<uint32_t>(f32_to_bf16(lo)) |
+               (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+      }
+      *reinterpret_cast<uint4*>(yo + static_cast<size_t>(item.m0 + row) * p.ldo + col0 +
+                                ch * 8) = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+  }
+}
+
+// One launch covers every row tile of every group (of groups 0..g_hi-1).
+// `plan` holds the row tiles per group as an exclusive prefix (G+1
+// entries); `counters` the per-XCD work counters, zero at launch.
+// COMBINE: the fused shared-expert down + combine.  One group of T token
+// rows (p.E = 0, p.S = 1, its tiles computed here, not read from the
+// plan); the K loop covers the shared experts' gate-scaled h rows against
+// their W_down one expert after the other (p.K = S * F, rows p.kcat = F
+// long), and the epilogue adds the routed outputs of each token's pairs
+// (see combine_epilogue) and writes y.
+template <class C, bool GATED, bool COMBINE = false>
 __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_t* plan,
                                                          int32_t* counters) {
   // ring slots of the A and B tiles; after the K loop the same memory
@@ -264,16 +356,25 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int wm = wave >> 2, wn = wave & 3;
   const int G = p.E + p.S;
-  for (int g = tid; g <= G; g += C::THREADS) ts[g] = plan[g];
+  if constexpr (COMBINE) {
+    if (tid == 0) {
+      ts[0] = 0;
+      ts[1] = (p.T + C::MT - 1) / C::MT;
+    }
+  } else {
+    for (int g = tid; g <= G; g += C::THREADS) ts[g] = plan[g];
+  }
   __syncthreads();
 
-  const long long total = static_cast<long long>(ts[G]) * p.n_tiles;
+  const int g_hi = p.g_hi > 0 ? p.g_hi : G;
+  const long long total = static_cast<long long>(ts[g_hi]) * p.n_tiles;
   const int xcd = blockIdx.x % kXcds;
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const size_t kT = static_cast<size_t>(p.k) * p.T;
   const int nk = p.K / C::BK;
-  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+  const int kld = COMBINE ? p.kcat : p.K;  // row length of h and W
+  const size_t wstride = static_cast<size_t>(p.N) * kld;
   // load j of a stage fills LDS rows RPL*j..; lane l lands in row
   // RPL*j + l / CPR (src_chunk gives the chunk it fetches)
   const int lrow = lane / C::CPR;
@@ -289,7 +390,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
                                    : kT + static_cast<size_t>(g - p.E) * p.T;
-    BigCtx<C> t;
+    BigCtx<C, COMBINE> t;
     if (wm == 1) {
 #pragma unroll
       for (int q = 0; q < C::LPW_A; ++q) {
@@ -301,7 +402,11 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
         if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
                                     : static_cast<size_t>(rr);
         else src_row = row_base + rr;
-        t.src[q] = A + src_row * p.K + src_chunk<C>(lane, j);
+        t.src[q] = A + src_row * kld + src_chunk<C>(lane, j);
+      }
+      if (COMBINE) {  // the next shared expert's rows of h
+        t.jump = static_cast<long long>(p.T) * kld - kld;
+        t.kcat = p.kcat;
       }
     } else {
       const int ge = routed ? g : g - p.E;
@@ -321,7 +426,11 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
           base = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0);
           col = item.n * C::NB + R;
         }
-        t.src[q] = base + ge * wstride + static_cast<size_t>(col) * p.K + src_chunk<C>(lane, j);
+        t.src[q] = base + ge * wstride + static_cast<size_t>(col) * kld + src_chunk<C>(lane, j);
+      }
+      if (COMBINE) {  // the next shared expert's W_down
+        t.jump = static_cast<long long>(wstride) - kld;
+        t.kcat = p.kcat;
       }
     }
 
@@ -357,6 +466,13 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
       bf16_t* trow = tile + row * NOUT + 4 * (lane >> 5);
       const int sw = row & (CPR - 1);
       if (GATED) {
+        // with p.gates, a shared expert's row of h (token m0 + row) carries
+        // that token's gate for the expert, for the fused down + combine
+        float gsc = 1.0f;
+        if (p.gates && !routed)
+          gsc = row < item.rows ? p.gates[static_cast<size_t>(item.m0 + row) * (p.k + p.S) +
+                                          p.k + (g - p.E)]
+                                : 0.0f;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           uint32_t w[2];
@@ -367,7 +483,7 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
             for (int e = 0; e < 2; ++e) {
               const float gt = acc[i][0][4 * q + 2 * t2 + e];
               const float up = acc[i][1][4 * q + 2 * t2 + e];
-              v[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+              v[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up * gsc;
             }
             w[t2] = static_cast<uint32_t>(f32_to_bf16(v[0])) |
                     (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
@@ -391,14 +507,18 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
       }
     }
     __syncthreads();
-    bf16_t* out = static_cast<bf16_t*>(routed ? p.out_routed : p.out_shared);
-    const size_t orow0 = routed ? static_cast<size_t>(p.offsets[g]) + item.m0
-                                : static_cast<size_t>(g - p.E) * p.T + item.m0;
     const int col0 = item.n * NOUT;
-    for (int c = tid; c < item.rows * CPR; c += C::THREADS) {
-      const int row = c / CPR, ch = c % CPR;
-      *reinterpret_cast<uint4*>(out + (orow0 + row) * p.ldo + col0 + ch * 8) =
-          *reinterpret_cast<const uint4*>(tile + row * NOUT + ((ch ^ (row & (CPR - 1))) << 3));
+    if constexpr (COMBINE) {
+      combine_epilogue<C, CPR>(p, item, tile, col0, tid);
+    } else {
+      bf16_t* out = static_cast<bf16_t*>(routed ? p.out_routed : p.out_shared);
+      const size_t orow0 = routed ? static_cast<size_t>(p.offsets[g]) + item.m0
+                                  : static_cast<size_t>(g - p.E) * p.T + item.m0;
+      for (int c = tid; c < item.rows * CPR; c += C::THREADS) {
+        const int row = c / CPR, ch = c % CPR;
+        *reinterpret_cast<uint4*>(out + (orow0 + row) * p.ldo + col0 + ch * 8) =
+            *reinterpret_cast<const uint4*>(tile + row * NOUT + ((ch ^ (row & (CPR - 1))) << 3));
+      }
     }
   }
 }
@@ -456,6 +576,20 @@ hipError_t launch_big(const FfnArgs& a, bool gated, int mt, const int32_t* plan,
     else ffn_big_kernel<BigCfg, false><<<grid, BigCfg::THREADS, 0, st>>>(a, plan, ctr);
   }
   if (marks && hipEventRecord(marks[0], st) != hipSuccess) return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_big_combine(const FfnArgs& a, int mt, int32_t* counters, hipStream_t st) {
+  if (a.T == 0) return hipSuccess;
+  if (a.E != 0 || a.S != 1 || a.k != kTopK || a.kcat <= 0 || a.K % a.kcat != 0 ||
+      a.K / a.kcat > 2 || a.n_tiles * 256 != a.N || !a.y || !a.y_routed || !a.gates ||
+      !a.pair_pos || !counters)
+    return hipErrorInvalidValue;
+  const int grid = (device_cus_big() + kXcds - 1) / kXcds * kXcds;
+  if (mt == MidCfg::MT)
+    ffn_big_kernel<MidCfg, false, true><<<grid, MidCfg::THREADS, 0, st>>>(a, nullptr, counters);
+  else
+    ffn_big_kernel<BigCfg, false, true><<<grid, BigCfg::THREADS, 0, st>>>(a, nullptr, counters);
   return hipGetLastError();
 }
 

@@ -87,12 +87,22 @@ struct FfnArgs {
   int ksplit;             // 32-row bf16 kernel, shared groups only: K slices per tile
   float* part;            // ksplit > 1: fp32 partial tiles [ksplit][S*T][n_tiles*256]
   int32_t* counters;      // ffn_bf16_kernel: kXcds work counters, zero at launch
+  int g_hi;               // large-batch kernel: groups 0..g_hi-1 only (0: all E + S)
+  // Fused shared experts + combine (large-batch forward, S > 0):
+  const float* gates;     // gate/up: [T, k+S]; each shared row of h is scaled by its
+                          // token's shared gate (null: no scaling)
+  const int32_t* pair_pos;  // combine launch: [T*k] row of each pair in y_routed, or -1
+  const void* y_routed;   // combine launch: routed expert outputs [T*k, d]
+  void* y;                // combine launch: the layer output [T, d]
+  int kcat;               // combine launch: K of one shared expert (F); the K loop runs
+                          // over the S shared experts' h and W_down one after the other
 };
 
 // Work counters after the last entry of a tile plan (zeroed by the kernel
-// that writes the plan): one set of kXcds for the gate/up GEMM and one for
-// the down GEMM that reuses the plan.
-enum { kCtrGateUp = 0, kCtrDown = 1, kCtrSets = 2 };
+// that writes the plan): one set of kXcds for the gate/up GEMM, one for the
+// down GEMM that reuses the plan and one for the fused shared-expert down +
+// combine launch.
+enum { kCtrGateUp = 0, kCtrDown = 1, kCtrCombine = 2, kCtrSets = 3 };
 
 // Next work item of a persistent workgroup on XCD `xcd`: the next index of
 // that XCD's contiguous chunk of [0, total), or once it is used up the next
@@ -180,6 +190,13 @@ hipError_t launch_tile_plan_big(const Shape& s, const int32_t* offsets, int mt, 
 // (optional) is recorded after the GEMM launch.
 hipError_t launch_big(const FfnArgs& a, bool gated, int mt, const int32_t* plan, int which,
                       hipEvent_t* marks, hipStream_t st);
+// The shared experts' down GEMM fused with the combine: one launch over
+// ceil(T / mt) token tiles x d / 256 column tiles, after the routed down
+// GEMM has written y_routed.  a: E = 0 and S = 1 (one group of T token
+// rows), K = S_shared * F, kcat = F, N = ldo = d, a = h (its shared rows
+// scaled by their gates), ws0 = the shared experts' W_down, y, y_routed,
+// gates, pair_pos.  counters: kXcds work counters, zero at launch.
+hipError_t launch_big_combine(const FfnArgs& a, int mt, int32_t* counters, hipStream_t st);
 // Tile plan of the large-batch GEMM: [row tiles per group, exclusive
 // prefix (G+1) | work counters kCtrSets GEMMs x kXcds].
 inline int big_plan_ints(int G) { return (G + 1) + kCtrSets * kXcds; }

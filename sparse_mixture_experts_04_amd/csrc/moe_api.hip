@@ -391,7 +391,9 @@ namespace {
 
 // moe_forward's launches; marks (7 events, or NULL) are recorded after the
 // router, the dispatch, the tile plan, the gate/up GEMM, the down GEMM, the
-// combine and the bias update.
+// combine and the bias update.  With the fused shared-expert down + combine
+// (large batches with shared experts) the down mark follows the routed
+// experts' down GEMM and the combine mark the fused launch.
 moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
                         float gamma, void* y, const moe_routing* routing, void* ws,
                         size_t ws_bytes, hipEvent_t* marks, hipStream_t stream) {
@@ -430,15 +432,26 @@ moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* 
   e = mark(1, e);
   if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
   e = mark(2, e);
+  // Large batches (256-row tiles) with shared experts: the shared experts'
+  // down GEMM runs after the routed one, fused with the combine (their rows
+  // of h carry their gates), so Y_s never goes through HBM.  With 128-row
+  // tiles (~100 rows per expert) the fused launch has about one tile per CU
+  // and its combine epilogue runs alone, slower than the combine kernel.
+  const bool fused = s.bf16 && s.S > 0 && mt == BigCfgRows;
   if (e == hipSuccess)
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
                        f.offsets, f.sorted_pair, f.plan, mt, f.h, f.part,
-                       marks ? marks + 3 : nullptr, stream);
+                       marks ? marks + 3 : nullptr, stream, fused ? f.gates : nullptr);
   if (e == hipSuccess)
     e = launch_down(s, w->w_down, w->ws_down, w->sc_down, f.offsets, f.plan, mt, f.h, f.y_routed,
-                    f.y_shared, f.part, marks ? marks + 4 : nullptr, stream);
-  if (e == hipSuccess)
-    e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
+                    f.y_shared, f.part, marks ? marks + 4 : nullptr, stream, fused);
+  if (e == hipSuccess) {
+    if (fused)
+      e = launch_shared_combine(s, w->ws_down, f.plan, mt, f.h, f.y_routed, f.gates,
+                                f.pair_pos, y, stream);
+    else
+      e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
+  }
   e = mark(5, e);
   if (e == hipSuccess && gamma != 0.0f) e = launch_bias_update(s, f.counts, gamma, bias, stream);
   e = mark(6, e);

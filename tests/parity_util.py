@@ -88,6 +88,38 @@ def run_forward(desc, inp, gamma, bias=None, weights=None):
     return b, bias
 
 
+def fused_combine(cfg):
+    """Whether moe_forward fuses the shared experts' down GEMM with the
+    combine: bf16 layers with shared experts at >= 160 routed rows per
+    expert (the 256-row tiles).  Its y then rounds differently from the
+    stage calls' y: the shared experts' rows of h carry their gates and their
+    gate-weighted sum is rounded to bf16 once, where the stage calls round
+    each shared expert's output."""
+    return cfg.act == "bf16" and cfg.S > 0 and cfg.T * cfg.k // cfg.E >= 160
+
+
+# Largest relative L2 between two bf16 y's that each sit one final bf16
+# rounding (plus, fused, one rounding of the shared sum) from the same fp32
+# sums: a few 2^-9 roundings of independent sign.
+Y_PATHS_RTOL = 4e-3
+
+
+def check_forward_matches_stages(cfg, b, bias_new, bf, bias_f):
+    """moe_forward against the stage calls on the same inputs: routing tables
+    and bias bit for bit; y bit for bit, or (fused combine) within
+    Y_PATHS_RTOL.  Returns the relative L2 between the two y's."""
+    for n in ("topk", "gates", "counts", "offsets", "sorted_pair", "pair_pos"):
+        assert torch.equal(getattr(b, n), getattr(bf, n)), n
+    assert torch.equal(bias_new, bias_f)
+    if not fused_combine(cfg):
+        assert torch.equal(b.y, bf.y)
+        return 0.0
+    e = rel_l2(np64(bf.y), np64(b.y))
+    log(f"  forward (fused shared down + combine) against the stage calls: y rel L2 {e:.2e}")
+    assert e <= Y_PATHS_RTOL
+    return e
+
+
 def check_routing(x64, wr64, b64, topk_gpu, gates_gpu, k=6, gate_norm="ratio", gate_scale=1.0):
     """Selection bit-exact outside oracle near-ties; gates to 1e-6 relative
     (the oracle's gates for the GPU's selection, in the given normalisation).

@@ -28,6 +28,9 @@ CASES = [
     MoEConfig("graph_decode", T=64, d=512, F=256, act="bf16", bias_range=0.05),
     # 96 rows per routed expert: the large-batch GEMM
     MoEConfig("graph_big", T=4096, d=512, F=256, act="bf16", bias_range=0.05),
+    # 192 rows per routed expert: 256-row tiles, shared experts' down fused
+    # with the combine
+    MoEConfig("graph_big256", T=8192, d=512, F=256, act="bf16", bias_range=0.05),
     # MXFP4 routed weights, 64-row shared-expert GEMM with K slices
     MoEConfig("graph_fp4", T=64, d=512, F=256, act="bf16", bias_range=0.05, fp4_weights=True),
     # capacity-limited dispatch

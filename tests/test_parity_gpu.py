@@ -16,8 +16,9 @@ from oracle import moe_oracle as O
 from sparse_mixture_experts_04_amd import configs, synth
 from sparse_mixture_experts_04_amd.configs import MoEConfig
 
-from parity_util import (Buffers, cap_for, check_bias, check_dispatch, check_routing,
-                         desc_for, device_weights, expert_getter, host_weights, log, np64, npi,
+from parity_util import (Buffers, cap_for, check_bias, check_dispatch,
+                         check_forward_matches_stages, check_routing, desc_for, device_weights,
+                         expert_getter, fused_combine, host_weights, log, np64, npi,
                          per_expert_rel_l2, rel_l2, run_forward, run_stages)
 
 pytestmark = pytest.mark.gpu
@@ -52,6 +53,13 @@ SMALL = {
                         bias_range=0.05),
     "e128_s1_big": MoEConfig("e128_s1_big", T=2048, d=256, F=256, E=128, S=1, act="bf16",
                              bias_range=0.05),
+    # 192 rows per routed expert and one shared expert: the 256-row tiles and
+    # the forward's fused shared-expert down + combine over a single expert
+    "e128_s1_mt256": MoEConfig("e128_s1_mt256", T=4096, d=256, F=256, E=128, S=1,
+                               act="bf16", bias_range=0.05),
+    # the fused combine with capacity-dropped pairs
+    "bf16_cap_mt256": MoEConfig("bf16_cap_mt256", T=7000, d=256, F=128, act="bf16",
+                                bias_range=0.05, capacity_factor=1.0),
     "e64_s2_f32_cap": MoEConfig("e64_s2_f32_cap", T=200, d=256, F=128, E=64, S=2, act="f32",
                                 bias_range=0.1, wd_std_from_F=True, capacity_factor=1.0),
     "e128_s0_lse_cap": MoEConfig("e128_s0_lse_cap", T=1200, d=512, F=128, E=128, S=0,
@@ -117,11 +125,15 @@ def test_full_parity_stagewise(name):
     assert e_comb <= (1e-6 if cfg.act == "f32" else 4e-3)
     assert e_y <= tol
 
-    # the fused entry point gives bit-identical results
+    # the fused entry point: the same routing and bias bit for bit; y bit
+    # for bit, or within the oracle tolerance where it fuses the shared
+    # experts' down GEMM with the combine
     bf, bias_f = run_forward(desc, inp, cfg.gamma)
-    for n in ("topk", "gates", "counts", "offsets", "sorted_pair", "pair_pos", "y"):
-        assert torch.equal(getattr(b, n), getattr(bf, n)), n
-    assert torch.equal(bias_new, bias_f)
+    check_forward_matches_stages(cfg, b, bias_new, bf, bias_f)
+    if fused_combine(cfg):
+        e_yf = rel_l2(np64(bf.y), y_ref)
+        log(f"  forward y rel L2 {e_yf:.2e}")
+        assert e_yf <= tol
 
 
 def test_empty_batch():
@@ -152,12 +164,13 @@ def sample_tokens(T, n, seed=0):
     return sorted(picks)
 
 
-def check_full_size_output(cfg, inp, b, dp, g_ref):
+def check_full_size_output(cfg, inp, b, dp, g_ref, y_forward=None):
     """Every output of a full-size workload against the oracle fed the GPU's
     selection: each routed expert's rows of y_routed (per-expert relative
     L2, so an error confined to one tile of one expert shows), each shared
     expert's y_shared per 256-column slice, combine on the GPU's own expert
-    outputs, and y end to end over every token."""
+    outputs, and y end to end over every token; with y_forward (moe_forward's
+    y on the same inputs), that y end to end too."""
     k, T, S = cfg.k, cfg.T, cfg.S
     x64 = np64(inp["x"])
     W = device_weights(inp)
@@ -181,6 +194,10 @@ def check_full_size_output(cfg, inp, b, dp, g_ref):
     tol = out_tol(cfg)
     assert e_exp <= tol and e_sl <= tol and e_y <= tol
     assert e_comb <= 4e-3
+    if y_forward is not None:
+        e_yf = rel_l2(np64(y_forward), y_ref)
+        log(f"  forward y rel L2 {e_yf:.2e}")
+        assert e_yf <= tol
 
 
 @pytest.mark.timeout(600)
@@ -203,12 +220,11 @@ def test_workload_parity_every_token(name):
     dp = check_dispatch(topk, b, cap=cap_for(cfg))
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
     del x64, r
-    check_full_size_output(cfg, inp, b, dp, g_ref)
-    # the fused entry point gives the stage calls' results bit for bit
+    # the fused entry point: the stage calls' routing and bias bit for bit,
+    # and its own y against the oracle over every token
     bf, bias_f = run_forward(desc, inp, cfg.gamma)
-    for n in ("topk", "gates", "counts", "offsets", "sorted_pair", "pair_pos", "y"):
-        assert torch.equal(getattr(b, n), getattr(bf, n)), n
-    assert torch.equal(bias_new, bias_f)
+    check_forward_matches_stages(cfg, b, bias_new, bf, bias_f)
+    check_full_size_output(cfg, inp, b, dp, g_ref, y_forward=bf.y)
     del inp, b, bf
     torch.cuda.empty_cache()
 
@@ -261,7 +277,7 @@ def combine_rel_l2_chunked(b, k, chunk=2048):
     return (num / den) ** 0.5
 
 
-def check_skewed_step_outputs(cfg, inp, b, dp, g_ref, step, x64):
+def check_skewed_step_outputs(cfg, inp, b, dp, g_ref, step, x64, y_forward=None):
     """At one step of the skewed workload: every row of four experts (the
     hottest, the second hottest, the median and the lightest non-empty one)
     against the oracle's SwiGLU of the same tokens; every row of each shared
@@ -297,10 +313,11 @@ def check_skewed_step_outputs(cfg, inp, b, dp, g_ref, step, x64):
     y_ref = O.output_rows(toks, x64, npi(b.topk), g_ref, expert_getter(inp, E),
                           pair_pos=dp["pair_pos"])
     e_y = rel_l2(np64(b.y)[toks], y_ref)
+    e_yf = 0.0 if y_forward is None else rel_l2(np64(y_forward)[toks], y_ref)
     log(f"  step {step}: experts {picks} worst rel L2 {worst:.2e}; shared columns "
         f"{c0}..{c0 + 255} {e_sh:.2e}; combine (every token) {e_comb:.2e}; y on "
-        f"{len(toks)} tokens of expert {hot} {e_y:.2e}")
-    assert worst <= 2e-2 and e_sh <= 2e-2 and e_y <= 2e-2
+        f"{len(toks)} tokens of expert {hot} {e_y:.2e} (forward {e_yf:.2e})")
+    assert worst <= 2e-2 and e_sh <= 2e-2 and e_y <= 2e-2 and e_yf <= 2e-2
     assert e_comb <= 4e-3
 
 
@@ -325,8 +342,12 @@ def test_skewed_workload_100_steps_lockstep():
         inp["x"] = synth.make_x(cfg, DEV, step)
         inp["bias"] = bias.clone()
         full = step in (0, 49, 99)
+        bf = None
         if full:
             b, bias = run_stages(desc, inp, cfg.gamma)
+            # moe_forward on the same inputs (its fused shared down + combine)
+            bf, bias_f = run_forward(desc, inp, cfg.gamma)
+            check_forward_matches_stages(cfg, b, bias, bf, bias_f)
         else:
             b, bias = run_forward(desc, inp, cfg.gamma)
         x64 = np64(inp["x"])
@@ -340,8 +361,9 @@ def test_skewed_workload_100_steps_lockstep():
         log(f"  step {step}: max/mean load {c.max() / c.mean():.2f}, near-ties {st['exempt']} "
             f"(differ {st['exempt_differ']}), gate rel {st['gate_max_rel']:.1e}")
         if full:
-            check_skewed_step_outputs(cfg, inp, b, dp, g_ref, step, x64)
-        del b, x64
+            check_skewed_step_outputs(cfg, inp, b, dp, g_ref, step, x64,
+                                      y_forward=bf.y)
+        del b, bf, x64
     log(f"  100 steps: near-tie tokens {exempt}, of which {differ} picked the other set")
     assert 0 <= differ <= exempt
     del inp
