@@ -903,6 +903,9 @@ def main():
         "ms_per_step_p10_p50_p90": inp.pop("_spread"),   # over groups of 5 of the timed steps
         "ms_per_step_hip_graph": round(inp.pop("_graph_ms"), 4),
         "stage_ms": {k: round(v, 4) for k, v in stages.items()},
+        "stage_note": ("256-row tiles: 'down' is the routed experts' down GEMM; 'combine' is "
+                       "the shared experts' down GEMM fused with the combine"
+                       if cfg.T * cfg.k // cfg.E >= 160 and cfg.S > 0 else None),
         "kernel_ms": {k: round(v, 4) for k, v in kernels.items()},
         "roofline": {"kernel": "ffn_big_kernel<gate/up> (grouped gate/up GEMM + SwiGLU over "
                                "every routed and shared row)",
