@@ -54,6 +54,7 @@ inline int router_cols_padded(const Shape& s) {
   return (n + kRouterColTile - 1) / kRouterColTile * kRouterColTile;
 }
 int router_ksplits(const Shape& s);
+size_t router_refine_ints(const Shape& s);
 
 // Dispatch segments: pairs handled by one stable-scatter wave.
 constexpr int kDispatchSeg = 512;
@@ -71,8 +72,8 @@ hipError_t launch_router_planes(const Shape& s, const float* w_router, bf16_t* p
                                 hipStream_t st);
 
 // prepared: planes from launch_router_planes, or null to split w_router
-// into wplanes (workspace) first.  refine: T + 1 ints of workspace (the
-// tokens the exact pass redoes).
+// into wplanes (workspace) first.  refine: router_refine_ints(s) ints of
+// workspace (the tokens the exact pass redoes, with their candidates).
 hipError_t launch_router(const Shape& s, const void* x, const float* w_router,
                          const bf16_t* prepared, const float* bias, int32_t* topk_idx,
                          float* gates, float* margin, bf16_t* wplanes, double* partial,

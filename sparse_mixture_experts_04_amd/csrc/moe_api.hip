@@ -88,7 +88,7 @@ RouterWs carve_router(Carver& c, const Shape& s) {
   const size_t npad = router_cols_padded(s);
   r.planes = c.take<bf16_t>(3 * npad * s.d);
   r.partial = c.take<double>(static_cast<size_t>(router_ksplits(s)) * s.T * npad);
-  r.refine = c.take<int32_t>(static_cast<size_t>(s.T) + 1);
+  r.refine = c.take<int32_t>(router_refine_ints(s));
   return r;
 }
 int32_t* carve_dispatch(Carver& c, const Shape& s) {

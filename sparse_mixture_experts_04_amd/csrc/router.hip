@@ -28,6 +28,11 @@ namespace moe {
 // could differ from exact arithmetic is redone, and few enough tokens that
 // the refinement is cheap.
 constexpr double kRefineGap = 1e-5;
+// The selection's record of a token for the exact pass: token, candidate
+// count (or -1 when there are more than kRefineCand), then the candidates'
+// expert ids in ascending order.
+constexpr int kRefineCand = 14;
+constexpr int kRefineRec = 2 + kRefineCand;
 
 // ---------------------------------------------------------------- planes
 
@@ -621,12 +626,41 @@ __global__ __launch_bounds__(256) void router_select(
   int i_sel[K];     // candidate j is expert j here
   double s_pick[K], z_pick[K], k_sel[K + 1];
   rank_rounds<K, EPL>(lane, valid, key, sv, zv, i_sel, s_pick, z_pick, k_sel);
-  write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk, gates,
-                    margin, logsumexp_norm, gate_scale);
   double gap = INFINITY;
 #pragma unroll
   for (int r = 0; r < K; ++r) gap = fmin(gap, k_sel[r] - k_sel[r + 1]);
-  if (lane == 0 && gap < kRefineGap) refine[1 + atomicAdd(refine, 1)] = t;
+  const bool listed = gap < kRefineGap;  // the same on every lane
+  // the candidates of a listed token: every routed expert whose key lies
+  // within kRefineGap of the (K + 1)-th best (lane masks per q)
+  unsigned long long m[EPL];
+  int nc = 0;
+#pragma unroll
+  for (int q = 0; q < EPL; ++q) {
+    m[q] = __ballot(listed && key[q] >= k_sel[K] - kRefineGap);
+    nc += __popcll(m[q]);
+  }
+  write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk, gates,
+                    margin, logsumexp_norm, gate_scale);
+  if (listed) {
+    int slot = 0;
+    if (lane == 0) slot = atomicAdd(refine, 1);
+    slot = __builtin_amdgcn_readfirstlane(slot);
+    int32_t* rec = refine + 1 + static_cast<size_t>(slot) * kRefineRec;
+    if (lane == 0) {
+      rec[0] = t;
+      rec[1] = nc <= kRefineCand ? nc : -1;
+    }
+    if (nc <= kRefineCand) {
+      // in ascending id: q outer, lane inner
+      int pos = 0;
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) {
+        if ((m[q] >> lane) & 1ull)
+          rec[2 + pos + __popcll(m[q] & ((1ull << lane) - 1ull))] = lane + 64 * q;
+        pos += __popcll(m[q]);
+      }
+    }
+  }
 }
 
 // Exact logits of the tokens router_select listed, for the experts that can
@@ -659,8 +693,16 @@ __global__ __launch_bounds__(512) void router_refine(
   const int lane = tid & 63, wave = tid >> 6;
   const int n = refine[0];
   for (int i = blockIdx.x; i < n; i += gridDim.x) {
-    const int t = refine[1 + i];
-    if (wave == 0) {
+    const int32_t* rec = refine + 1 + static_cast<size_t>(i) * kRefineRec;
+    const int t = rec[0];
+    const int nrec = rec[1];
+    if (nrec >= 0) {
+      // the selection listed the candidates
+      if (tid < nrec) cand[tid] = rec[2 + tid];
+      if (tid < S) cand[nrec + tid] = E + tid;
+      if (tid == 0) s_nc = nrec;
+    } else if (wave == 0) {
+      // more than kRefineCand candidates: list them again from the keys
       double zv[EPL], sv[EPL], key[EPL], z_unused;
       token_keys<EPL, S>(partial, nks, T, npad, E, t, lane, bias, zv, sv, key, z_unused);
       bool valid[EPL];
@@ -685,6 +727,9 @@ __global__ __launch_bounds__(512) void router_refine(
     __syncthreads();
     const int nc = s_nc;
     const int ntot = nc + S;
+    // the candidates' biases, loaded while the exact logits are summed
+    const double bias_c =
+        wave == 0 && lane < nc && lane < 64 ? static_cast<double>(bias[cand[lane]]) : 0.0;
     // K in spans of 512 threads x 4 elements x CH chunks; each group of NB
     // candidates issues all of its loads for the span before any addition,
     // so a token costs about one round trip per span and group
@@ -751,21 +796,30 @@ __global__ __launch_bounds__(512) void router_refine(
       }
     }
     if (wave == 0) {
-      // candidate j = lane + 64q is cand[j] (routed ones only, ascending id)
-      bool valid[EPL];
-      double zv[EPL], sv[EPL], key[EPL];
-#pragma unroll
-      for (int q = 0; q < EPL; ++q) {
-        const int j = lane + 64 * q;
-        valid[q] = j < nc;
-        zv[q] = valid[q] ? zc[j] : 0.0;
-        sv[q] = sigmoid64(zv[q]);
-        key[q] = valid[q] ? sv[q] + static_cast<double>(bias[cand[j]]) : -INFINITY;
-      }
+      // candidate j = lane + 64q is cand[j] (routed ones only, ascending
+      // id); up to 64 of them (always, from a record) sit one per lane
       const double z_sh = lane < S ? zc[nc + lane] : 0.0;
       int j_sel[K], i_sel[K];
       double s_pick[K], z_pick[K], k_sel[K + 1];
-      rank_rounds<K, EPL>(lane, valid, key, sv, zv, j_sel, s_pick, z_pick, k_sel);
+      if (nc <= 64) {
+        const bool valid[1] = {lane < nc};
+        const double zv[1] = {valid[0] ? zc[lane] : 0.0};
+        const double sv[1] = {sigmoid64(zv[0])};
+        const double key[1] = {valid[0] ? sv[0] + bias_c : -INFINITY};
+        rank_rounds<K, 1>(lane, valid, key, sv, zv, j_sel, s_pick, z_pick, k_sel);
+      } else {
+        bool valid[EPL];
+        double zv[EPL], sv[EPL], key[EPL];
+#pragma unroll
+        for (int q = 0; q < EPL; ++q) {
+          const int j = lane + 64 * q;
+          valid[q] = j < nc;
+          zv[q] = valid[q] ? zc[j] : 0.0;
+          sv[q] = sigmoid64(zv[q]);
+          key[q] = valid[q] ? sv[q] + static_cast<double>(bias[cand[j]]) : -INFINITY;
+        }
+        rank_rounds<K, EPL>(lane, valid, key, sv, zv, j_sel, s_pick, z_pick, k_sel);
+      }
 #pragma unroll
       for (int r = 0; r < K; ++r) i_sel[r] = cand[j_sel[r]];
       write_token<K, S>(t, lane, i_sel, s_pick, z_pick, sigmoid64(z_sh), z_sh, k_sel, topk,
@@ -778,6 +832,10 @@ __global__ __launch_bounds__(512) void router_refine(
 // ------------------------------------------------------------------ host
 
 int router_chunk(const Shape& s) { return s.d % kRouterChunk == 0 ? kRouterChunk : 32; }
+
+size_t router_refine_ints(const Shape& s) {
+  return 1 + static_cast<size_t>(s.T) * kRefineRec;
+}
 
 int router_ksplits(const Shape& s) {
   const int tiles = ((s.T + 127) / 128) * (router_cols_padded(s) / kRouterColTile);

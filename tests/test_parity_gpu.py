@@ -588,6 +588,45 @@ def test_identical_tokens_with_an_exact_tie(T):
     assert np.array_equal(y, np.broadcast_to(y[0], y.shape))   # identical rows out
 
 
+def test_twenty_way_exact_tie():
+    """The 6th choice's routing vector copied into 19 other experts outside
+    the top 5, every token the same: 20 experts share the 6th key exactly,
+    more candidates than the selection hands to the exact pass in its record,
+    so that pass lists them again from the keys.  The lowest of the 20 ids
+    must win ("Inkling, Dissected", 02b, ties to the lower index), as in the
+    oracle, and the outputs match."""
+    cfg = MoEConfig("same20", T=600, d=512, F=256, act="bf16", bias_range=0.0)
+    log(f"[20-way tie] {cfg.describe()}")
+    inp = synth.make_inputs(cfg, device="cpu")
+    inp["x"][:] = inp["x"][0]
+    x0 = inp["x"][0].double().numpy()
+    z = np64(inp["w_router"][: cfg.E]) @ x0
+    order = np.argsort(-z, kind="stable")
+    j6 = int(order[5])
+    top5 = set(order[:5].tolist())
+    others = [e for e in range(cfg.E) if e not in top5 and e != j6][:19]
+    for e in others:
+        inp["w_router"][e] = inp["w_router"][j6]
+    tied = sorted(others + [j6])
+    inp = to_dev(inp)
+    desc = desc_for(cfg)
+    b, bias_new = run_forward(desc, inp, cfg.gamma)
+    topk = npi(b.topk)
+    want = np.array(list(order[:5]) + [tied[0]])
+    assert np.array_equal(topk, np.broadcast_to(want, topk.shape)), topk[:2]
+    x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
+    r, g_ref, _ = check_routing(x64, wr64, b64, topk, np64(b.gates))
+    assert np.array_equal(r["topk_idx"], topk)
+    dp = check_dispatch(topk, b, E=cfg.E)
+    check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
+    hw = host_weights(inp)
+    yr_ref, ys_ref = O.expert_ffn(x64, hw, dp["offsets"], dp["sorted_pair"], cfg.k)
+    y_ref = O.combine(yr_ref, ys_ref, g_ref, dp["pair_pos"], cfg.k)
+    e_y = rel_l2(np64(b.y), y_ref)
+    log(f"  20 tied experts from {tied[0]}; rel L2 y {e_y:.2e}")
+    assert e_y <= out_tol(cfg)
+
+
 def test_binding_rejects_short_routing_tables():
     """The expert calls read offsets[0..E] and sorted_pair[0..T*k-1]; the
     binding refuses tables of any other length before anything launches."""
