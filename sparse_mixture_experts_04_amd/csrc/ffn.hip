@@ -249,16 +249,7 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   for (int g = tid; g <= G; g += 256) ts[g] = p.tile_start[g];
   __syncthreads();
 
-  // items of groups g_lo..G-1, each tile cut into ksplit K slices (slice
-  // index innermost, so the slices of a tile run side by side).  The
-  // 64-row instantiation serves the shared experts alone: each has T rows,
-  // in ceil(T / 64) row tiles, and its items are numbered directly.
-  const int ksplit = p.ksplit > 1 ? p.ksplit : 1;
-  const int srt = (p.T + MT - 1) / MT;   // row tiles of a shared expert (MT == 64)
-  const long long first = MT == 64 ? 0 : static_cast<long long>(ts[p.g_lo]) * p.n_tiles;
-  const long long total =
-      MT == 64 ? static_cast<long long>(p.S) * srt * p.n_tiles * ksplit
-               : (static_cast<long long>(ts[G]) * p.n_tiles - first) * ksplit;
+  const long long total = static_cast<long long>(ts[G]) * p.n_tiles;
   const int xcd = blockIdx.x & 7;
   __shared__ long long s_item;
 
@@ -270,7 +261,7 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
   const int lrow = lane >> 3;
   const int lchunk[2] = {((lane & 7) ^ lrow) * 8, ((lane & 7) ^ lrow ^ 1) * 8};
   static_assert(C::B_LOADS % 2 == 0, "B load parity follows q");
-  const int nk_all = p.K / C::BK;
+  const int nk = p.K / C::BK;
 
   for (;;) {
     // persistent: the next item of this XCD's chunk, then of the others'
@@ -278,24 +269,7 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
     __syncthreads();
     const long long it = s_item;
     if (it < 0) break;
-    const int ks = static_cast<int>(it % ksplit);
-    Item item;
-    if constexpr (MT == 64) {
-      // shared expert, column tile outer, row tile inner
-      const long long t2 = it / ksplit;
-      const int per = srt * p.n_tiles;
-      const int local = static_cast<int>(t2 % per);
-      item.g = p.E + static_cast<int>(t2 / per);
-      item.n = local / srt;
-      item.m0 = (local % srt) * MT;
-      item.grows = p.T;
-      item.rows = p.T - item.m0 < MT ? p.T - item.m0 : MT;
-    } else {
-      item = decode_item(first + it / ksplit, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
-    }
-    const int kb = ks * nk_all / ksplit;                 // this slice's K steps
-    const int nk = (ks + 1) * nk_all / ksplit - kb;
-    const size_t koff = static_cast<size_t>(kb) * C::BK;
+    const Item item = decode_item(it, ts, G, p.n_tiles, MT, p.offsets, p.T, p.E);
     const int g = item.g;
     const bool routed = g < p.E;
     const size_t row_base = routed ? static_cast<size_t>(p.offsets[g])
@@ -315,7 +289,7 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
       if (GATED) src_row = routed ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
                                   : static_cast<size_t>(rr);
       else src_row = row_base + rr;
-      t.a_src[q] = A + src_row * p.K + koff + lchunk[(wave * C::A_LOADS + q) & 1];
+      t.a_src[q] = A + src_row * p.K + lchunk[(wave * C::A_LOADS + q) & 1];
     }
     const size_t wstride = static_cast<size_t>(p.N) * p.K;
     const int ge = routed ? g : g - p.E;
@@ -328,12 +302,12 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
       const int col = item.n * C::NOUT + wave * 32 + lrow;
       const bf16_t* wg = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
       const bf16_t* wu = static_cast<const bf16_t*>(routed ? p.w1 : p.ws1) + ge * wstride;
-      t.b_src0 = wg + static_cast<size_t>(col) * p.K + koff;
-      t.b_src1 = wu + static_cast<size_t>(col) * p.K + koff;
+      t.b_src0 = wg + static_cast<size_t>(col) * p.K;
+      t.b_src1 = wu + static_cast<size_t>(col) * p.K;
     } else {
       const int col = item.n * C::NOUT + wave * C::B_LOADS * 8 + lrow;
       const bf16_t* wd = static_cast<const bf16_t*>(routed ? p.w0 : p.ws0) + ge * wstride;
-      t.b_src0 = wd + static_cast<size_t>(col) * p.K + koff;
+      t.b_src0 = wd + static_cast<size_t>(col) * p.K;
       t.b_src1 = t.b_src0;
     }
 
@@ -361,26 +335,6 @@ __global__ __launch_bounds__(256, 1) void ffn_bf16_kernel(FfnArgs p) {
 
     // ---- epilogue.  32x32 accumulator layout: lane l holds column l%32 and
     // rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
-    if (p.part) {
-      // a K slice of a shared tile: fp32 accumulators as they are (weight
-      // row order of the tile, no activation); shared_reduce_kernel sums
-      // the slices
-      const size_t ldp = static_cast<size_t>(p.n_tiles) * C::NB;
-      float* prow0 = p.part + (static_cast<size_t>(ks) * p.S * p.T +
-                               static_cast<size_t>(g - p.E) * p.T + item.m0) * ldp;
-#pragma unroll
-      for (int i = 0; i < C::BM; ++i) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = wm * C::WM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-          if (row >= item.rows) continue;
-#pragma unroll
-          for (int j = 0; j < C::BN; ++j)
-            prow0[row * ldp + item.n * C::NB + wn * C::WN + j * 32 + (lane & 31)] = acc[i][j][r];
-        }
-      }
-      continue;
-    }
     bf16_t* out = static_cast<bf16_t*>(routed ? p.out_routed : p.out_shared);
     const size_t orow0 = routed ? static_cast<size_t>(p.offsets[g]) + item.m0
                                 : static_cast<size_t>(g - p.E) * p.T + item.m0;
@@ -547,19 +501,24 @@ __global__ __launch_bounds__(256) void shared_reduce_kernel(const float* __restr
 size_t shared_partial_floats(const Shape& s) {
   if (!s.w_fp4 || !s.bf16 || s.S == 0) return 0;
   const size_t rows = static_cast<size_t>(s.S) * s.T;
-  const int kg = shared_ksplit(s, s.F / 128, s.d / 64, kSharedRows);
-  const int kd = shared_ksplit(s, s.d / 256, s.F / 64, kSharedRows);
-  const size_t g = kg > 1 ? kg * rows * 2 * s.F : 0;
-  const size_t d = kd > 1 ? kd * rows * s.d : 0;
+  const size_t g = kFp4SharedSlices * rows * 2 * s.F;
+  const size_t d = kFp4SharedSlices * rows * s.d;
   return g > d ? g : d;
 }
 
-// The shared experts alone on the bf16 kernel with 64-row tiles (FP4 routed
-// weights), K-sliced when their tiles are too few to fill the chip.  At
-// decode sizes a shared expert's rows then sit in one row tile, so each of
-// its weight bytes passes through one CU rather than one per 32 rows.
+// The shared experts' slices of the FP4 launch summed (shared_reduce_kernel)
+// into h's shared rows (GATED, with SwiGLU) or y_shared.
 template <bool GATED>
-static hipError_t run_shared_bf16(FfnArgs a, const Shape& s, float* part, hipStream_t st);
+static hipError_t reduce_fp4_shared(const FfnArgs& a, const Shape& s, hipStream_t st) {
+  const int rows = s.S * s.T;
+  const int nout = GATED ? s.F : s.d;
+  const long long n = static_cast<long long>(rows) * nout;
+  const long long blocks = (n + 255) / 256;
+  shared_reduce_kernel<GATED><<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0,
+                                st>>>(a.part, a.ksplit, rows, a.n_tiles * 256, nout,
+                                      static_cast<bf16_t*>(a.out_shared));
+  return hipGetLastError();
+}
 
 template <int MT, bool GATED>
 static hipError_t run_bf16(const FfnArgs& a, hipStream_t st) {
@@ -572,25 +531,6 @@ static hipError_t run_bf16(const FfnArgs& a, hipStream_t st) {
 static hipError_t record_marks(hipEvent_t* marks, hipStream_t st) {
   if (marks && hipEventRecord(marks[0], st) != hipSuccess) return hipErrorInvalidValue;
   return hipSuccess;
-}
-
-template <bool GATED>
-static hipError_t run_shared_bf16(FfnArgs a, const Shape& s, float* part, hipStream_t st) {
-  if (s.S == 0) return hipSuccess;
-  a.g_lo = s.E;
-  a.ksplit = shared_ksplit(s, a.n_tiles, a.K / 64, kSharedRows);
-  a.part = a.ksplit > 1 ? part : nullptr;
-  if (a.ksplit > 1 && !part) return hipErrorInvalidValue;
-  hipError_t e = run_bf16<kSharedRows, GATED>(a, st);
-  if (e != hipSuccess || !a.part) return e;
-  const int rows = s.S * s.T;
-  const int nout = GATED ? s.F : s.d;
-  const long long n = static_cast<long long>(rows) * nout;
-  const long long blocks = (n + 255) / 256;
-  shared_reduce_kernel<GATED><<<static_cast<unsigned>(blocks < 4096 ? blocks : 4096), 256, 0,
-                                st>>>(part, a.ksplit, rows, a.n_tiles * 256, nout,
-                                      static_cast<bf16_t*>(a.out_shared));
-  return hipGetLastError();
 }
 
 template <bool GATED>
@@ -634,9 +574,12 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
     if (fold_gates) return hipErrorInvalidValue;  // the fused combine is large-batch only
     int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1;
     a.counters = ctr + kCtrGateUp * kXcds;  // FP4 kernel: static order, no counters
-    if (s.w_fp4) {  // routed experts in FP4, then the bf16 shared experts
+    if (s.w_fp4) {  // routed experts in FP4 and the bf16 shared experts, one launch
+      if (s.S > 0 && !part) return hipErrorInvalidValue;
+      a.ksplit = s.S > 0 ? (s.d / 32 < kFp4SharedSlices ? s.d / 32 : kFp4SharedSlices) : 0;
+      a.part = part;
       hipError_t e = launch_fp4(a, true, st);
-      if (e == hipSuccess) e = run_shared_bf16<true>(a, s, part, st);
+      if (e == hipSuccess && s.S > 0) e = reduce_fp4_shared<true>(a, s, st);
       return e == hipSuccess ? record_marks(marks, st) : e;
     }
     hipError_t e = run_bf16<32, true>(a, st);
@@ -676,8 +619,11 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const ui
     int32_t* ctr = const_cast<int32_t*>(tile_start) + s.E + s.S + 1;
     a.counters = ctr + kCtrDown * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {
+      if (s.S > 0 && !part) return hipErrorInvalidValue;
+      a.ksplit = s.S > 0 ? (s.F / 32 < kFp4SharedSlices ? s.F / 32 : kFp4SharedSlices) : 0;
+      a.part = part;
       hipError_t e = launch_fp4(a, false, st);
-      if (e == hipSuccess) e = run_shared_bf16<false>(a, s, part, st);
+      if (e == hipSuccess && s.S > 0) e = reduce_fp4_shared<false>(a, s, st);
       return e == hipSuccess ? record_marks(marks, st) : e;
     }
     hipError_t e = run_bf16<32, false>(a, st);

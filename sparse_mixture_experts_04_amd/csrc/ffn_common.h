@@ -83,9 +83,8 @@ struct FfnArgs {
   int n_tiles;            // column tiles
   const uint8_t* sc0;     // FP4 routed weights: scales of w0 / w1 [E, K/32, N]
   const uint8_t* sc1;
-  int g_lo;               // first group the 32-row bf16 kernel processes
-  int ksplit;             // 32-row bf16 kernel, shared groups only: K slices per tile
-  float* part;            // ksplit > 1: fp32 partial tiles [ksplit][S*T][n_tiles*256]
+  int ksplit;             // FP4 kernel: K slices of a shared-expert tile (0: none)
+  float* part;            // FP4 kernel: fp32 partial tiles [ksplit][S*T][n_tiles*256]
   int32_t* counters;      // ffn_bf16_kernel: kXcds work counters, zero at launch
   int g_hi;               // large-batch kernel: groups 0..g_hi-1 only (0: all E + S)
   // Fused shared experts + combine (large-batch forward, S > 0):
@@ -120,23 +119,6 @@ __device__ __forceinline__ long long claim_item(int32_t* counters, int xcd, long
   }
   return -1;
 }
-
-// Row tile of the shared-expert GEMMs when the bf16 kernel runs them alone
-// (beside FP4 routed experts).
-constexpr int kSharedRows = 64;
-
-// K slices of those tiles (S * ceil(T / rows) * n_tiles of them): enough
-// items to cover 256 workgroups, at most 8 slices and never more than the
-// K steps (nk) of a tile.
-inline int shared_ksplit(const Shape& s, int n_tiles, int nk, int rows) {
-  const long long items = static_cast<long long>(s.S) * ((s.T + rows - 1) / rows) * n_tiles;
-  if (items <= 0) return 1;
-  long long k = (256 + items - 1) / items;
-  k = k > 8 ? 8 : k;
-  k = k > nk ? nk : k;
-  return static_cast<int>(k < 1 ? 1 : k);
-}
-
 
 // ---------------------------------------------------------- LDS helpers
 
@@ -201,7 +183,12 @@ hipError_t launch_big_combine(const FfnArgs& a, int mt, int32_t* counters, hipSt
 // prefix (G+1) | work counters kCtrSets GEMMs x kXcds].
 inline int big_plan_ints(int G) { return (G + 1) + kCtrSets * kXcds; }
 
-// Decode-batch GEMMs over the routed groups with FP4 weights (ffn_fp4.hip).
+// Decode-batch GEMMs over the routed groups with FP4 weights (ffn_fp4.hip);
+// with a.ksplit > 0 the same launch also runs the shared experts' bf16
+// tiles in a.ksplit K slices, writing fp32 partials to a.part
+// ([ksplit][S*T][n_tiles*256]) for shared_reduce.
 hipError_t launch_fp4(const FfnArgs& a, bool gated, hipStream_t st);
+// K slices of a shared-expert tile in the FP4 launch.
+constexpr int kFp4SharedSlices = 4;
 
 }  // namespace moe

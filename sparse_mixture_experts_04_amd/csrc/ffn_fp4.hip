@@ -187,8 +187,150 @@ __device__ __forceinline__ void fp4_stage(const uint8_t* st, int wn, int lane,
   }
 }
 
-// Routed groups only (the shared experts' weights are bf16 and go through
-// the bf16 kernel).  Persistent workgroups over the items of groups
+// ------------------------------------------- shared experts in the launch
+
+// The shared experts' weights stay bf16 ("Under The Hood: Inkling",
+// "Quantization: BF16 vs NVFP4"); their tiles run in the same persistent
+// launch as the FP4 routed tiles, after each XCD's routed items, so they
+// fill the last round of the static item order instead of running alone
+// afterwards.  A shared tile: 64 token rows x 256 weight rows (the same
+// weight-row layout as the FP4 tiles: for GATED, wave w's rows
+// 64w..64w+31 are W_gate columns 32w.. of the 128-column output tile and
+// rows 64w+32.. the same W_up columns), one of kFp4SharedSlices K slices,
+// K step 32 through the FP4 ring's memory (LDS rows of 64 bytes, chunk c
+// of row r in slot c ^ ((r >> 2) & 3)): per stage 64 activation rows (4
+// KiB) then 256 weight rows (16 KiB), one activation and four weight loads
+// of 1 KiB per wave.  A slice writes its fp32 accumulators to
+// part[slice][s*T + row][n*256 + weight row]; shared_reduce_kernel sums the
+// slices after the launch.  kFp4SharedSlices slices make a shared item
+// stream about as many bytes as an FP4 item (bf16 is 32/17 times the FP4
+// bytes per weight).
+constexpr int kFp4SharedRows = 64;
+constexpr int kFp4SharedBK = 32;
+constexpr int kFp4SharedA = kFp4SharedRows * kFp4SharedBK * 2;   // 4 KiB
+constexpr int kFp4SharedB = Fp4Cfg::NB * kFp4SharedBK * 2;      // 16 KiB
+static_assert(kFp4SharedA + kFp4SharedB <= Fp4Cfg::STAGE, "a shared stage fits an FP4 stage");
+
+template <bool GATED>
+__device__ __forceinline__ void fp4_shared_item(const FfnArgs& p, long long si,
+                                                const uint8_t* ring, uint32_t ring_base,
+                                                int wave, int lane) {
+  using C = Fp4Cfg;
+  // si -> (shared expert, column tile, row tile, slice), slice innermost
+  const int srt = (p.T + kFp4SharedRows - 1) / kFp4SharedRows;
+  const int ks = static_cast<int>(si % p.ksplit);
+  long long rest = si / p.ksplit;
+  const int mt = static_cast<int>(rest % srt);
+  rest /= srt;
+  const int n = static_cast<int>(rest % p.n_tiles);
+  const int se = static_cast<int>(rest / p.n_tiles);
+  const int m0 = mt * kFp4SharedRows;
+  const int rows = p.T - m0 < kFp4SharedRows ? p.T - m0 : kFp4SharedRows;
+  const int nk_all = p.K / kFp4SharedBK;
+  const int kb = ks * nk_all / p.ksplit;
+  const int nk = (ks + 1) * nk_all / p.ksplit - kb;
+
+  // load sources (16 LDS rows of 64 bytes per load; lane l lands in row
+  // 16j + l/4, slot l%4, and fetches chunk (l%4) ^ ((l >> 4) & 3))
+  const int lr = lane >> 2;
+  const int sch = ((lane & 3) ^ ((lane >> 4) & 3)) * 8;
+  const bf16_t* a_src;
+  {
+    int r = 16 * wave + lr;
+    r = r < rows ? r : rows - 1;
+    const size_t row = GATED ? static_cast<size_t>(m0 + r)
+                             : static_cast<size_t>(p.k) * p.T +
+                                   static_cast<size_t>(se) * p.T + m0 + r;  // h's shared rows
+    a_src = static_cast<const bf16_t*>(p.a) + row * p.K + sch;
+  }
+  const bf16_t* b_src[4];
+  const size_t wstride = static_cast<size_t>(p.N) * p.K;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int R = 16 * (4 * wave + q) + lr;  // weight row of the tile
+    const bf16_t* base;
+    int col;
+    if (GATED) {
+      const int cg = R >> 6, rl = R & 63;
+      base = static_cast<const bf16_t*>(rl >= 32 ? p.ws1 : p.ws0);
+      col = n * (C::NB / 2) + cg * 32 + (rl & 31);
+    } else {
+      base = static_cast<const bf16_t*>(p.ws0);
+      col = n * C::NB + R;
+    }
+    b_src[q] = base + se * wstride + static_cast<size_t>(col) * p.K + sch;
+  }
+  auto issue = [&](int kt, uint32_t slot) {
+    const int k0 = (kb + kt) * kFp4SharedBK;
+    dma16_lds(a_src + k0, slot + wave * 1024);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      dma16_lds(b_src[q] + k0, slot + kFp4SharedA + (4 * wave + q) * 1024);
+  };
+
+  f32x16_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+  const int nblk = rows > 32 ? 2 : 1;  // 32-row blocks holding rows
+
+  // fragment offset of substep kk: row r32 = l % 32 of a 32-row block,
+  // chunk 2kk + l/32
+  const int r32 = lane & 31;
+  int off[2];
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk) off[kk] = r32 * 32 + (((2 * kk + (lane >> 5)) ^ ((r32 >> 2) & 3)) << 3);
+
+  // every wave is done with the previous item's LDS before refilling it
+  wait_vm<0>();
+  lds_barrier();
+#pragma unroll
+  for (int s_ = 0; s_ < C::NS - 1; ++s_) issue(s_ < nk ? s_ : nk - 1, ring_base + s_ * C::STAGE);
+  for (int kt = 0; kt < nk; ++kt) {
+    wait_vm<(C::NS - 2) * 5>();  // stage kt landed (5 loads per wave per stage)
+    lds_barrier();
+    const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
+    issue(kn, ring_base + ((kt + C::NS - 1) % C::NS) * C::STAGE);
+    const bf16_t* sA = reinterpret_cast<const bf16_t*>(ring + (kt % C::NS) * C::STAGE);
+    const bf16_t* sB = sA + kFp4SharedA / 2;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      bf16x8_t b[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        b[j] = *reinterpret_cast<const bf16x8_t*>(sB + (64 * wave + 32 * j) * 32 + off[kk]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (i >= nblk) continue;
+        const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sA + i * 32 * 32 + off[kk]);
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+  // fp32 partials: lane l holds weight row 32j + l%32 of the wave's 64 and
+  // token rows 8(r/4) + 4(l/32) + r%4 of block i
+  const size_t ldp = static_cast<size_t>(p.n_tiles) * C::NB;
+  float* prow0 = p.part + (static_cast<size_t>(ks) * p.S * p.T +
+                           static_cast<size_t>(se) * p.T + m0) * ldp +
+                 static_cast<size_t>(n) * C::NB + 64 * wave + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      if (row >= rows) continue;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) prow0[row * ldp + 32 * j] = acc[i][j][r];
+    }
+}
+
+// Routed groups, then (p.ksplit > 0) the shared experts' bf16 tiles.  Persistent workgroups over the items of groups
 // 0..E-1, cut into one contiguous chunk per XCD.  Two workgroups share each
 // CU (a 3-stage ring each, 77 KiB of LDS): every item starts by waiting a
 // full HBM latency for its first stage, and the other workgroup's stream
@@ -207,13 +349,23 @@ __global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
   for (int g = tid; g <= G; g += 256) ts[g] = p.tile_start[g];
   __syncthreads();
 
+  // routed items, then the shared items; each XCD takes a contiguous chunk
+  // of both, its routed chunk first
   const long long total = static_cast<long long>(ts[p.E]) * p.n_tiles;  // routed items
+  const long long shared =
+      p.ksplit > 0 ? static_cast<long long>(p.S) *
+                         ((p.T + kFp4SharedRows - 1) / kFp4SharedRows) * p.n_tiles * p.ksplit
+                   : 0;
   const int xcd = blockIdx.x & 7;
   const int per_xcd = gridDim.x >> 3;
   const int slot_id = blockIdx.x >> 3;
   const long long chunk = (total + 7) / 8;
-  const long long beg = xcd * chunk;
+  const long long beg = xcd * chunk < total ? xcd * chunk : total;
   const long long end = beg + chunk < total ? beg + chunk : total;
+  const long long schunk = (shared + 7) / 8;
+  const long long sbeg = xcd * schunk < shared ? xcd * schunk : shared;
+  const long long send = sbeg + schunk < shared ? sbeg + schunk : shared;
+  const long long nitems = (end - beg) + (send - sbeg);
 
   const bf16_t* A = static_cast<const bf16_t*>(p.a);
   const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(ring)));
@@ -226,7 +378,12 @@ __global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
   // source chunk (l%4) ^ ((row >> 2) & 3)
   const int crow = lane >> 2;
 
-  for (long long it = beg + slot_id; it < end; it += per_xcd) {
+  for (long long i = slot_id; i < nitems; i += per_xcd) {
+    if (i >= end - beg) {
+      fp4_shared_item<GATED>(p, sbeg + (i - (end - beg)), ring, ring_base, wave, lane);
+      continue;
+    }
+    const long long it = beg + i;
     const Item item = decode_item(it, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E);
     const int g = item.g;  // routed
     const size_t row_base = static_cast<size_t>(p.offsets[g]);
