@@ -88,6 +88,96 @@ __global__ __launch_bounds__(CB) void combine_kernel(const T* __restrict__ yr,
   Vec<T>::store(y + static_cast<size_t>(t) * d + c0, acc);
 }
 
+// Layers with FP4 routed weights: the shared experts' down outputs arrive
+// as ksplit fp32 K-slice partials (part[ks][s*Tn + t][c], ldp columns per
+// row).  Each output is summed in slice order and rounded to bf16, the
+// value the reduction pass would have stored as y_shared, then combined as
+// in combine_kernel.
+template <int K, int S>
+__global__ __launch_bounds__(CB) void combine_part_kernel(const bf16_t* __restrict__ yr,
+                                                          const float* __restrict__ part,
+                                                          int ksplit, int ldp,
+                                                          const float* __restrict__ gates,
+                                                          const int32_t* __restrict__ pair_pos,
+                                                          int Tn, int d, int nchunk,
+                                                          bf16_t* __restrict__ y) {
+  constexpr int V = 8;
+  const int t = blockIdx.x / nchunk;
+  const int c0 = ((blockIdx.x % nchunk) * CB + threadIdx.x) * V;
+  if (c0 >= d) return;
+  int pos[K];
+  float g[K + S];
+#pragma unroll
+  for (int j = 0; j < K; ++j) pos[j] = pair_pos[static_cast<size_t>(t) * K + j];
+#pragma unroll
+  for (int j = 0; j < K + S; ++j) g[j] = gates[static_cast<size_t>(t) * (K + S) + j];
+  float v[K + S][V];
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    Vec<bf16_t>::load(yr + static_cast<size_t>(pos[j] < 0 ? 0 : pos[j]) * d + c0, v[j]);
+  const size_t slice = static_cast<size_t>(S) * Tn * ldp;
+  float ps[S][kFp4SharedSlicesMax][V];
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int ks = 0; ks < kFp4SharedSlicesMax; ++ks)
+      if (ks < ksplit) {
+        const float* src = part + ks * slice + (static_cast<size_t>(s) * Tn + t) * ldp + c0;
+        float lo[4], hi[4];
+        Vec<float>::load(src, lo);
+        Vec<float>::load(src + 4, hi);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ps[s][ks][i] = lo[i];
+          ps[s][ks][4 + i] = hi[i];
+        }
+      }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float sum = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < kFp4SharedSlicesMax; ++ks)
+        if (ks < ksplit) sum += ps[s][ks][i];
+      v[K + s][i] = bf16_to_f32(f32_to_bf16(sum));
+    }
+  float acc[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) acc[i] = 0.0f;
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    if (pos[j] < 0) continue;  // dropped at the expert's capacity
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g[j], v[j][i], acc[i]);
+  }
+#pragma unroll
+  for (int s = 0; s < S; ++s)
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = fmaf(g[K + s], v[K + s][i], acc[i]);
+  Vec<bf16_t>::store(y + static_cast<size_t>(t) * d + c0, acc);
+}
+
+hipError_t launch_combine_part(const Shape& s, const void* y_routed, const float* part,
+                               int ksplit, const float* gates, const int32_t* pair_pos, void* y,
+                               hipStream_t st) {
+  if (s.T == 0) return hipSuccess;
+  if (!s.bf16 || s.S < 1 || s.S > 2 || ksplit < 1 || ksplit > kFp4SharedSlicesMax ||
+      s.d % 256 != 0)
+    return hipErrorInvalidValue;
+  const int nchunk = (s.d + CB * 8 - 1) / (CB * 8);
+  const long long blocks = static_cast<long long>(s.T) * nchunk;
+  const bf16_t* yr = static_cast<const bf16_t*>(y_routed);
+  bf16_t* out = static_cast<bf16_t*>(y);
+  if (s.S == 1)
+    combine_part_kernel<6, 1><<<static_cast<unsigned>(blocks), CB, 0, st>>>(
+        yr, part, ksplit, s.d, gates, pair_pos, s.T, s.d, nchunk, out);
+  else
+    combine_part_kernel<6, 2><<<static_cast<unsigned>(blocks), CB, 0, st>>>(
+        yr, part, ksplit, s.d, gates, pair_pos, s.T, s.d, nchunk, out);
+  return hipGetLastError();
+}
+
 template <typename T, int S>
 static void run_combine(const Shape& s, const void* y_routed, const void* y_shared,
                         const float* gates, const int32_t* pair_pos, void* y, hipStream_t st) {

@@ -83,6 +83,18 @@ hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* cou
                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                            int32_t* seg_counts, hipStream_t st);
 
+// Small batches (T * k <= kDispatchSmallPairs, E <= 256): the dispatch in
+// one launch, optionally followed by the row-tile plan (tile_start set; the
+// plan launch_tile_plan writes for row_tile 32) and the bias update
+// (gamma != 0; bias as launch_bias_update updates it).  Outputs as
+// launch_dispatch's.
+constexpr int kDispatchSmallPairs = 4096;
+bool dispatch_is_small(const Shape& s);
+hipError_t launch_dispatch_small(const Shape& s, const int32_t* topk_idx, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                 int row_tile, int32_t* tile_start, float gamma, float* bias,
+                                 hipStream_t st);
+
 hipError_t launch_tile_plan(const Shape& s, const int32_t* offsets, int row_tile,
                             int32_t* tile_start, hipStream_t st);
 
@@ -103,10 +115,14 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
 
 // routed_only (large-batch tiles only): the routed experts' tiles alone; the
 // shared experts' down GEMM is left to launch_shared_combine.
+// shared_partials (FP4 routed weights, S > 0): the shared experts' K-slice
+// partials are left in part for launch_combine_part instead of being
+// reduced into y_shared.
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
                        const void* h, void* y_routed, void* y_shared, float* part,
-                       hipEvent_t* marks, hipStream_t st, bool routed_only = false);
+                       hipEvent_t* marks, hipStream_t st, bool routed_only = false,
+                       bool shared_partials = false);
 
 // The shared experts' down GEMM over their gate-scaled rows of h (from
 // launch_gate_up with fold_gates), fused with the combine: writes
@@ -129,6 +145,17 @@ hipError_t launch_quantize_mxfp4(long long E, int N, int K, const void* w, uint8
 hipError_t launch_combine(const Shape& s, const void* y_routed, const void* y_shared,
                           const float* gates, const int32_t* pair_pos, void* y,
                           hipStream_t st);
+
+// Combine for layers with FP4 routed weights and S > 0: the shared
+// experts' down outputs are read as the ksplit fp32 K-slice partials the FP4
+// down launch leaves in part (launch_down with shared_partials), summed and
+// rounded as the reduction pass would have stored them.  bf16, d % 256 == 0.
+constexpr int kFp4SharedSlicesMax = 4;
+hipError_t launch_combine_part(const Shape& s, const void* y_routed, const float* part,
+                               int ksplit, const float* gates, const int32_t* pair_pos, void* y,
+                               hipStream_t st);
+// K slices of a shared-expert tile in the FP4 launch for a GEMM over K.
+int fp4_shared_slices(int K);
 
 hipError_t launch_bias_update(const Shape& s, const int32_t* counts, float gamma,
                               float* bias, hipStream_t st);

@@ -22,7 +22,7 @@
 // rank reaches the expert's capacity is dropped (pair_pos = -1).  A pair
 // whose expert id lies outside [0, E) is counted nowhere and also gets
 // pair_pos = -1.
-#include "common.h"
+#include "ffn_common.h"  // the tile plan's layout (work counters after it)
 
 namespace moe {
 
@@ -143,9 +143,143 @@ __global__ __launch_bounds__(64) void dispatch_scatter(const int32_t* __restrict
   }
 }
 
+// Small batches (at most kDispatchSmallPairs pairs, e.g. decode steps): the
+// three passes in one workgroup of 512 threads, where each launch would
+// otherwise cost more than its work.  Wave w plays the part of a segment: it
+// owns the contiguous pairs w*seg .. w*seg+seg-1 (seg a multiple of 64), so
+// counts, offsets and ranks are those of the multi-block passes.  With
+// tile_start set it then writes the row-tile plan of the decode GEMMs
+// (tile_start[g] = first tile of group g, tile_start[E+S] = total, the work
+// counters after it zeroed: what tile_plan_kernel writes), and with
+// gamma != 0 applies the bias update (the router has read the bias by then).
+__global__ __launch_bounds__(512) void dispatch_small(
+    const int32_t* __restrict__ topk, int npairs, int E, int capacity,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_pair, int32_t* __restrict__ pair_pos, int S, int T, int MT,
+    int32_t* __restrict__ tile_start, long long kT, float gamma, float* __restrict__ bias) {
+  constexpr int W = 8;
+  __shared__ int run[W][256];  // per wave: its count of expert e, then its running rank
+  __shared__ int off[256];
+  __shared__ int sc[512];
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int seg = (npairs + W * 64 - 1) / (W * 64) * 64;
+  const int pb = w * seg;
+  const int pe = pb + seg < npairs ? pb + seg : npairs;
+  for (int i = tid; i < W * 256; i += 512) (&run[0][0])[i] = 0;
+  __syncthreads();
+  for (int p = pb + lane; p < pe; p += 64) {
+    const int e = topk[p];
+    if (static_cast<unsigned>(e) < static_cast<unsigned>(E)) atomicAdd(&run[w][e], 1);
+  }
+  __syncthreads();
+  // thread e: the waves' counts become their running bases; demand and kept
+  int tot = 0;
+  if (tid < E) {
+#pragma unroll
+    for (int ww = 0; ww < W; ++ww) {
+      const int c = run[ww][tid];
+      run[ww][tid] = tot;
+      tot += c;
+    }
+  }
+  const int kept = tid < E ? (tot < capacity ? tot : capacity) : 0;
+  sc[tid] = kept;
+  __syncthreads();
+  for (int o = 1; o < 512; o <<= 1) {
+    const int v = tid >= o ? sc[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += v;
+    __syncthreads();
+  }
+  if (tid < E) {
+    counts[tid] = tot;
+    offsets[tid] = sc[tid] - kept;
+    off[tid] = sc[tid] - kept;
+  }
+  if (tid == E - 1) offsets[E] = sc[tid];
+  __syncthreads();
+  // stable scatter, 64 pairs at a time per wave (every wave runs seg / 64
+  // rounds, so the block barriers below are reached by all)
+  for (int c = 0; c < seg; c += 64) {
+    const int p = pb + c + lane;
+    const bool in_range = p < pe;
+    const int e = in_range ? topk[p] : 0;
+    const bool valid = in_range && static_cast<unsigned>(e) < static_cast<unsigned>(E);
+    if (in_range && !valid) pair_pos[p] = -1;
+    unsigned long long peers = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const bool bit = (e >> b) & 1;
+      const unsigned long long m = __ballot(valid && bit);
+      peers &= bit ? m : ~m;
+    }
+    int cnt = 0;
+    if (valid) {
+      const int r = run[w][e] + __popcll(peers & ((1ull << lane) - 1ull));
+      if (r < capacity) {
+        const int pos = off[e] + r;
+        sorted_pair[pos] = p;
+        pair_pos[p] = pos;
+      } else {
+        pair_pos[p] = -1;
+      }
+      cnt = __popcll(peers);
+    }
+    __syncthreads();
+    if (valid && (peers >> lane) == 1ull) run[w][e] += cnt;
+    __syncthreads();
+  }
+  if (tile_start) {
+    // thread g: row tiles of group g (routed: its kept rows; shared: T)
+    const int G = E + S;
+    int rows = 0;
+    if (tid < E) rows = kept;
+    else if (tid < G) rows = T;
+    const int nt = (rows + MT - 1) / MT;
+    __syncthreads();  // every thread is past its last read of sc
+    sc[tid] = nt;
+    __syncthreads();
+    for (int o = 1; o < 512; o <<= 1) {
+      const int v = tid >= o ? sc[tid - o] : 0;
+      __syncthreads();
+      sc[tid] += v;
+      __syncthreads();
+    }
+    if (tid < G) tile_start[tid] = sc[tid] - nt;
+    if (tid == G - 1) tile_start[G] = sc[tid];
+    if (tid < kCtrSets * kXcds) tile_start[G + 1 + tid] = 0;
+  }
+  if (gamma != 0.0f && tid < E) {
+    const long long diff = kT - static_cast<long long>(E) * tot;
+    const float sgn = diff > 0 ? 1.0f : (diff < 0 ? -1.0f : 0.0f);
+    bias[tid] = bias[tid] + gamma * sgn;
+  }
+}
+
+bool dispatch_is_small(const Shape& s) {
+  return static_cast<long long>(s.T) * s.k <= kDispatchSmallPairs && s.E <= 256 &&
+         s.E + s.S <= 512;
+}
+
+hipError_t launch_dispatch_small(const Shape& s, const int32_t* topk_idx, int32_t* counts,
+                                 int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
+                                 int row_tile, int32_t* tile_start, float gamma, float* bias,
+                                 hipStream_t st) {
+  if (!dispatch_is_small(s)) return hipErrorInvalidValue;
+  dispatch_small<<<1, 512, 0, st>>>(topk_idx, s.T * s.k, s.E, s.capacity, counts, offsets,
+                                    sorted_pair, pair_pos, s.S, s.T, row_tile, tile_start,
+                                    static_cast<long long>(s.k) * s.T, gamma, bias);
+  return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const Shape& s, const int32_t* topk_idx, int32_t* counts,
                            int32_t* offsets, int32_t* sorted_pair, int32_t* pair_pos,
                            int32_t* seg_counts, hipStream_t st) {
+  if (dispatch_is_small(s))
+    return launch_dispatch_small(s, topk_idx, counts, offsets, sorted_pair, pair_pos, 32,
+                                 nullptr, 0.0f, nullptr, st);
   const long long npairs = static_cast<long long>(s.T) * s.k;
   const int nseg = dispatch_segments(s);
   if (nseg > 0) dispatch_count<<<nseg, 256, 0, st>>>(topk_idx, npairs, s.E, seg_counts);

@@ -498,6 +498,8 @@ __global__ __launch_bounds__(256) void shared_reduce_kernel(const float* __restr
   }
 }
 
+int fp4_shared_slices(int K) { return K / 32 < kFp4SharedSlices ? K / 32 : kFp4SharedSlices; }
+
 size_t shared_partial_floats(const Shape& s) {
   if (!s.w_fp4 || !s.bf16 || s.S == 0) return 0;
   const size_t rows = static_cast<size_t>(s.S) * s.T;
@@ -576,7 +578,7 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
     a.counters = ctr + kCtrGateUp * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {  // routed experts in FP4 and the bf16 shared experts, one launch
       if (s.S > 0 && !part) return hipErrorInvalidValue;
-      a.ksplit = s.S > 0 ? (s.d / 32 < kFp4SharedSlices ? s.d / 32 : kFp4SharedSlices) : 0;
+      a.ksplit = s.S > 0 ? fp4_shared_slices(s.d) : 0;
       a.part = part;
       hipError_t e = launch_fp4(a, true, st);
       if (e == hipSuccess && s.S > 0) e = reduce_fp4_shared<true>(a, s, st);
@@ -593,8 +595,10 @@ hipError_t launch_gate_up(const Shape& s, const void* x, const void* wg, const v
 hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const uint8_t* scd,
                        const int32_t* offsets, const int32_t* tile_start, int row_tile,
                        const void* h, void* y_routed, void* y_shared, float* part,
-                       hipEvent_t* marks, hipStream_t st, bool routed_only) {
+                       hipEvent_t* marks, hipStream_t st, bool routed_only,
+                       bool shared_partials) {
   if (s.T == 0) return record_marks(marks, st);
+  if (shared_partials && (!s.w_fp4 || !s.bf16 || s.S == 0)) return hipErrorInvalidValue;
   FfnArgs a{};
   a.sc0 = scd;
   a.a = h;
@@ -620,10 +624,10 @@ hipError_t launch_down(const Shape& s, const void* wd, const void* wsd, const ui
     a.counters = ctr + kCtrDown * kXcds;  // FP4 kernel: static order, no counters
     if (s.w_fp4) {
       if (s.S > 0 && !part) return hipErrorInvalidValue;
-      a.ksplit = s.S > 0 ? (s.F / 32 < kFp4SharedSlices ? s.F / 32 : kFp4SharedSlices) : 0;
+      a.ksplit = s.S > 0 ? fp4_shared_slices(s.F) : 0;
       a.part = part;
       hipError_t e = launch_fp4(a, false, st);
-      if (e == hipSuccess && s.S > 0) e = reduce_fp4_shared<false>(a, s, st);
+      if (e == hipSuccess && s.S > 0 && !shared_partials) e = reduce_fp4_shared<false>(a, s, st);
       return e == hipSuccess ? record_marks(marks, st) : e;
     }
     hipError_t e = run_bf16<32, false>(a, st);

@@ -19,6 +19,15 @@ struct Item {
   int grows;  // rows of the group
 };
 
+// A wave-uniform read of device memory through the scalar data cache: its
+// completion is counted by lgkmcnt, not vmcnt, so using the value does not
+// wait for the wave's vector loads in flight (e.g. direct-to-LDS loads of
+// later K steps).  Reads only.
+typedef const int32_t __attribute__((address_space(4)))* const_scalar_i32;
+__device__ __forceinline__ int32_t sload(const int32_t* base, int idx) {
+  return ((const_scalar_i32)base)[__builtin_amdgcn_readfirstlane(idx)];
+}
+
 // Binary search over tile_start (in LDS), then the item's place in its
 // group.  A group's row tiles are taken in bands of up to kBand tiles; a
 // band's items run column tile outer, row tile inner.  Routed experts at
@@ -188,7 +197,8 @@ inline int big_plan_ints(int G) { return (G + 1) + kCtrSets * kXcds; }
 // tiles in a.ksplit K slices, writing fp32 partials to a.part
 // ([ksplit][S*T][n_tiles*256]) for shared_reduce.
 hipError_t launch_fp4(const FfnArgs& a, bool gated, hipStream_t st);
-// K slices of a shared-expert tile in the FP4 launch.
-constexpr int kFp4SharedSlices = 4;
+// K slices of a shared-expert tile in the FP4 launch (fp4_shared_slices
+// gives fewer when K has fewer than 4 steps of 32).
+constexpr int kFp4SharedSlices = kFp4SharedSlicesMax;
 
 }  // namespace moe

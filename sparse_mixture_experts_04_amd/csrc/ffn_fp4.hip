@@ -206,6 +206,7 @@ __device__ __forceinline__ void fp4_stage(const uint8_t* st, int wn, int lane,
 // stream about as many bytes as an FP4 item (bf16 is 32/17 times the FP4
 // bytes per weight).
 constexpr int kFp4SharedRows = 64;
+constexpr int kFp4MaxGroups = 256 + 2;  // E + S (the descriptor allows E <= 256, S <= 2)
 constexpr int kFp4SharedBK = 32;
 constexpr int kFp4SharedA = kFp4SharedRows * kFp4SharedBK * 2;   // 4 KiB
 constexpr int kFp4SharedB = Fp4Cfg::NB * kFp4SharedBK * 2;      // 16 KiB
@@ -330,23 +331,309 @@ __device__ __forceinline__ void fp4_shared_item(const FfnArgs& p, long long si,
     }
 }
 
-// Routed groups, then (p.ksplit > 0) the shared experts' bf16 tiles.  Persistent workgroups over the items of groups
-// 0..E-1, cut into one contiguous chunk per XCD.  Two workgroups share each
-// CU (a 3-stage ring each, 77 KiB of LDS): every item starts by waiting a
-// full HBM latency for its first stage, and the other workgroup's stream
-// covers that wait (8% faster at T=64 than one workgroup with a 4-stage
-// ring; 5 or 6 stages in one workgroup gain nothing).
+// ------------------------------------------------------- routed items
+
+// What the issuing side needs of a routed item: the item, its group's first
+// row in the expert-sorted order, and the source row of each of the lane's A
+// loads (the token for gate/up, the row of h for down).  The tile plan and
+// the group offsets are in LDS and the gate/up token rows are read with
+// sload, so building it does not wait for the direct loads in flight.
+struct Fp4Meta {
+  Item item;
+  int row_base;
+  int src_row[Fp4Cfg::A_LOADS];
+};
+
+template <bool GATED>
+__device__ __forceinline__ Fp4Meta fp4_meta(const FfnArgs& p, const int* ts, const int* ofs,
+                                            long long it, int wave, int lane) {
+  using C = Fp4Cfg;
+  Fp4Meta m;
+  const Item d = decode_item(it, ts, p.E + p.S, p.n_tiles, C::MT, ofs, p.T, p.E);
+  m.item.g = __builtin_amdgcn_readfirstlane(d.g);
+  m.item.m0 = __builtin_amdgcn_readfirstlane(d.m0);
+  m.item.rows = __builtin_amdgcn_readfirstlane(d.rows);
+  m.item.n = __builtin_amdgcn_readfirstlane(d.n);
+  m.item.grows = __builtin_amdgcn_readfirstlane(d.grows);
+  m.row_base = __builtin_amdgcn_readfirstlane(ofs[m.item.g]);
+  // A load j fills rows 4j..4j+3 (lane l: row 4j + l/16), clamped to the
+  // tile's last row
+  const int sel = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < C::A_LOADS; ++q) {
+    const int j = wave * C::A_LOADS + q;
+    if (GATED) {
+      int v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * j + u < m.item.rows ? 4 * j + u : m.item.rows - 1;
+        v[u] = sload(p.sorted_pair, m.row_base + m.item.m0 + r) / p.k;
+      }
+      m.src_row[q] = sel == 0 ? v[0] : sel == 1 ? v[1] : sel == 2 ? v[2] : v[3];
+    } else {
+      const int r = 4 * j + sel < m.item.rows ? 4 * j + sel : m.item.rows - 1;
+      m.src_row[q] = m.row_base + m.item.m0 + r;
+    }
+  }
+  return m;
+}
+
+// Load sources of an item (see Fp4Ctx).
+template <bool GATED>
+__device__ __forceinline__ Fp4Ctx fp4_ctx(const FfnArgs& p, const Fp4Meta& m, int wave,
+                                          int lane) {
+  using C = Fp4Cfg;
+  const Item& item = m.item;
+  Fp4Ctx t;
+  {
+    const int left = item.rows - 4 * wave * C::A_LOADS;   // rows from this wave's first group
+    const int groups = left <= 0 ? 0 : (left + 3) / 4;
+    t.na = groups < C::A_LOADS ? groups : C::A_LOADS;
+  }
+  const bf16_t* A = static_cast<const bf16_t*>(p.a);
+  const int arow = lane >> 4;
+#pragma unroll
+  for (int q = 0; q < C::A_LOADS; ++q) {
+    const int rc = 4 * (wave * C::A_LOADS + q) + arow;
+    t.a_src[q] = A + static_cast<size_t>(m.src_row[q]) * p.K + (((lane & 15) ^ (rc & 15)) << 3);
+  }
+  // code load j fills rows 16j..16j+15: lane l -> row 16j + l/4, slot l%4,
+  // source chunk (l%4) ^ ((row >> 2) & 3)
+  const int crow = lane >> 2;
+  const int g = item.g;
+  const size_t cstride = static_cast<size_t>(p.N) * (p.K / 2);   // bytes per expert
+  const size_t sstride_e = static_cast<size_t>(p.K / 32) * p.N;
+#pragma unroll
+  for (int q = 0; q < C::C_LOADS; ++q) {
+    const int j = wave * C::C_LOADS + q;
+    const int R = 16 * j + crow;  // LDS B row
+    int col;
+    const uint8_t* base;
+    if (GATED) {
+      const int cg = R >> 6, rl = R & 63;
+      base = static_cast<const uint8_t*>(rl >= 32 ? p.w1 : p.w0);
+      col = item.n * (C::NB / 2) + cg * 32 + (rl & 31);
+    } else {
+      base = static_cast<const uint8_t*>(p.w0);
+      col = item.n * C::NB + R;
+    }
+    t.c_src[q] = base + g * cstride + static_cast<size_t>(col) * (p.K / 2) +
+                 (((lane & 3) ^ ((R >> 2) & 3)) << 4);
+  }
+  {
+    // scale load of K block 4kt + wave: LDS bytes 4l..4l+3 = rows 4l..4l+3
+    const int R = 4 * lane;
+    int col;
+    const uint8_t* sbase;
+    if (GATED) {
+      const int cg = R >> 6, rl = R & 63;
+      sbase = rl >= 32 ? p.sc1 : p.sc0;
+      col = item.n * (C::NB / 2) + cg * 32 + (rl & 31);
+    } else {
+      sbase = p.sc0;
+      col = item.n * C::NB + R;
+    }
+    t.s_src = sbase + g * sstride_e + static_cast<size_t>(wave) * p.N + col;
+  }
+  return t;
+}
+
+// An item's outputs as bf16, packed two per register.  32x32 accumulator
+// layout: lane l holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4.
+// GATED: SwiGLU of the gate (acc[0]) and up (acc[1]) columns, 16 values;
+// down: both column blocks, 32 values.
+struct Fp4Out {
+  uint32_t w[16];
+};
+
+template <bool GATED>
+__device__ __forceinline__ void fp4_pack(const f32x16_t (&acc)[2], Fp4Out& o) {
+  if (GATED) {
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      float v[2];
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const float gt = acc[0][r + e];
+        const float up = acc[1][r + e];
+        v[e] = gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up;
+      }
+      o.w[r / 2] = static_cast<uint32_t>(f32_to_bf16(v[0])) |
+                   (static_cast<uint32_t>(f32_to_bf16(v[1])) << 16);
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        o.w[8 * j + r / 2] = static_cast<uint32_t>(f32_to_bf16(acc[j][r])) |
+                             (static_cast<uint32_t>(f32_to_bf16(acc[j][r + 1])) << 16);
+  }
+}
+
+template <bool GATED>
+__device__ __forceinline__ void fp4_store(const FfnArgs& p, const Item& item, int row_base,
+                                          int wave, int lane, const Fp4Out& o) {
+  using C = Fp4Cfg;
+  bf16_t* out = static_cast<bf16_t*>(p.out_routed);
+  const size_t orow0 = static_cast<size_t>(row_base) + item.m0;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+    if (row >= item.rows) continue;
+    bf16_t* orow = out + (orow0 + row) * p.ldo;
+    if (GATED) {
+      const uint32_t w = o.w[r / 2];
+      orow[item.n * (C::NB / 2) + wave * 32 + (lane & 31)] =
+          static_cast<bf16_t>((r & 1) ? (w >> 16) : (w & 0xffffu));
+    } else {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t w = o.w[8 * j + r / 2];
+        orow[item.n * C::NB + wave * 64 + j * 32 + (lane & 31)] =
+            static_cast<bf16_t>((r & 1) ? (w >> 16) : (w & 0xffffu));
+      }
+    }
+  }
+}
+
+// s_waitcnt vmcnt(n) for the n loads this wave issued after the stage waited
+// for (one stage: the C + 1 code and scale loads and 0..A_LOADS A loads).
+__device__ __forceinline__ void fp4_wait_stage(int n) {
+  using C = Fp4Cfg;
+  static_assert(C::A_LOADS == 2, "wait cases");
+  if (n == C::LPW) wait_vm<C::LPW>();
+  else if (n == C::LPW - 1) wait_vm<C::LPW - 1>();
+  else wait_vm<C::LPW - 2>();
+}
+
+// The routed items first, first + stride, ... (< nr) of the list beg + i,
+// with the ring run as one stream across items: the last two K steps of an
+// item issue the first two stages of the next one, so a new item does not
+// start by waiting a full HBM latency for its first stage.  An item's
+// outputs are stored after the next item's first wait: a store counts in
+// vmcnt like a load, and stores issued behind the next item's first stages
+// would make that wait cover them too.  Needs nk >= 3 (the next item's
+// metadata is read at the end of K step 0 and used at step nk - 2).
+template <bool GATED>
+__device__ __forceinline__ void fp4_routed_stream(const FfnArgs& p, const int* ts, const int* ofs,
+                                                  long long beg, long long nr, long long first,
+                                                  int stride, const uint8_t* ring,
+                                                  uint32_t ring_base, int wave, int lane) {
+  using C = Fp4Cfg;
+  const int nk = p.K / C::BK;
+  long long ic = first;
+  Fp4Meta cur = fp4_meta<GATED>(p, ts, ofs, beg + ic, wave, lane);
+  Fp4Ctx t = fp4_ctx<GATED>(p, cur, wave, lane);
+  // every wave is done with the ring before it is refilled
+  wait_vm<0>();
+  lds_barrier();
+  t.issue(0, ring_base, wave, p.N);
+  t.issue(1, ring_base + C::STAGE, wave, p.N);
+  int pend = t.na + C::C_LOADS + 1;  // loads of the last stage issued
+  int sc = 0;                        // ring slot of the next stage computed
+  int si = 2;                        // ring slot of the next stage issued
+  Fp4Meta nxt = cur;
+  bool more = false;
+
+  // K step kt of the current item: wait for its stage, issue the stage two
+  // ahead (of this item, else of the next, else a repeat of the last one,
+  // which keeps the wait counts uniform), compute
+  Fp4Out prev;
+  Item prev_item = cur.item;
+  int prev_base = cur.row_base;
+  auto step = [&](int kt, f32x16_t (&acc)[2], bool store_prev) {
+    fp4_wait_stage(pend);
+    lds_barrier();
+    if (store_prev) fp4_store<GATED>(p, prev_item, prev_base, wave, lane, prev);
+    const int s2 = kt + C::NS - 1;
+    if (s2 < nk) {
+      t.issue(s2, ring_base + si * C::STAGE, wave, p.N);
+    } else if (more) {
+      if (s2 == nk) t = fp4_ctx<GATED>(p, nxt, wave, lane);
+      t.issue(s2 - nk, ring_base + si * C::STAGE, wave, p.N);
+    } else {
+      t.issue(nk - 1, ring_base + si * C::STAGE, wave, p.N);
+    }
+    pend = t.na + C::C_LOADS + 1;
+    si = si == C::NS - 1 ? 0 : si + 1;
+    fp4_stage(ring + sc * C::STAGE, wave, lane, acc);
+    sc = sc == C::NS - 1 ? 0 : sc + 1;
+  };
+
+  bool held = false;
+  for (;;) {
+    const long long in = ic + stride;
+    more = in < nr;
+    f32x16_t acc[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+    step(0, acc, held);
+    if (more) nxt = fp4_meta<GATED>(p, ts, ofs, beg + in, wave, lane);
+    for (int kt = 1; kt < nk; ++kt) step(kt, acc, false);
+    fp4_pack<GATED>(acc, prev);
+    prev_item = cur.item;
+    prev_base = cur.row_base;
+    if (!more) break;
+    held = true;
+    cur = nxt;
+    ic = in;
+  }
+  fp4_store<GATED>(p, prev_item, prev_base, wave, lane, prev);
+}
+
+// One routed item with its own pipeline fill (items of fewer than 3 K steps).
+template <bool GATED>
+__device__ __forceinline__ void fp4_routed_item(const FfnArgs& p, const int* ts, const int* ofs,
+                                                long long it, const uint8_t* ring,
+                                                uint32_t ring_base, int wave, int lane) {
+  using C = Fp4Cfg;
+  const int nk = p.K / C::BK;
+  const Fp4Meta m = fp4_meta<GATED>(p, ts, ofs, it, wave, lane);
+  const Fp4Ctx t = fp4_ctx<GATED>(p, m, wave, lane);
+  f32x16_t acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
+  // every wave is done with the previous item's LDS before refilling it
+  wait_vm<0>();
+  lds_barrier();
+#pragma unroll
+  for (int s = 0; s < C::NS - 1; ++s)
+    t.issue(s < nk ? s : nk - 1, ring_base + s * C::STAGE, wave, p.N);
+  for (int kt = 0; kt < nk; ++kt) {
+    fp4_wait_stage(t.na + C::C_LOADS + 1);
+    lds_barrier();
+    const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
+    t.issue(kn, ring_base + ((kt + C::NS - 1) % C::NS) * C::STAGE, wave, p.N);
+    fp4_stage(ring + (kt % C::NS) * C::STAGE, wave, lane, acc);
+  }
+  Fp4Out o;
+  fp4_pack<GATED>(acc, o);
+  fp4_store<GATED>(p, m.item, m.row_base, wave, lane, o);
+}
+
+// Routed groups, then (p.ksplit > 0) the shared experts' bf16 tiles.
+// Persistent workgroups over the items, cut into one contiguous chunk per
+// XCD; workgroup slot s of an XCD takes items s, s + 64, ... of its chunk
+// (routed first).  Two workgroups share each CU (a 3-stage ring each, 77 KiB
+// of LDS), so one's stream covers the other's pipeline fills.
 template <bool GATED>
 __global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
   using C = Fp4Cfg;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[C::NS * C::STAGE];
-  __shared__ int ts[512];
+  __shared__ int ts[kFp4MaxGroups + 1];   // tile plan
+  __shared__ int ofs[kFp4MaxGroups + 1];  // group offsets of the routed rows
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = p.E + p.S;
   for (int g = tid; g <= G; g += 256) ts[g] = p.tile_start[g];
+  for (int g = tid; g <= p.E; g += 256) ofs[g] = p.offsets[g];
   __syncthreads();
 
   // routed items, then the shared items; each XCD takes a contiguous chunk
@@ -365,124 +652,23 @@ __global__ __launch_bounds__(256, 2) void ffn_fp4_kernel(FfnArgs p) {
   const long long schunk = (shared + 7) / 8;
   const long long sbeg = xcd * schunk < shared ? xcd * schunk : shared;
   const long long send = sbeg + schunk < shared ? sbeg + schunk : shared;
-  const long long nitems = (end - beg) + (send - sbeg);
-
-  const bf16_t* A = static_cast<const bf16_t*>(p.a);
+  const long long nr = end - beg;
+  const long long nitems = nr + (send - sbeg);
   const uint32_t ring_base = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(LDS_PTR(ring)));
-  const int nk = p.K / C::BK;
-  const int kb_per_row = p.K / 32;
-  // A load j fills rows 4j..4j+3: lane l -> row 4j + l/16, slot l%16,
-  // source chunk (l%16) ^ (row & 15)
-  const int arow = lane >> 4;
-  // code load j fills rows 16j..16j+15: lane l -> row 16j + l/4, slot l%4,
-  // source chunk (l%4) ^ ((row >> 2) & 3)
-  const int crow = lane >> 2;
 
-  for (long long i = slot_id; i < nitems; i += per_xcd) {
-    if (i >= end - beg) {
-      fp4_shared_item<GATED>(p, sbeg + (i - (end - beg)), ring, ring_base, wave, lane);
-      continue;
-    }
-    const long long it = beg + i;
-    const Item item = decode_item(it, ts, G, p.n_tiles, C::MT, p.offsets, p.T, p.E);
-    const int g = item.g;  // routed
-    const size_t row_base = static_cast<size_t>(p.offsets[g]);
-    Fp4Ctx t;
-    {
-      const int left = item.rows - 4 * wave * C::A_LOADS;   // rows from this wave's first group
-      const int groups = left <= 0 ? 0 : (left + 3) / 4;
-      t.na = groups < C::A_LOADS ? groups : C::A_LOADS;
-    }
-#pragma unroll
-    for (int q = 0; q < C::A_LOADS; ++q) {
-      const int j = wave * C::A_LOADS + q;
-      int r = 4 * j + arow;
-      const int rc = r;
-      r = r < item.rows ? r : item.rows - 1;
-      const int rr = item.m0 + r;
-      const size_t src_row = GATED ? static_cast<size_t>(p.sorted_pair[row_base + rr] / p.k)
-                                   : row_base + rr;
-      t.a_src[q] = A + src_row * p.K + (((lane & 15) ^ (rc & 15)) << 3);
-    }
-    const size_t cstride = static_cast<size_t>(p.N) * (p.K / 2);   // bytes per expert
-    const size_t sstride_e = static_cast<size_t>(kb_per_row) * p.N;
-#pragma unroll
-    for (int q = 0; q < C::C_LOADS; ++q) {
-      const int j = wave * C::C_LOADS + q;
-      const int R = 16 * j + crow;  // LDS B row
-      int col;
-      const uint8_t* base;
-      if (GATED) {
-        const int cg = R >> 6, rl = R & 63;
-        base = static_cast<const uint8_t*>(rl >= 32 ? p.w1 : p.w0);
-        col = item.n * (C::NB / 2) + cg * 32 + (rl & 31);
-      } else {
-        base = static_cast<const uint8_t*>(p.w0);
-        col = item.n * C::NB + R;
-      }
-      t.c_src[q] = base + g * cstride + static_cast<size_t>(col) * (p.K / 2) +
-                   (((lane & 3) ^ ((R >> 2) & 3)) << 4);
-    }
-    {
-      // scale load of K block 4kt + wave: LDS bytes 4l..4l+3 = rows 4l..4l+3
-      const int R = 4 * lane;
-      int col;
-      const uint8_t* sbase;
-      if (GATED) {
-        const int cg = R >> 6, rl = R & 63;
-        sbase = rl >= 32 ? p.sc1 : p.sc0;
-        col = item.n * (C::NB / 2) + cg * 32 + (rl & 31);
-      } else {
-        sbase = p.sc0;
-        col = item.n * C::NB + R;
-      }
-      t.s_src = sbase + g * sstride_e + static_cast<size_t>(wave) * p.N + col;
-    }
-
-    f32x16_t acc[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[j][r] = 0.0f;
-
-    // every wave is done with the previous item's LDS before refilling it
-    wait_vm<0>();
-    lds_barrier();
-#pragma unroll
-    for (int s = 0; s < C::NS - 1; ++s)
-      t.issue(s < nk ? s : nk - 1, ring_base + s * C::STAGE, wave, p.N);
-    static_assert(C::NS == 3 && C::A_LOADS == 2, "wait cases");
-    for (int kt = 0; kt < nk; ++kt) {
-      if (t.na == 2) wait_vm<C::LPW>();
-      else if (t.na == 1) wait_vm<C::LPW - 1>();
-      else wait_vm<C::LPW - 2>();
-      lds_barrier();
-      const int kn = kt + C::NS - 1 < nk ? kt + C::NS - 1 : nk - 1;
-      t.issue(kn, ring_base + ((kt + C::NS - 1) % C::NS) * C::STAGE, wave, p.N);
-      fp4_stage(ring + (kt % C::NS) * C::STAGE, wave, lane, acc);
-    }
-
-    // ---- epilogue.  32x32 accumulator layout: lane l holds column l%32 and
-    // rows 8*(r/4) + 4*(l/32) + r%4 for r = 0..15.
-    bf16_t* out = static_cast<bf16_t*>(p.out_routed);
-    const size_t orow0 = static_cast<size_t>(p.offsets[g]) + item.m0;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (row >= item.rows) continue;
-      bf16_t* orow = out + (orow0 + row) * p.ldo;
-      if (GATED) {
-        const float gt = acc[0][r];
-        const float up = acc[1][r];
-        orow[item.n * (C::NB / 2) + wave * 32 + (lane & 31)] =
-            f32_to_bf16(gt * __builtin_amdgcn_rcpf(1.0f + __expf(-gt)) * up);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          orow[item.n * C::NB + wave * 64 + j * 32 + (lane & 31)] = f32_to_bf16(acc[j][r]);
-      }
+  long long i = slot_id;
+  if (i < nr) {
+    if (p.K / C::BK >= 3) {
+      fp4_routed_stream<GATED>(p, ts, ofs, beg, nr, i, per_xcd, ring, ring_base, wave, lane);
+      i += (nr - i + per_xcd - 1) / per_xcd * per_xcd;   // first index past the routed items
+    } else {
+      for (; i < nr; i += per_xcd)
+        fp4_routed_item<GATED>(p, ts, ofs, beg + i, ring, ring_base, wave, lane);
     }
   }
+  for (; i < nitems; i += per_xcd)
+    fp4_shared_item<GATED>(p, sbeg + (i - nr), ring, ring_base, wave, lane);
+  wait_vm<0>();  // no direct load may still be landing in LDS when the workgroup ends
 }
 
 hipError_t launch_fp4(const FfnArgs& a, bool gated, hipStream_t st) {

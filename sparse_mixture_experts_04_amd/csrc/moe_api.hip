@@ -391,7 +391,9 @@ namespace {
 
 // moe_forward's launches; marks (7 events, or NULL) are recorded after the
 // router, the dispatch, the tile plan, the gate/up GEMM, the down GEMM, the
-// combine and the bias update.  With the fused shared-expert down + combine
+// combine and the bias update.  Small batches with 32-row tiles make the
+// tile plan and the bias update in the dispatch launch (their marks then
+// follow the dispatch and the combine).  With the fused shared-expert down + combine
 // (large batches with shared experts) the down mark follows the routed
 // experts' down GEMM and the combine mark the fused launch.
 moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* w, float* bias,
@@ -427,10 +429,19 @@ moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* 
                                margin, f.router.planes, f.router.partial, f.router.refine,
                                stream);
   e = mark(0, e);
-  if (e == hipSuccess)
-    e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg, stream);
+  // small batches with 32-row tiles: dispatch, tile plan and bias update in
+  // one launch (the bias has been read by the router)
+  const bool small = mt == 32 && dispatch_is_small(s);
+  if (e == hipSuccess) {
+    if (small)
+      e = launch_dispatch_small(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, mt,
+                                f.plan, gamma, bias, stream);
+    else
+      e = launch_dispatch(s, f.topk, f.counts, f.offsets, f.sorted_pair, f.pair_pos, f.seg,
+                          stream);
+  }
   e = mark(1, e);
-  if (e == hipSuccess) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
+  if (e == hipSuccess && !small) e = launch_tile_plan(s, f.offsets, mt, f.plan, stream);
   e = mark(2, e);
   // Large batches (256-row tiles) with shared experts: the shared experts'
   // down GEMM runs after the routed one, fused with the combine (their rows
@@ -442,18 +453,25 @@ moe_status forward_impl(const moe_desc* desc, const void* x, const moe_weights* 
     e = launch_gate_up(s, x, w->w_gate, w->w_up, w->ws_gate, w->ws_up, w->sc_gate, w->sc_up,
                        f.offsets, f.sorted_pair, f.plan, mt, f.h, f.part,
                        marks ? marks + 3 : nullptr, stream, fused ? f.gates : nullptr);
+  // FP4 routed weights with shared experts: the combine sums the shared
+  // experts' K-slice partials itself
+  const bool fp4_part = s.w_fp4 && s.bf16 && s.S > 0 && mt == 32;
   if (e == hipSuccess)
     e = launch_down(s, w->w_down, w->ws_down, w->sc_down, f.offsets, f.plan, mt, f.h, f.y_routed,
-                    f.y_shared, f.part, marks ? marks + 4 : nullptr, stream, fused);
+                    f.y_shared, f.part, marks ? marks + 4 : nullptr, stream, fused, fp4_part);
   if (e == hipSuccess) {
     if (fused)
       e = launch_shared_combine(s, w->ws_down, f.plan, mt, f.h, f.y_routed, f.gates,
                                 f.pair_pos, y, stream);
+    else if (fp4_part)
+      e = launch_combine_part(s, f.y_routed, f.part, fp4_shared_slices(s.F), f.gates,
+                              f.pair_pos, y, stream);
     else
       e = launch_combine(s, f.y_routed, f.y_shared, f.gates, f.pair_pos, y, stream);
   }
   e = mark(5, e);
-  if (e == hipSuccess && gamma != 0.0f) e = launch_bias_update(s, f.counts, gamma, bias, stream);
+  if (e == hipSuccess && !small && gamma != 0.0f)
+    e = launch_bias_update(s, f.counts, gamma, bias, stream);
   e = mark(6, e);
   return hip_status(e);
 }

@@ -555,29 +555,26 @@ __device__ __forceinline__ void write_token(int t, int lane, const int (&i_sel)[
 
 __device__ __forceinline__ double sigmoid64(double z) { return 1.0 / (1.0 + exp(-z)); }
 
-// Keys of token t from the matrix-core logits (sum of the K-split partials):
-// lane l holds routed experts l + 64q.
-// z_sh: shared expert E + lane's logit on lanes < S (0 elsewhere).  The
-// partials of a group of 4 splits are loaded for all of the lane's experts
-// before any is added (at T=64 K is split 28 ways, and a load at a time
-// per expert would cost a round trip each); each logit still adds its
-// splits in split order.
-template <int EPL, int S>
-__device__ __forceinline__ void token_keys(const double* __restrict__ partial, int nks, int T,
-                                           int npad, int E, int t, int lane,
-                                           const float* __restrict__ bias, double (&zv)[EPL],
-                                           double (&sv)[EPL], double (&key)[EPL],
-                                           double& z_sh) {
+// Logits of token t from the matrix-core partials of K splits kb..ke-1,
+// added in split order: lane l gets routed experts l + 64q (zv) and, on
+// lanes < S, shared expert E + lane (z_sh; 0 elsewhere).  The partials of
+// a group of G splits are loaded for all of the lane's experts before any
+// is added (at T=64 K is split 28 ways, and a load at a time per expert
+// would cost a round trip each).
+template <int EPL, int S, int G>
+__device__ __forceinline__ void token_logits(const double* __restrict__ partial, int kb, int ke,
+                                             int T, int npad, int E, int t, int lane,
+                                             double (&zv)[EPL], double& z_sh) {
   const size_t kstride = static_cast<size_t>(T) * npad;
   const double* row = partial + static_cast<size_t>(t) * npad;
 #pragma unroll
   for (int q = 0; q < EPL; ++q) zv[q] = 0.0;
   z_sh = 0.0;
-  for (int ks = 0; ks < nks; ks += 4) {
-    double v[4][EPL], vs[4];
+  for (int ks = kb; ks < ke; ks += G) {
+    double v[G][EPL], vs[G];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (ks + j < nks) {
+    for (int j = 0; j < G; ++j) {
+      if (ks + j < ke) {
         const double* r = row + static_cast<size_t>(ks + j) * kstride;
 #pragma unroll
         for (int q = 0; q < EPL; ++q) v[j][q] = r[lane + 64 * q];
@@ -585,20 +582,38 @@ __device__ __forceinline__ void token_keys(const double* __restrict__ partial, i
       }
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      if (ks + j < nks) {
+    for (int j = 0; j < G; ++j) {
+      if (ks + j < ke) {
 #pragma unroll
         for (int q = 0; q < EPL; ++q) zv[q] += v[j][q];
         z_sh += vs[j];
       }
     }
   }
+}
+
+// Affinities s = sigmoid(z) and selection keys s + b of the lane's experts.
+template <int EPL>
+__device__ __forceinline__ void token_keys_from(const double (&zv)[EPL], int lane,
+                                                const float* __restrict__ bias,
+                                                double (&sv)[EPL], double (&key)[EPL]) {
 #pragma unroll
   for (int q = 0; q < EPL; ++q) {
     const int e = lane + 64 * q;
     sv[q] = sigmoid64(zv[q]);
     key[q] = sv[q] + static_cast<double>(bias[e]);
   }
+}
+
+// Keys of token t from all nks splits, one wave.
+template <int EPL, int S>
+__device__ __forceinline__ void token_keys(const double* __restrict__ partial, int nks, int T,
+                                           int npad, int E, int t, int lane,
+                                           const float* __restrict__ bias, double (&zv)[EPL],
+                                           double (&sv)[EPL], double (&key)[EPL],
+                                           double& z_sh) {
+  token_logits<EPL, S, 4>(partial, 0, nks, T, npad, E, t, lane, zv, z_sh);
+  token_keys_from<EPL>(zv, lane, bias, sv, key);
 }
 
 // One wave per token, from the matrix-core logits.  Their error (the
@@ -608,18 +623,45 @@ __device__ __forceinline__ void token_keys(const double* __restrict__ partial, i
 // therefore appended to `refine` (count at refine[0], tokens from refine[1];
 // the list's order does not matter), and router_refine redoes it from
 // exact logits; the outputs written here stand for every other token.
-template <int K, int S, int EPL>
+//
+// WPT = 1: four tokens per workgroup, a wave each.  WPT = 4 (many K splits):
+// one token per workgroup; wave w adds splits w*nks/4 .. (w+1)*nks/4 - 1 in
+// one round of loads, and wave 0 adds the four sums in wave order and
+// selects.
+template <int K, int S, int EPL, int WPT>
 __global__ __launch_bounds__(256) void router_select(
     const double* __restrict__ partial, int nks, int T, int npad, int E,
     const float* __restrict__ bias, int32_t* __restrict__ topk, float* __restrict__ gates,
     float* __restrict__ margin, bool logsumexp_norm, double gate_scale,
     int32_t* __restrict__ refine) {
+  static_assert(WPT == 1 || WPT == 4, "waves per token");
   const int lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T) return;  // whole wave leaves together; no block barrier below
+  const int wave = threadIdx.x >> 6;
+  const int t = WPT == 1 ? blockIdx.x * 4 + wave : blockIdx.x;
+  if (t >= T) return;  // whole wave (WPT 1) or workgroup (WPT 4) leaves together
 
   double zv[EPL], sv[EPL], key[EPL], z_sh;
-  token_keys<EPL, S>(partial, nks, T, npad, E, t, lane, bias, zv, sv, key, z_sh);
+  if constexpr (WPT == 1) {
+    token_keys<EPL, S>(partial, nks, T, npad, E, t, lane, bias, zv, sv, key, z_sh);
+  } else {
+    __shared__ double part_sum[WPT - 1][EPL + 1][64];
+    token_logits<EPL, S, 8>(partial, wave * nks / WPT, (wave + 1) * nks / WPT, T, npad, E, t,
+                            lane, zv, z_sh);
+    if (wave > 0) {
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) part_sum[wave - 1][q][lane] = zv[q];
+      part_sum[wave - 1][EPL][lane] = z_sh;
+    }
+    __syncthreads();
+    if (wave > 0) return;
+#pragma unroll
+    for (int w = 0; w < WPT - 1; ++w) {
+#pragma unroll
+      for (int q = 0; q < EPL; ++q) zv[q] += part_sum[w][q][lane];
+      z_sh += part_sum[w][EPL][lane];
+    }
+    token_keys_from<EPL>(zv, lane, bias, sv, key);
+  }
   bool valid[EPL];
 #pragma unroll
   for (int q = 0; q < EPL; ++q) valid[q] = true;
@@ -863,9 +905,14 @@ constexpr int kRefineGrid = 256;
 
 template <int S, int EPL>
 static void launch_select(const Shape& s, const SelectArgs& a, hipStream_t st) {
-  router_select<6, S, EPL><<<(s.T + 3) / 4, 256, 0, st>>>(
-      a.partial, a.nks, s.T, a.npad, s.E, a.bias, a.topk_idx, a.gates, a.margin,
-      s.gate_logsumexp, s.gate_scale, a.refine);
+  if (a.nks > 8)  // many splits (small batches): one round of loads per wave
+    router_select<6, S, EPL, 4><<<s.T, 256, 0, st>>>(
+        a.partial, a.nks, s.T, a.npad, s.E, a.bias, a.topk_idx, a.gates, a.margin,
+        s.gate_logsumexp, s.gate_scale, a.refine);
+  else
+    router_select<6, S, EPL, 1><<<(s.T + 3) / 4, 256, 0, st>>>(
+        a.partial, a.nks, s.T, a.npad, s.E, a.bias, a.topk_idx, a.gates, a.margin,
+        s.gate_logsumexp, s.gate_scale, a.refine);
   router_refine<6, S, EPL><<<s.T < kRefineGrid ? s.T : kRefineGrid, 512, 0, st>>>(
       a.partial, a.nks, s.T, a.npad, s.E, s.d, a.x, s.bf16, a.w_router, a.refine, a.bias,
       a.topk_idx, a.gates, a.margin, s.gate_logsumexp, s.gate_scale);
