@@ -151,15 +151,11 @@ struct Fp4Ctx {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
-// B fragment of substep kk for column block j of wave wn: lane l holds the
-// 8 values k = 16kk + 8(l/32) .. of weight row 64wn + 32j + l%32.
-__device__ __forceinline__ bf16x8_t fp4_frag(const uint8_t* st, int row, int kk, int half) {
-  using C = Fp4Cfg;
-  const int chunk = (kk >> 1) ^ ((row >> 2) & 3);   // 16-byte chunk holding bytes 8kk..
-  const uint32_t word = *reinterpret_cast<const uint32_t*>(
-      st + C::A_BYTES + row * 64 + chunk * 16 + (kk & 1) * 8 + half * 4);
-  const uint32_t sb = st[C::A_BYTES + C::C_BYTES + (kk >> 1) * 256 + row];
-  const float scale = __uint_as_float(sb == 0 ? 0x00400000u : sb << 23);  // 2^(sb-127)
+// B fragment from 4 code bytes (8 values) and their block's scale byte:
+// converted to bf16 with the scale applied (2^(sb-127); sb = 0 is 2^-127,
+// a subnormal float).
+__device__ __forceinline__ bf16x8_t fp4_frag(uint32_t word, uint32_t sb) {
+  const float scale = __uint_as_float(sb == 0 ? 0x00400000u : sb << 23);
   const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 0);
   const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 1);
   const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, scale, 2);
@@ -170,21 +166,44 @@ __device__ __forceinline__ bf16x8_t fp4_frag(const uint8_t* st, int row, int kk,
   return r;
 }
 
+// One K step of a wave: every LDS read of the stage is issued first (8 A
+// fragments, and for each of the wave's two column blocks 8 code words and
+// 4 scale bytes), so their latencies overlap; then the conversions and
+// MFMAs.  B fragment of substep kk for column block j of wave wn: lane l
+// holds the 8 values k = 16kk + 8(l/32) .. of weight row 64wn + 32j + l%32.
 __device__ __forceinline__ void fp4_stage(const uint8_t* st, int wn, int lane,
                                           f32x16_t (&acc)[2]) {
+  using C = Fp4Cfg;
+  constexpr int KK = C::BK / 16;
   const int r32 = lane & 31;
   const int half = lane >> 5;
   const bf16_t* sa = reinterpret_cast<const bf16_t*>(st);
+  bf16x8_t a[KK];
+  uint32_t word[2][KK];
+  uint32_t sb[2][KK / 2];
 #pragma unroll
-  for (int kk = 0; kk < Fp4Cfg::BK / 16; ++kk) {
+  for (int kk = 0; kk < KK; ++kk) {
     const int c = 2 * kk + half;  // 16-byte chunk of the A row
-    const bf16x8_t a = *reinterpret_cast<const bf16x8_t*>(sa + r32 * 128 + ((c ^ (r32 & 15)) << 3));
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8_t b = fp4_frag(st, wn * 64 + j * 32 + r32, kk, half);
-      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
-    }
+    a[kk] = *reinterpret_cast<const bf16x8_t*>(sa + r32 * 128 + ((c ^ (r32 & 15)) << 3));
   }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int row = wn * 64 + j * 32 + r32;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int chunk = (kk >> 1) ^ ((row >> 2) & 3);   // 16-byte chunk holding bytes 8kk..
+      word[j][kk] = *reinterpret_cast<const uint32_t*>(
+          st + C::A_BYTES + row * 64 + chunk * 16 + (kk & 1) * 8 + half * 4);
+    }
+#pragma unroll
+    for (int m = 0; m < KK / 2; ++m) sb[j][m] = st[C::A_BYTES + C::C_BYTES + m * 256 + row];
+  }
+#pragma unroll
+  for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kk], fp4_frag(word[j][kk], sb[j][kk >> 1]),
+                                                       acc[j], 0, 0, 0);
 }
 
 // ------------------------------------------- shared experts in the launch
