@@ -198,6 +198,7 @@ __device__ __forceinline__ void fp4_stage(const uint8_t* st, int wn, int lane,
 #pragma unroll
     for (int m = 0; m < KK / 2; ++m) sb[j][m] = st[C::A_BYTES + C::C_BYTES + m * 256 + row];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the first conversion
 #pragma unroll
   for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
