@@ -132,12 +132,12 @@ struct BigFrags {
 // Fragment reads.  Rows of a 32-row block differ only above bit 4, so the
 // swizzle depends only on the lane's row inside the block: one per-lane
 // offset per substep (`off[kk]`, in elements) plus a compile-time block
-// offset addresses every fragment.  `nv` (wave-uniform) is the number of
-// this wave's row blocks that hold rows of the tile.
-template <class C>
-__device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* sB, int grp,
-                                               int wn, int nv, const int (&off)[C::KK],
-                                               BigFrags<C>& f) {
+// offset addresses every fragment.  NV is the number of this wave's row
+// blocks that hold rows of the tile (a compile-time count, so that the
+// reads and MFMAs of a step are straight-line code).
+template <class C, int GRP, int NV>
+__device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* sB, int wn,
+                                               const int (&off)[C::KK], BigFrags<C>& f) {
   constexpr int BLK = 32 * C::BK;  // elements of a 32-row block
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk) {
@@ -146,9 +146,8 @@ __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* s
       f.b[kk][j] =
           *reinterpret_cast<const bf16x8_t*>(sB + (wn * 2 + j) * BLK + off[kk]);
 #pragma unroll
-    for (int i = 0; i < C::BM; ++i)
-      if (i < nv)
-        f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + grp) * BLK + off[kk]);
+    for (int i = 0; i < NV; ++i)
+      f.a[kk][i] = *reinterpret_cast<const bf16x8_t*>(sA + (2 * i + GRP) * BLK + off[kk]);
   }
 }
 
@@ -156,14 +155,12 @@ __device__ __forceinline__ void big_read_frags(const bf16_t* sA, const bf16_t* s
 // is the transposed product (output columns down the lane's registers, tile
 // rows across lanes): a lane then holds 4 consecutive output columns of one
 // row, which the epilogue writes as one 8-byte word.
-template <class C>
-__device__ __forceinline__ void big_mfma(const BigFrags<C>& f, int nv,
-                                         f32x16_t (&acc)[C::BM][C::BN]) {
+template <class C, int NV>
+__device__ __forceinline__ void big_mfma(const BigFrags<C>& f, f32x16_t (&acc)[C::BM][C::BN]) {
 #pragma unroll
   for (int kk = 0; kk < C::KK; ++kk)
 #pragma unroll
-    for (int i = 0; i < C::BM; ++i)
-      if (i < nv)
+    for (int i = 0; i < NV; ++i)
 #pragma unroll
         for (int j = 0; j < C::BN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[kk][j], f.a[kk][i], acc[i][j],
@@ -189,15 +186,17 @@ __device__ __forceinline__ void big_mfma(const BigFrags<C>& f, int nv,
 // operand on its own waves lets the B loads run far ahead without the A
 // waits depending on them.  Past the last K step the loads repeat the last
 // step (L2 hits into slots never read), which keeps the counts uniform.
-template <class C, int U, bool GATED, class Ctx>
+// GRP (the wave's group) and NV are compile-time, so a step has no
+// branches: the MFMAs and fragment reads of a step are straight-line code.
+template <class C, int U, bool GATED, int GRP, int NV, class Ctx>
 __device__ __forceinline__ void big_pp_step(const Ctx& t, int kt, int nk,
                                             bf16_t* const (&sA)[C::NSA],
-                                            bf16_t* const (&sB)[C::NSB], int grp, int wig,
-                                            int nv, const int (&off)[C::KK],
+                                            bf16_t* const (&sB)[C::NSB], int wig,
+                                            const int (&off)[C::KK],
                                             f32x16_t (&acc)[C::BM][C::BN]) {
   BigFrags<C> f;
-  big_read_frags<C>(sA[U % C::NSA], sB[U % C::NSB], grp, wig, nv, off, f);
-  if (grp == 0) {
+  big_read_frags<C, GRP, NV>(sA[U % C::NSA], sB[U % C::NSB], wig, off, f);
+  if constexpr (GRP == 0) {
     const int ks = kt + C::NSB - 1 < nk ? kt + C::NSB - 1 : nk - 1;
     t.template issue<C::LPW_B>(ks * C::BK, sB[(U + C::NSB - 1) % C::NSB], wig);
   } else {
@@ -205,19 +204,20 @@ __device__ __forceinline__ void big_pp_step(const Ctx& t, int kt, int nk,
     t.template issue<C::LPW_A>(ks * C::BK, sA[(U + C::NSA - 1) % C::NSA], wig);
   }
   __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): fragments in registers
-  if (grp == 1) wait_vm<(C::NSA - 2) * C::LPW_A>();
+  if constexpr (GRP == 1) wait_vm<(C::NSA - 2) * C::LPW_A>();
   lds_barrier();
-  big_mfma<C>(f, nv, acc);
-  if (grp == 0) wait_vm<(C::NSB - 2) * C::LPW_B>();
+  big_mfma<C, NV>(f, acc);
+  if constexpr (GRP == 0) wait_vm<(C::NSB - 2) * C::LPW_B>();
   lds_barrier();
 }
 
-template <class C, bool GATED, class Ctx>
+template <class C, bool GATED, int GRP, int NV, class Ctx>
 __device__ __forceinline__ void big_kloop(const Ctx& t, int nk,
                                           bf16_t* const (&sA)[C::NSA],
                                           bf16_t* const (&sB)[C::NSB], int wave, int lane,
-                                          int nv, f32x16_t (&acc)[C::BM][C::BN]) {
-  const int grp = wave >> 2, wig = wave & 3;
+                                          f32x16_t (&acc)[C::BM][C::BN]) {
+  constexpr int grp = GRP;
+  const int wig = wave & 3;
   const int r32 = lane & 31;
   int off[C::KK];
 #pragma unroll
@@ -237,14 +237,28 @@ __device__ __forceinline__ void big_kloop(const Ctx& t, int nk,
   lds_barrier();                  // point 0: stage 0 complete
   if (grp == 1) lds_barrier();    // point 1 for group 1 (its phase 0 is idle)
   for (int kt = 0; kt < nk; kt += 6) {
-    big_pp_step<C, 0, GATED>(t, kt, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 1 < nk) big_pp_step<C, 1, GATED>(t, kt + 1, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 2 < nk) big_pp_step<C, 2, GATED>(t, kt + 2, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 3 < nk) big_pp_step<C, 3, GATED>(t, kt + 3, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 4 < nk) big_pp_step<C, 4, GATED>(t, kt + 4, nk, sA, sB, grp, wig, nv, off, acc);
-    if (kt + 5 < nk) big_pp_step<C, 5, GATED>(t, kt + 5, nk, sA, sB, grp, wig, nv, off, acc);
+    big_pp_step<C, 0, GATED, GRP, NV>(t, kt, nk, sA, sB, wig, off, acc);
+    if (kt + 1 < nk) big_pp_step<C, 1, GATED, GRP, NV>(t, kt + 1, nk, sA, sB, wig, off, acc);
+    if (kt + 2 < nk) big_pp_step<C, 2, GATED, GRP, NV>(t, kt + 2, nk, sA, sB, wig, off, acc);
+    if (kt + 3 < nk) big_pp_step<C, 3, GATED, GRP, NV>(t, kt + 3, nk, sA, sB, wig, off, acc);
+    if (kt + 4 < nk) big_pp_step<C, 4, GATED, GRP, NV>(t, kt + 4, nk, sA, sB, wig, off, acc);
+    if (kt + 5 < nk) big_pp_step<C, 5, GATED, GRP, NV>(t, kt + 5, nk, sA, sB, wig, off, acc);
   }
   if (grp == 0) lds_barrier();    // both groups pass the same number of points
+}
+
+// The K loop instantiated for the wave's group and its count of row blocks
+// holding rows (nv, 0..BM; chosen once per item).
+template <class C, bool GATED, int GRP, int NV, class Ctx>
+__device__ __forceinline__ void big_kloop_nv(const Ctx& t, int nk, bf16_t* const (&sA)[C::NSA],
+                                             bf16_t* const (&sB)[C::NSB], int wave, int lane,
+                                             int nv, f32x16_t (&acc)[C::BM][C::BN]) {
+  if constexpr (NV == 0) {
+    big_kloop<C, GATED, GRP, 0>(t, nk, sA, sB, wave, lane, acc);
+  } else {
+    if (nv == NV) big_kloop<C, GATED, GRP, NV>(t, nk, sA, sB, wave, lane, acc);
+    else big_kloop_nv<C, GATED, GRP, NV - 1>(t, nk, sA, sB, wave, lane, nv, acc);
+  }
 }
 
 // Epilogue of the fused shared-expert down + combine ("Inkling, Dissected",
@@ -445,7 +459,8 @@ __global__ __launch_bounds__(512, 1) void ffn_big_kernel(FfnArgs p, const int32_
     // row blocks of this wave's group (2i + wm) that hold rows of the tile
     const int nblk = (item.rows + 31) >> 5;
     const int nv = min((nblk - wm + 1) >> 1, C::BM);
-    big_kloop<C, GATED>(t, nk, sA, sB, wave, lane, nv, acc);
+    if (wm == 0) big_kloop_nv<C, GATED, 0, C::BM>(t, nk, sA, sB, wave, lane, nv, acc);
+    else big_kloop_nv<C, GATED, 1, C::BM>(t, nk, sA, sB, wave, lane, nv, acc);
     // the last steps refill ring slots with copies of the final stage, and
     // those copies may still be landing: drain every wave's loads before the
     // ring memory is reused for the output tile
