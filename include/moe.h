@@ -336,8 +336,11 @@ moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w,
 /* The whole layer ("Inkling, Dissected", 02b: the per-token sketch of
  * router, top-6, joint gates and the weighted sum of the 8 experts' outputs;
  * 02e: the bias moves once the batch is done): router (with the incoming
- * bias), dispatch, expert FFN, combine, then the bias update in place (the
- * next batch routes with the new bias; gamma == 0 leaves it unchanged).
+ * bias), dispatch, expert FFN, combine, and the bias update in place from
+ * this batch's loads (the next batch routes with the new bias; gamma == 0
+ * leaves it unchanged).  The update is applied once the router has read
+ * the bias: for batches of at most 4096 (token, slot) pairs routed to
+ * 32-row tiles it runs in the dispatch launch, otherwise after the combine.
  * Writes y [T, d] and, when `routing` is non-NULL, its non-NULL members
  * (the tensors a caller wants to keep; the others live in the workspace). */
 moe_status moe_forward(const moe_desc* desc, const void* x,
@@ -350,8 +353,10 @@ moe_status moe_forward(const moe_desc* desc, const void* x,
  * Same arguments, results and workspace; in addition marks[0..6] are
  * recorded after the router, the dispatch, the GEMMs' tile plan, the
  * gate/up GEMM, the down GEMM, the combine and the bias update (marks[6]
- * also when gamma == 0).  marks[0..6] must be valid events (MOE_ERR_NULL
- * otherwise). */
+ * also when gamma == 0).  Where the dispatch launch also writes the tile
+ * plan and applies the bias update (small batches, see moe_forward),
+ * marks[2] follows marks[1] and marks[6] follows marks[5] directly.
+ * marks[0..6] must be valid events (MOE_ERR_NULL otherwise). */
 moe_status moe_forward_marked(const moe_desc* desc, const void* x,
                               const moe_weights* w, float* bias, float gamma,
                               void* y, const moe_routing* routing_or_null,
