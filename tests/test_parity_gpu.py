@@ -65,6 +65,13 @@ SMALL = {
     "e128_s0_lse_cap": MoEConfig("e128_s0_lse_cap", T=1200, d=512, F=128, E=128, S=0,
                                  act="bf16", bias_range=0.05, gate_norm="logsumexp",
                                  gate_scale=2.5, capacity_factor=1.25),
+    # either side of the one-workgroup dispatch (at most 4096 pairs; in the
+    # forward it also writes the tile plan and applies the bias update),
+    # under a capacity that drops pairs
+    "bf16_dispatch_4092": MoEConfig("bf16_dispatch_4092", T=682, d=256, F=128, act="bf16",
+                                    bias_range=0.05, capacity_factor=1.0),
+    "bf16_dispatch_4098": MoEConfig("bf16_dispatch_4098", T=683, d=256, F=128, act="bf16",
+                                    bias_range=0.05, capacity_factor=1.0),
 }
 
 
