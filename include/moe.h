@@ -156,9 +156,9 @@ typedef struct {
  *   w_gate, w_up [E, F, d]   w_down [E, d, F]        (act dtype)
  *   ws_gate, ws_up [S, F, d] ws_down [S, d, F]       (act dtype)
  * With weight == MOE_MXFP4 the routed matrices are the outputs of
- * moe_quantize_mxfp4: w_gate, w_up [E, F, d/2] and w_down [E, d, F/2]
- * bytes of packed FP4 codes, and sc_gate, sc_up [E, d/32, F], sc_down
- * [E, F/32, d] their scale bytes (NULL otherwise).
+ * moe_quantize_mxfp4: w_gate, w_up [E, d/128, F, 64] and w_down
+ * [E, F/128, d, 64] bytes of packed FP4 codes, and sc_gate, sc_up
+ * [E, d/32, F], sc_down [E, F/32, d] their scale bytes (NULL otherwise).
  * w_router_planes (optional, may be NULL): the output of moe_router_prepare
  * for this w_router; moe_forward then routes with it instead of splitting
  * w_router again on every call.  It must be refreshed whenever w_router
@@ -327,9 +327,12 @@ moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts,
  * with largest magnitude a: X = floor(log2 a) - 2, clamped to [-127, 127]
  * (-127 when a = 0); each value v becomes the E2M1 magnitude nearest to
  * |v| / 2^X (ties to the even code; above 6 saturates to 6) with v's sign
- * as bit 3.  Quantizes a bf16 stack w [E, N, K] (K % 32 == 0) into
- * codes [E, N, K/2] (value 2i in the low nibble of byte i) and scales
- * [E, K/32, N] (bytes X + 127).  Device pointers; asynchronous. */
+ * as bit 3.  Quantizes a bf16 stack w [E, N, K] (K % 128 == 0, else
+ * MOE_ERR_SHAPE) into codes [E, K/128, N, 64]: for each 128-value K tile,
+ * the 64 code bytes of every row n, rows consecutive (value 2i of the tile
+ * in the low nibble of byte i), and scales [E, K/32, N] (bytes X + 127).
+ * Both are E * N * K/2 and E * N * K/32 bytes.  Device pointers;
+ * asynchronous. */
 moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 

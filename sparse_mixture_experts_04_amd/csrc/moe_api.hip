@@ -377,7 +377,7 @@ moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts, float ga
 
 moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w, uint8_t* codes,
                               uint8_t* scales, hipStream_t stream) {
-  if (E < 0 || N <= 0 || K <= 0 || K % 32 != 0) return MOE_ERR_SHAPE;
+  if (E < 0 || N <= 0 || K <= 0 || K % 128 != 0) return MOE_ERR_SHAPE;
   if (E == 0) return MOE_OK;
   if (!w || !codes || !scales) return MOE_ERR_NULL;
   if (reinterpret_cast<uintptr_t>(w) % 16 != 0 || reinterpret_cast<uintptr_t>(codes) % 16 != 0)

@@ -164,12 +164,13 @@ def test_binding_rejects_host_tensors():
 
 def test_quantize_argument_checks():
     P = ctypes.c_void_p(0x1000)
-    assert lib.moe_quantize_mxfp4(2, 8, 48, P, P, P, None) == 2       # K % 32
-    assert lib.moe_quantize_mxfp4(-1, 8, 64, P, P, P, None) == 2
-    assert lib.moe_quantize_mxfp4(2, 0, 64, P, P, P, None) == 2
-    assert lib.moe_quantize_mxfp4(2, 8, 64, None, P, P, None) == 1
-    assert lib.moe_quantize_mxfp4(2, 8, 64, ctypes.c_void_p(0x1004), P, P, None) == 5
-    assert lib.moe_quantize_mxfp4(0, 8, 64, None, None, None, None) == 0  # nothing to do
+    assert lib.moe_quantize_mxfp4(2, 8, 48, P, P, P, None) == 2       # K % 128
+    assert lib.moe_quantize_mxfp4(2, 8, 64, P, P, P, None) == 2
+    assert lib.moe_quantize_mxfp4(-1, 8, 128, P, P, P, None) == 2
+    assert lib.moe_quantize_mxfp4(2, 0, 128, P, P, P, None) == 2
+    assert lib.moe_quantize_mxfp4(2, 8, 128, None, P, P, None) == 1
+    assert lib.moe_quantize_mxfp4(2, 8, 128, ctypes.c_void_p(0x1004), P, P, None) == 5
+    assert lib.moe_quantize_mxfp4(0, 8, 128, None, None, None, None) == 0  # nothing to do
 
 
 def test_dispatch_noalloc_validates_before_launch():

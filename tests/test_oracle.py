@@ -579,9 +579,20 @@ def test_mxfp4_error_bound_and_round_trip():
 
 
 def test_mxfp4_pack_layout():
-    codes = np.arange(64, dtype=np.uint8).reshape(1, 1, 64) % 16   # E=1, N=1, K=64
-    X = np.array([[[3, -4]]])
+    # E=1, N=3, K=256: code of row n, value k is (3n + k) mod 16
+    n_, k_ = np.meshgrid(np.arange(3), np.arange(256), indexing="ij")
+    codes = ((3 * n_ + k_) % 16).astype(np.uint8).reshape(1, 3, 256)
+    X = np.zeros((1, 3, 8), dtype=np.int64)
+    X[0, 1, :] = [3, -4, 0, 1, 2, 5, -127, 127]
     packed, scales = O.mxfp4_pack(codes, X)
-    assert packed.shape == (1, 1, 32) and packed[0, 0, 0] == (0 | (1 << 4))
-    assert packed[0, 0, 7] == (14 | (15 << 4))
-    assert scales.shape == (1, 2, 1) and list(scales[0, :, 0]) == [130, 123]
+    assert packed.shape == (1, 2, 3, 64)              # [E, K/128, N, 64]
+    assert packed[0, 0, 0, 0] == 0x10                 # row 0, values 0, 1
+    assert packed[0, 0, 0, 7] == 0xFE                 # row 0, values 14, 15
+    assert packed[0, 1, 2, 0] == 0x76                 # row 2, values 128, 129: 6, 7
+    assert packed[0, 1, 1, 63] == 0x21                # row 1, values 254, 255: 1, 2
+    flat = packed.reshape(-1)                         # K tile 1 starts after 3 rows of tile 0
+    assert flat[3 * 64] == packed[0, 1, 0, 0] == 0x10  # row 0, values 128, 129: 0, 1
+    assert scales.shape == (1, 8, 3) and list(scales[0, :, 1]) == [130, 123, 127, 128, 129,
+                                                                   132, 0, 254]
+    with pytest.raises(ValueError):
+        O.mxfp4_pack(codes[:, :, :192], X[:, :, :6])
