@@ -158,7 +158,8 @@ typedef struct {
  * With weight == MOE_MXFP4 the routed matrices are the outputs of
  * moe_quantize_mxfp4: w_gate, w_up [E, d/128, F, 64] and w_down
  * [E, F/128, d, 64] bytes of packed FP4 codes, and sc_gate, sc_up
- * [E, d/32, F], sc_down [E, F/32, d] their scale bytes (NULL otherwise).
+ * [E, d/128, F, 4], sc_down [E, F/128, d, 4] their scale bytes (NULL
+ * otherwise).
  * w_router_planes (optional, may be NULL): the output of moe_router_prepare
  * for this w_router; moe_forward then routes with it instead of splitting
  * w_router again on every call.  It must be refreshed whenever w_router
@@ -330,8 +331,9 @@ moe_status moe_bias_update(const moe_desc* desc, const int32_t* counts,
  * as bit 3.  Quantizes a bf16 stack w [E, N, K] (K % 128 == 0, else
  * MOE_ERR_SHAPE) into codes [E, K/128, N, 64]: for each 128-value K tile,
  * the 64 code bytes of every row n, rows consecutive (value 2i of the tile
- * in the low nibble of byte i), and scales [E, K/32, N] (bytes X + 127).
- * Both are E * N * K/2 and E * N * K/32 bytes.  Device pointers;
+ * in the low nibble of byte i), and scales [E, K/128, N, 4]: for each K
+ * tile, the bytes X + 127 of its 4 blocks for every row n, rows
+ * consecutive.  They are E * N * K/2 and E * N * K/32 bytes.  Device pointers;
  * asynchronous. */
 moe_status moe_quantize_mxfp4(int32_t E, int32_t N, int32_t K, const void* w,
                               uint8_t* codes, uint8_t* scales, hipStream_t stream);

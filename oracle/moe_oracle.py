@@ -339,17 +339,19 @@ def mxfp4_pack(codes, X):
     multiple of 128): code bytes [E, K/128, N, 64], i.e. for each 128-value
     K tile the 64 bytes of every row n, rows consecutive, with value 2i of the
     tile in the low nibble of byte i; and scale bytes X + 127 laid out
-    [E, K/32, N] (the scales of one K block of consecutive weight rows are
-    contiguous).  The layout is the library's storage format, not the pages'
-    (they fix only values, block size and scales)."""
+    [E, K/128, N, 4], i.e. for each K tile the scales of its 4 blocks of 32
+    values for every row n, rows consecutive.  The layout is the library's
+    storage format, not the pages' (they fix only values, block size and
+    scales)."""
     codes = np.asarray(codes, dtype=np.uint8)
     E, N, K = codes.shape
     if K % 128:
         raise ValueError("the code layout tiles K by 128 values")
     nib = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)   # [E, N, K/2]
     packed = np.ascontiguousarray(nib.reshape(E, N, K // 128, 64).transpose(0, 2, 1, 3))
-    scales = (np.asarray(X) + 127).astype(np.uint8)
-    return packed, np.ascontiguousarray(np.swapaxes(scales, -1, -2))
+    scales = (np.asarray(X) + 127).astype(np.uint8)                      # [E, N, K/32]
+    scales = np.ascontiguousarray(scales.reshape(E, N, K // 128, 4).transpose(0, 2, 1, 3))
+    return packed, scales
 
 
 def silu(u):

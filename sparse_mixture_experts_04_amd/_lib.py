@@ -209,12 +209,12 @@ def weights_from(inp):
 
 def quantize_mxfp4(w):
     """moe_quantize_mxfp4 of a bf16 stack w [E, N, K]: returns (codes
-    uint8 [E, K/128, N, 64], scales uint8 [E, K/32, N]) on w's device."""
+    uint8 [E, K/128, N, 64], scales uint8 [E, K/128, N, 4]) on w's device."""
     E, N, K = w.shape
     if K % 128:
         raise ValueError(f"quantize_mxfp4: K = {K} is not a multiple of 128")
     codes = torch.empty((E, K // 128, N, 64), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((E, K // 32, N), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((E, K // 128, N, 4), dtype=torch.uint8, device=w.device)
     st = lib.moe_quantize_mxfp4(E, N, K, _ptr(w, torch.bfloat16, (E, N, K), "w"),
                                 codes.data_ptr(), scales.data_ptr(), _stream(w.device))
     _check("moe_quantize_mxfp4", st)
@@ -235,9 +235,9 @@ def fp4_weights(inp):
     wt.w_gate = _ptr(q["w_gate"], torch.uint8, (E, d // 128, F, 64), "w_gate")
     wt.w_up = _ptr(q["w_up"], torch.uint8, (E, d // 128, F, 64), "w_up")
     wt.w_down = _ptr(q["w_down"], torch.uint8, (E, F // 128, d, 64), "w_down")
-    wt.sc_gate = _ptr(q["sc_gate"], torch.uint8, (E, d // 32, F), "sc_gate")
-    wt.sc_up = _ptr(q["sc_up"], torch.uint8, (E, d // 32, F), "sc_up")
-    wt.sc_down = _ptr(q["sc_down"], torch.uint8, (E, F // 32, d), "sc_down")
+    wt.sc_gate = _ptr(q["sc_gate"], torch.uint8, (E, d // 128, F, 4), "sc_gate")
+    wt.sc_up = _ptr(q["sc_up"], torch.uint8, (E, d // 128, F, 4), "sc_up")
+    wt.sc_down = _ptr(q["sc_down"], torch.uint8, (E, F // 128, d, 4), "sc_down")
     dt = torch.bfloat16
     wt.ws_gate = _ptr(inp["ws_gate"], dt, (S, F, d), "ws_gate")
     wt.ws_up = _ptr(inp["ws_up"], dt, (S, F, d), "ws_up")

@@ -90,7 +90,7 @@ struct FfnArgs {
   int T, K, N, E, S, k;   // N = weight rows per expert (F for gate/up, d for down)
   int ldo;                // row length of the output
   int n_tiles;            // column tiles
-  const uint8_t* sc0;     // FP4 routed weights: scales of w0 / w1 [E, K/32, N]
+  const uint8_t* sc0;     // FP4 routed weights: scales of w0 / w1 [E, K/128, N, 4]
   const uint8_t* sc1;
   int ksplit;             // FP4 kernel: K slices of a shared-expert tile (0: none)
   float* part;            // FP4 kernel: fp32 partial tiles [ksplit][S*T][n_tiles*256]

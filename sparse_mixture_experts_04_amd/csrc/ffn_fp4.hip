@@ -16,8 +16,10 @@
 //                        GEMM's K step over 256 weight rows is one
 //                        contiguous 16 KiB block (about 9% faster to stream
 //                        from HBM than 256 separate 64-byte row pieces)
-//   scales [E, K/32, N] bytes X + 127; the scales of one K block of
-//                        consecutive weight rows are contiguous
+//   scales [E, K/128, N, 4] bytes X + 127: for each 128-value K tile, the
+//                        scales of its 4 K blocks for every row n, rows
+//                        consecutive (a K step's 256 rows read 1 KiB in
+//                        pieces of 128 bytes or more)
 #include "ffn_common.h"
 
 namespace moe {
@@ -72,7 +74,7 @@ __global__ __launch_bounds__(256) void mxfp4_quantize_kernel(const bf16_t* __res
     const long long tile = e * (K / 128) + kb / 4;   // 128-value K tile of expert e
     *reinterpret_cast<uint4*>(codes + (tile * N + n) * 64 + (kb & 3) * 16) =
         make_uint4(packed[0], packed[1], packed[2], packed[3]);
-    scales[(e * kb_per_row + kb) * N + n] = static_cast<uint8_t>(X + 127);
+    scales[(tile * N + n) * 4 + (kb & 3)] = static_cast<uint8_t>(X + 127);
   }
 }
 
@@ -96,10 +98,10 @@ hipError_t launch_quantize_mxfp4(long long E, int N, int K, const void* w, uint8
 // Per stage, LDS holds
 //   A      32 rows x 256 B (bf16), 16-byte chunk c of row r in slot c ^ (r & 15);
 //   codes  256 rows x 64 B, chunk c of row r in slot c ^ ((r >> 2) & 3);
-//   scales 4 K blocks x 256 rows (bytes);
+//   scales 256 rows x 4 K blocks (bytes);
 // all filled with direct global -> LDS loads: per wave up to 2 A loads and
-// 4 code loads of 1 KiB and one 256-byte scale load (the scales of K block
-// 4kt + wave).  An A load covers 4 rows and is skipped when none of them
+// 4 code loads of 1 KiB and one 256-byte scale load (the 4 scales of each
+// of rows 64 wave .. 64 wave + 63).  An A load covers 4 rows and is skipped when none of them
 // holds a row of the tile (decode tiles hold a row or two): the LDS rows it
 // would fill only feed accumulator rows that are never stored, and the
 // wave's wait counts follow its number of loads.  B fragments are read as 4 code bytes + 1 scale byte per lane and
@@ -203,8 +205,12 @@ __device__ __forceinline__ void fp4_stage(const uint8_t* st, int wn, int lane,
       word[j][kk] = *reinterpret_cast<const uint32_t*>(
           st + C::A_BYTES + row * 64 + chunk * 16 + (kk & 1) * 8 + half * 4);
     }
+    {
+      const uint32_t s4 =
+          *reinterpret_cast<const uint32_t*>(st + C::A_BYTES + C::C_BYTES + row * 4);
 #pragma unroll
-    for (int m = 0; m < KK / 2; ++m) sb[j][m] = st[C::A_BYTES + C::C_BYTES + m * 256 + row];
+      for (int m = 0; m < KK / 2; ++m) sb[j][m] = (s4 >> (8 * m)) & 0xffu;
+    }
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every read ahead of the first conversion
 #pragma unroll
@@ -449,8 +455,8 @@ __device__ __forceinline__ Fp4Ctx fp4_ctx(const FfnArgs& p, const Fp4Meta& m, in
                  (((lane & 3) ^ ((R >> 2) & 3)) << 4);
   }
   {
-    // scale load of K block 4kt + wave: LDS bytes 4l..4l+3 = rows 4l..4l+3
-    const int R = 4 * lane;
+    // scale load of rows 64 wave + l: LDS bytes 4R..4R+3 = row R's 4 K blocks
+    const int R = 64 * wave + lane;
     int col;
     const uint8_t* sbase;
     if (GATED) {
@@ -461,7 +467,7 @@ __device__ __forceinline__ Fp4Ctx fp4_ctx(const FfnArgs& p, const Fp4Meta& m, in
       sbase = p.sc0;
       col = item.n * C::NB + R;
     }
-    t.s_src = sbase + g * sstride_e + static_cast<size_t>(wave) * p.N + col;
+    t.s_src = sbase + g * sstride_e + static_cast<size_t>(col) * 4;
   }
   return t;
 }

@@ -592,7 +592,10 @@ def test_mxfp4_pack_layout():
     assert packed[0, 1, 1, 63] == 0x21                # row 1, values 254, 255: 1, 2
     flat = packed.reshape(-1)                         # K tile 1 starts after 3 rows of tile 0
     assert flat[3 * 64] == packed[0, 1, 0, 0] == 0x10  # row 0, values 128, 129: 0, 1
-    assert scales.shape == (1, 8, 3) and list(scales[0, :, 1]) == [130, 123, 127, 128, 129,
-                                                                   132, 0, 254]
+    assert scales.shape == (1, 2, 3, 4)               # [E, K/128, N, 4]
+    assert list(scales[0, 0, 1]) == [130, 123, 127, 128]   # row 1, blocks 0..3
+    assert list(scales[0, 1, 1]) == [129, 132, 0, 254]     # row 1, blocks 4..7
+    assert list(scales[0, 1, 0]) == [127] * 4
+    assert scales.reshape(-1)[12 + 4] == 129          # tile 1 starts after 3 rows x 4 bytes
     with pytest.raises(ValueError):
         O.mxfp4_pack(codes[:, :, :192], X[:, :, :6])
