@@ -101,11 +101,12 @@ hipError_t launch_quantize_mxfp4(long long E, int N, int K, const void* w, uint8
 //   scales 256 rows x 4 K blocks (bytes);
 // all filled with direct global -> LDS loads: per wave up to 2 A loads and
 // 4 code loads of 1 KiB and one 256-byte scale load (the 4 scales of each
-// of rows 64 wave .. 64 wave + 63).  An A load covers 4 rows and is skipped when none of them
-// holds a row of the tile (decode tiles hold a row or two): the LDS rows it
-// would fill only feed accumulator rows that are never stored, and the
-// wave's wait counts follow its number of loads.  B fragments are read as 4 code bytes + 1 scale byte per lane and
-// converted to bf16 in registers.
+// of rows 64 wave .. 64 wave + 63).  An A load covers 4 rows and is skipped
+// when none of them holds a row of the tile (decode tiles hold a row or
+// two): the LDS rows it would fill only feed accumulator rows that are
+// never stored, and the wave's wait counts follow its number of loads.  A
+// B fragment is 4 code bytes per lane and its block's scale byte (a lane
+// reads its row's 4 scales as one dword), converted to bf16 in registers.
 struct Fp4Cfg {
   static constexpr int MT = 32;
   static constexpr int NB = 256;
