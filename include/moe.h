@@ -94,7 +94,9 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+/* 4: MXFP4 codes and scales stored by 128-value K tile (see
+ * moe_quantize_mxfp4) */
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,

@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 # MOE_ABI_VERSION of include/moe.h that the structures below follow
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 F32, BF16, MXFP4 = 0, 1, 2
 CALL_ROUTER, CALL_DISPATCH, CALL_GATE_UP, CALL_DOWN = 0, 1, 2, 3

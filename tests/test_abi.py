@@ -29,7 +29,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert lib.moe_abi_version() == L.ABI_VERSION == 3
+    assert lib.moe_abi_version() == L.ABI_VERSION == 4
     for code in range(7):
         s = lib.moe_status_string(code)
         assert s and isinstance(s, bytes)
@@ -171,6 +171,14 @@ def test_quantize_argument_checks():
     assert lib.moe_quantize_mxfp4(2, 8, 128, None, P, P, None) == 1
     assert lib.moe_quantize_mxfp4(2, 8, 128, ctypes.c_void_p(0x1004), P, P, None) == 5
     assert lib.moe_quantize_mxfp4(0, 8, 128, None, None, None, None) == 0  # nothing to do
+
+
+def test_quantize_binding_needs_whole_k_tiles():
+    # the codes are stored by 128-value K tiles; the binding refuses other K
+    # before it touches any device memory
+    torch = pytest.importorskip("torch")
+    with pytest.raises(ValueError, match="multiple of 128"):
+        L.quantize_mxfp4(torch.zeros((2, 8, 96), dtype=torch.bfloat16))
 
 
 def test_dispatch_noalloc_validates_before_launch():
