@@ -6,7 +6,6 @@ workloads; the skewed workload's 100 bias steps at full size in lock-step,
 with its outputs checked at three of them; the native-shape and capacity
 workloads on sampled tokens.
 """
-import math
 
 import numpy as np
 import pytest
