@@ -120,33 +120,82 @@ def test_fp4_layer_full_parity(name):
     del keep
 
 
-def test_fp4_decode_workload_sampled():
+def _unpack_mxfp4(codes, scales):
+    """Codes [N, K] and exponents X [N, K/32] of one expert from the library's
+    storage by K tile (codes [K/128, N, 64], scales [K/128, N, 4])."""
+    kt, N, _ = codes.shape
+    nib = codes.transpose(1, 0, 2).reshape(N, kt * 64)
+    c = np.empty((N, kt * 128), dtype=np.uint8)
+    c[:, 0::2] = nib & 15
+    c[:, 1::2] = nib >> 4
+    X = scales.transpose(1, 0, 2).reshape(N, kt * 4).astype(np.int64) - 127
+    return c, X
+
+
+@pytest.mark.timeout(900)
+def test_fp4_decode_workload_every_token():
+    """Workload Cfp4 at its own size (T=64, d=7168, F=2048, MXFP4 routed
+    weights), every output.  The GPU's codes and scales of the first and last
+    touched expert equal the oracle's quantization bit for bit (and unpack
+    back to it); every touched expert's weights are then the oracle's
+    dequantization of the GPU's codes, against which every expert row, both
+    shared experts and y of all 64 tokens are compared."""
+    import concurrent.futures as cf
+
     cfg = configs.get("Cfp4")
-    log(f"[fp4 workload] {cfg.describe()}")
+    log(f"[fp4 workload, every token] {cfg.describe()}")
     inp = synth.make_inputs(cfg, device=DEV)
     desc = desc_for(cfg)
-    wq, keep = L.fp4_weights(inp)
-    b, bias_new = run_forward(desc, inp, cfg.gamma, weights=wq)
+    wq, q = L.fp4_weights(inp)
+    b, bias_new = run_stages(desc, inp, cfg.gamma, weights=wq)
     x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
     topk = npi(b.topk)
     _, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates))
     dp = check_dispatch(topk, b)
     check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
-    toks = [0, 63]
+    touched = [int(e) for e in np.nonzero(dp["counts"])[0]]
+    names = ("w_gate", "w_up", "w_down")
 
-    def get(e):
-        if e < cfg.E:
-            out = []
-            for n in ("w_gate", "w_up", "w_down"):
-                c, X = O.mxfp4_quantize(inp[n][e].float().cpu().numpy())
-                out.append(O.mxfp4_dequantize(c, X))
-            return tuple(out)
-        s = e - cfg.E
-        return tuple(np64(inp[n][s]) for n in ("ws_gate", "ws_up", "ws_down"))
+    def stored(n, e):
+        return q[n][e].cpu().numpy(), q["sc_" + n[2:]][e].cpu().numpy()
 
-    y_ref = O.output_rows(toks, x64, topk, g_ref, get, pair_pos=dp["pair_pos"])
-    e = rel_l2(np64(b.y)[toks], y_ref)
-    log(f"  routing {st}; sampled {len(toks)} tokens: rel L2 {e:.2e}")
-    assert e <= 2e-2
-    del keep, inp
+    for e in (touched[0], touched[-1]):
+        for n in names:
+            c_ref, x_ref = O.mxfp4_quantize(inp[n][e].float().cpu().numpy())
+            p_ref, s_ref = O.mxfp4_pack(c_ref[None], x_ref[None])
+            codes, scales = stored(n, e)
+            assert np.array_equal(codes, p_ref[0]) and np.array_equal(scales, s_ref[0]), (n, e)
+            c_u, x_u = _unpack_mxfp4(codes, scales)
+            assert np.array_equal(c_u, c_ref) and np.array_equal(x_u, x_ref), (n, e)
+
+    off, sp, k = dp["offsets"], dp["sorted_pair"], cfg.k
+    n_rows = int(off[-1])
+    yr_ref = np.zeros((n_rows, cfg.d))
+    pool = cf.ThreadPoolExecutor(max_workers=8)
+    for i in range(0, len(touched), 8):
+        batch = touched[i:i + 8]
+        raw = [[stored(n, e) for n in names] for e in batch]
+        deq = [[pool.submit(lambda cs: O.mxfp4_dequantize(*_unpack_mxfp4(*cs)), cs) for cs in r]
+               for r in raw]
+        for e, fut in zip(batch, deq):
+            wg, wu, wd = (f.result() for f in fut)
+            lo, hi = int(off[e]), int(off[e + 1])
+            yr_ref[lo:hi] = O.swiglu(x64[sp[lo:hi] // k], wg, wu, wd)
+        del raw, deq
+    pool.shutdown()
+    ys_ref = np.stack([O.swiglu(x64, np64(inp["ws_gate"][s_]), np64(inp["ws_up"][s_]),
+                                np64(inp["ws_down"][s_])) for s_ in range(cfg.S)])
+    e_yr = rel_l2(np64(b.y_routed)[:n_rows], yr_ref)
+    e_ys = rel_l2(np64(b.y_shared), ys_ref)
+    y_ref = O.combine(yr_ref, ys_ref, g_ref, dp["pair_pos"], k)
+    y = np64(b.y)
+    e_y = rel_l2(y, y_ref)
+    tok = np.linalg.norm(y - y_ref, axis=1) / np.linalg.norm(y_ref, axis=1)
+    log(f"  routing {st}; {len(touched)} experts; rel L2 y_routed {e_yr:.2e} y_shared {e_ys:.2e} "
+        f"y {e_y:.2e} (worst token {tok.max():.2e})")
+    assert e_yr <= 2e-2 and e_ys <= 2e-2 and e_y <= 2e-2
+    # the fused entry point gives the stage calls' bits
+    bf, _ = run_forward(desc, inp, cfg.gamma, weights=wq)
+    assert torch.equal(b.y, bf.y) and torch.equal(b.topk, bf.topk)
+    del q, inp, b, bf
     torch.cuda.empty_cache()
