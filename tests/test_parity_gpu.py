@@ -162,14 +162,6 @@ def test_determinism_bitwise():
     assert torch.equal(bias1, bias2)
 
 
-def sample_tokens(T, n, seed=0):
-    if n >= T:
-        return list(range(T))
-    rng = np.random.default_rng(seed)
-    picks = {0, T - 1} | set(rng.choice(T, size=n - 2, replace=False).tolist())
-    return sorted(picks)
-
-
 def check_full_size_output(cfg, inp, b, dp, g_ref, y_forward=None):
     """Every output of a full-size workload against the oracle fed the GPU's
     selection: each routed expert's rows of y_routed (per-expert relative
@@ -207,11 +199,14 @@ def check_full_size_output(cfg, inp, b, dp, g_ref, y_forward=None):
 
 
 @pytest.mark.timeout(600)
-@pytest.mark.parametrize("name", ["B", "C", "D"])
+@pytest.mark.parametrize("name", ["B", "C", "D", "I", "Ecap"])
 def test_workload_parity_every_token(name):
-    """Workloads B (prefill chunk), C (decode) and D (large batch) at their
-    own sizes: routing, dispatch and bias in full, and every output element
-    against the oracle (D: the whole 11.5 TFLOP layer in float64)."""
+    """Workloads B (prefill chunk), C (decode), D (large batch), I (the
+    native shape with logsumexp gates) and Ecap (skewed routing under
+    capacity 1.25, its first batch) at their own sizes: routing, dispatch
+    and bias in full, and every output element against the oracle (D: the
+    whole 11.5 TFLOP layer in float64); moe_forward run twice gives the same
+    bits."""
     cfg = configs.get(name)
     log(f"[workload parity, every token] {name}: {cfg.describe()}")
     inp = synth.make_inputs(cfg, device=DEV)
@@ -231,33 +226,9 @@ def test_workload_parity_every_token(name):
     bf, bias_f = run_forward(desc, inp, cfg.gamma)
     check_forward_matches_stages(cfg, b, bias_new, bf, bias_f)
     check_full_size_output(cfg, inp, b, dp, g_ref, y_forward=bf.y)
-    del inp, b, bf
-    torch.cuda.empty_cache()
-
-
-@pytest.mark.parametrize("name,nsample", [("I", 16), ("Ecap", 16)])
-def test_workload_parity_sampled(name, nsample):
-    cfg = configs.get(name)
-    log(f"[workload parity, sampled] {name}: {cfg.describe()}")
-    inp = synth.make_inputs(cfg, device=DEV)
-    desc = desc_for(cfg)
-    b, bias_new = run_forward(desc, inp, cfg.gamma)
-    x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
-    topk = npi(b.topk)
-    r, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates),
-                                 gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
-    log(f"  routing {st}")
-    dp = check_dispatch(topk, b, cap=cap_for(cfg))
-    check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T)
-    toks = sample_tokens(cfg.T, nsample)
-    y_ref = O.output_rows(toks, x64, topk, g_ref, expert_getter(inp), pair_pos=dp["pair_pos"])
-    e = rel_l2(np64(b.y)[toks], y_ref)
-    log(f"  sampled {len(toks)} tokens: rel L2 {e:.2e}")
-    assert e <= out_tol(cfg)
-    # a second run is bit-identical
     b2, _ = run_forward(desc, inp, cfg.gamma)
-    assert torch.equal(b.y, b2.y) and torch.equal(b.sorted_pair, b2.sorted_pair)
-    del inp, b, b2
+    assert torch.equal(bf.y, b2.y) and torch.equal(bf.sorted_pair, b2.sorted_pair)
+    del inp, b, bf, b2
     torch.cuda.empty_cache()
 
 
