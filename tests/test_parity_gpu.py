@@ -305,9 +305,11 @@ def test_skewed_workload_100_steps_lockstep():
     bias the GPU routed with ("Inkling, Dissected", 02e: the bias moves after
     each batch; 02g runs 100 such steps): selection outside near-ties, gates,
     counts, offsets, the permutation and the new bias bit for bit.  At steps
-    0, 49 and 99 the expert outputs, combine and y are checked as well
-    (check_skewed_step_outputs).  Near-tie counts are logged per step and in
-    total."""
+    0, 49 and 99 every output is checked as well (check_full_size_output:
+    every expert's rows, every shared slice, combine and y on every token,
+    for the stage calls and for moe_forward), after the hottest experts'
+    tile-boundary rows (check_skewed_step_outputs).  Near-tie counts are
+    logged per step and in total."""
     cfg = configs.get("E")
     log(f"[skewed lock-step, 100 steps] {cfg.describe()}")
     inp = synth.make_inputs(cfg, device=DEV)
@@ -340,6 +342,7 @@ def test_skewed_workload_100_steps_lockstep():
         if full:
             check_skewed_step_outputs(cfg, inp, b, dp, g_ref, step, x64,
                                       y_forward=bf.y)
+            check_full_size_output(cfg, inp, b, dp, g_ref, y_forward=bf.y)
         del b, bf, x64
     log(f"  100 steps: near-tie tokens {exempt}, of which {differ} picked the other set")
     assert 0 <= differ <= exempt
