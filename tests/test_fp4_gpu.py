@@ -199,3 +199,56 @@ def test_fp4_decode_workload_every_token():
     assert torch.equal(b.y, bf.y) and torch.equal(b.topk, bf.topk)
     del q, inp, b, bf
     torch.cuda.empty_cache()
+
+
+def fp4_sweep_cases(n=8, seed=4242):
+    """Seeded MXFP4 layers over the decode range (T * k < 48 * E): routed
+    experts 64/128/256, shared 0-2, widths giving 1 to 6 K tiles of 128, both
+    gate forms, with and without capacity."""
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        E = int(rng.choice([64, 128, 256]))
+        S = int(rng.integers(0, 3))
+        d = int(rng.choice([256, 512, 768]))
+        F = int(rng.choice([128, 256, 384]))
+        T = int(rng.integers(1, 8 * E))
+        gate = "logsumexp" if rng.random() < 0.4 else "ratio"
+        cf = float(rng.choice([0.0, 0.0, 1.0, 1.25]))
+        cases.append(MoEConfig(f"fp4sweep{i}", T=T, d=d, F=F, E=E, S=S, act="bf16",
+                               bias_range=0.05, fp4_weights=True, gate_norm=gate,
+                               gate_scale=2.0 if gate == "logsumexp" else 1.0,
+                               capacity_factor=cf))
+    return cases
+
+
+FP4_SWEEP = fp4_sweep_cases()
+
+
+@pytest.mark.parametrize("i", range(len(FP4_SWEEP)))
+def test_fp4_sweep_full_parity(i):
+    cfg = FP4_SWEEP[i]
+    log(f"[fp4 sweep {i}] {cfg.describe()} gates={cfg.gate_norm} cf={cfg.capacity_factor}")
+    inp = {k: v.to(DEV) for k, v in synth.make_inputs(cfg, device="cpu").items()}
+    desc = desc_for(cfg)
+    wq, keep = L.fp4_weights(inp)
+    b, bias_new = run_stages(desc, inp, cfg.gamma, weights=wq)
+    x64, wr64, b64 = np64(inp["x"]), np64(inp["w_router"]), np64(inp["bias"])
+    topk = npi(b.topk)
+    _, g_ref, st = check_routing(x64, wr64, b64, topk, np64(b.gates), k=cfg.k,
+                                 gate_norm=cfg.gate_norm, gate_scale=cfg.gate_scale)
+    cap = O.capacity(cfg.capacity_factor, cfg.k, cfg.T, cfg.E)
+    dp = check_dispatch(topk, b, E=cfg.E, cap=cap)
+    check_bias(npi(b.counts), cfg.gamma, inp["bias"], bias_new, cfg.T, cfg.k)
+    hw = _fp4_oracle_weights(inp)
+    yr_ref, ys_ref = O.expert_ffn(x64, hw, dp["offsets"], dp["sorted_pair"], cfg.k)
+    n = int(dp["offsets"][-1])
+    y_ref = O.combine(yr_ref, ys_ref, g_ref, dp["pair_pos"], cfg.k)
+    e_yr = rel_l2(np64(b.y_routed)[:n], yr_ref[:n])
+    e_ys = rel_l2(np64(b.y_shared), ys_ref) if cfg.S else 0.0
+    e_y = rel_l2(np64(b.y), y_ref)
+    log(f"  routing {st}; rel L2 y_routed {e_yr:.2e} y_shared {e_ys:.2e} y {e_y:.2e}")
+    assert e_yr <= 2e-2 and e_ys <= 2e-2 and e_y <= 2e-2
+    bf, _ = run_forward(desc, inp, cfg.gamma, weights=wq)
+    assert torch.equal(b.y, bf.y) and torch.equal(b.topk, bf.topk)
+    del keep
